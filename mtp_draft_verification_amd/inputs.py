@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs shared by the GPU path's tests/benchmark and the oracle.
+
+This module draws random tensors and nothing else: it holds none of the verify
+step's arithmetic (no RoPE, attention, logits, softmax or acceptance).  Every
+tensor has its own generator, seeded from (seed, tensor name, chunk index), so a
+tensor does not change when another one is added or resized.  Values are drawn
+in fp32 and rounded once to bf16 (round-to-nearest-even, torch's conversion)
+for bf16 workloads; both sides then consume identical bits.
+
+Tensors can be generated on the CPU (small workloads, CPU-only tests) or
+directly on the GPU (workloads of several GB); the two devices give different
+streams for the same seed, so a test always feeds the oracle host copies of the
+very tensors the GPU consumed.
+"""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+import torch
+
+_CHUNK = 1 << 26  # elements per generator chunk (bounds the fp32 temporary)
+
+
+def _seed_of(seed: int, name: str, chunk: int = 0) -> int:
+    h = hashlib.sha256(f"{int(seed)}/{name}/{int(chunk)}".encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def generator(seed: int, name: str, device="cpu", chunk: int = 0) -> torch.Generator:
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(_seed_of(seed, name, chunk))
+    return g
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+
+def normal(shape, std: float, seed: int, name: str, device="cpu", dtype: str = "bf16") -> torch.Tensor:
+    """N(0, std^2) entries, drawn in fp32 chunks along the first dimension."""
+    shape = tuple(int(s) for s in shape)
+    out = torch.empty(shape, dtype=torch_dtype(dtype), device=device)
+    if out.numel() == 0:
+        return out
+    flat = out.view(-1)
+    n = flat.numel()
+    for c, start in enumerate(range(0, n, _CHUNK)):
+        m = min(_CHUNK, n - start)
+        g = generator(seed, name, device, c)
+        x = torch.randn(m, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        flat[start:start + m].copy_(x)
+    return out
+
+
+def uniform(shape, seed: int, name: str, device="cpu") -> torch.Tensor:
+    """U[0,1) fp32 entries (the random numbers a sampling step consumes)."""
+    g = generator(seed, name, device)
+    return torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32)
+
+
+def randint(shape, lo: int, hi_inclusive: int, seed: int, name: str, device="cpu") -> torch.Tensor:
+    g = generator(seed, name, device)
+    return torch.randint(int(lo), int(hi_inclusive) + 1, tuple(shape), generator=g, device=device,
+                         dtype=torch.int64).to(torch.int32)
+
+
+def bernoulli(shape, p: float, seed: int, name: str, device="cpu") -> torch.Tensor:
+    return uniform(shape, seed, name, device) < p
+
+
+def dirichlet_rows(rows: int, vocab: int, alpha: float, seed: int, name: str, device="cpu") -> torch.Tensor:
+    """Rows of Dirichlet(alpha) probabilities over the vocabulary, fp32 [rows, vocab]."""
+    g = generator(seed, name, device)
+    conc = torch.full((rows, vocab), float(alpha), dtype=torch.float32, device=device)
+    x = torch._standard_gamma(conc, generator=g)
+    x = x / x.sum(dim=1, keepdim=True)
+    return x.to(torch.float32)
+
+
+def categorical(probs: torch.Tensor, seed: int, name: str) -> torch.Tensor:
+    """One draw per row of a probability matrix [rows, vocab] -> int32 [rows]."""
+    g = generator(seed, name, probs.device)
+    return torch.multinomial(probs, 1, replacement=True, generator=g)[:, 0].to(torch.int32)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """Host uint16 array holding the bit patterns of a bf16 tensor."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def host_f32(t: torch.Tensor) -> np.ndarray:
+    """Host fp32 copy (exact for bf16 and fp32 tensors)."""
+    return t.detach().float().contiguous().cpu().numpy()
+
+
+# --------------------------------------------------------------------------
+# workload builders (shapes from configs.py)
+# --------------------------------------------------------------------------
+
+def attn_inputs(cfg, seed: int = 0, device="cpu", capacity_extra: int = 0) -> dict:
+    """Inputs of one verify-attention call: committed lengths, a cache filled with
+    rotated-key-like rows below them, and the pre-RoPE queries / new rows."""
+    ly = cfg.layer
+    B, nq = cfg.batch, cfg.k + 1
+    lens = randint((B,), cfg.ctx_lo, cfg.ctx_hi, seed, "cache_len", "cpu")
+    cap = int(lens.max()) + nq + capacity_extra
+    dt = cfg.dtype
+    k_cache = normal((B, ly.n_heads_kv, cap, ly.head_dim), cfg.std, seed, "k_cache", device, dt)
+    v_cache = None if ly.k_is_v else normal((B, ly.n_heads_kv, cap, ly.head_dim), cfg.std, seed,
+                                            "v_cache", device, dt)
+    q = normal((B, nq, ly.n_heads_q, ly.head_dim), cfg.std, seed, "q", device, dt)
+    k_new = normal((B, nq, ly.n_heads_kv, ly.head_dim), cfg.std, seed, "k_new", device, dt)
+    v_new = None if ly.k_is_v else normal((B, nq, ly.n_heads_kv, ly.head_dim), cfg.std, seed,
+                                          "v_new", device, dt)
+    return dict(cache_len=lens.to(device), cap=cap, k_cache=k_cache, v_cache=v_cache, q=q,
+                k_new=k_new, v_new=v_new)
+
+
+def stack_weights(cfg, seed: int = 0, device="cpu") -> dict:
+    """Random-init weights of a decoder stack, N(0, 1/fan_in) entries.
+
+    Per layer: wqkv [Hq*D + Hkv*D (+ Hkv*D for V), d] (q, k, v projections stacked
+    along the output dimension), wo [d, Hq*D], and with an MLP wg, wu [d_ff, d]
+    and wd [d, d_ff].  The embedding table E [vocab, d] is tied to the LM head."""
+    dt = cfg.dtype
+    d = cfg.d_model
+    W = {"E": normal((cfg.vocab, d), d ** -0.5, seed, "E", device, dt), "layers": []}
+    for i, ly in enumerate(cfg.layers):
+        nq = ly.n_heads_q * ly.head_dim
+        nk = ly.n_heads_kv * ly.head_dim
+        nout = nq + nk + (0 if ly.k_is_v else nk)
+        lw = {"wqkv": normal((nout, d), d ** -0.5, seed, f"L{i}.wqkv", device, dt),
+              "wo": normal((d, nq), nq ** -0.5, seed, f"L{i}.wo", device, dt)}
+        if cfg.d_ff:
+            lw["wg"] = normal((cfg.d_ff, d), d ** -0.5, seed, f"L{i}.wg", device, dt)
+            lw["wu"] = normal((cfg.d_ff, d), d ** -0.5, seed, f"L{i}.wu", device, dt)
+            lw["wd"] = normal((d, cfg.d_ff), cfg.d_ff ** -0.5, seed, f"L{i}.wd", device, dt)
+        W["layers"].append(lw)
+    return W
+
+
+def stack_caches(cfg, seed: int = 0, device="cpu", capacity: int | None = None,
+                 fill_from: int | None = None) -> list:
+    """Per layer: k [B, Hkv, cap, D] (and v unless K = V), rows [fill_lo, ctx) ~ N(0,1),
+    all other rows zero.  fill_from=None fills every committed row; a sliding-window
+    layer reads only its last `window` rows, so large workloads fill only those."""
+    B = cfg.batch
+    cap = capacity if capacity is not None else cfg.ctx + (cfg.k + 1) * max(cfg.steps, 1) + 8
+    dt = cfg.dtype
+    caches = []
+    for i, ly in enumerate(cfg.layers):
+        lo = 0
+        if fill_from is not None:
+            lo = fill_from if ly.window == 0 else max(0, cfg.ctx - ly.window - 8)
+        shape = (B, ly.n_heads_kv, cap, ly.head_dim)
+        ent = {}
+        for nm in (("k",) if ly.k_is_v else ("k", "v")):
+            t = torch.zeros(shape, dtype=torch_dtype(dt), device=device)
+            if cfg.ctx > lo:
+                t[:, :, lo:cfg.ctx, :] = normal((B, ly.n_heads_kv, cfg.ctx - lo, ly.head_dim), 1.0,
+                                                seed, f"L{i}.cache_{nm}", device, dt)
+            ent[nm] = t
+        ent["v"] = ent.get("v")
+        caches.append(ent)
+    return caches

@@ -1,0 +1,295 @@
+"""CPU oracle for the MTP verify step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never uses it, shares no
+code with it, and the product path fails loudly instead of falling back to it.
+
+The arithmetic lives in ``svoracle.c`` (plain fp64 loops, built with gcc into
+``liboracle.so``).  This module only marshals numpy arrays into those loops;
+``model.py`` composes them into a whole verify step of a small decoder stack.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "svoracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (OpenMP, no fast-math: IEEE fp64)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-std=gnu11", "-Wall", "-shared", "-fPIC",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_q", ctypes.c_int32), ("group", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("rope_dims", ctypes.c_int32), ("k_is_v", ctypes.c_int32),
+        ("append", ctypes.c_int32), ("q_pos_offset", ctypes.c_int32),
+        ("round_bf16", ctypes.c_int32), ("pad_", ctypes.c_int32),
+        ("rope_base", ctypes.c_double), ("scale", ctypes.c_double),
+        ("cap", ctypes.c_int64), ("L", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("out", ctypes.c_void_p),
+    ]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [
+        ("top1_id", ctypes.c_int32), ("top2_id", ctypes.c_int32),
+        ("top1", ctypes.c_double), ("top2", ctypes.c_double),
+        ("lse", ctypes.c_double), ("draft_logit", ctypes.c_double),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+        L.svo_num_threads.restype = ctypes.c_int
+        L.svo_bf16_round.restype = f64
+        L.svo_bf16_round.argtypes = [f64]
+        L.svo_bf16_round_array.argtypes = [P, i64]
+        L.svo_rope.argtypes = [P, ctypes.c_int, f64, f64]
+        L.svo_attn_group.argtypes = [ctypes.POINTER(AttnArgs)]
+        L.svo_attn_group.restype = ctypes.c_int
+        L.svo_linear.argtypes = [i64, i64, i64, P, P, ctypes.c_int, P]
+        L.svo_rmsnorm.argtypes = [i64, i64, f64, P, P]
+        L.svo_gelu_tanh.argtypes = [f64]
+        L.svo_gelu_tanh.restype = f64
+        L.svo_geglu.argtypes = [i64, P, P, P]
+        L.svo_lmhead.argtypes = [i64, i64, i64, P, P, ctypes.c_int, P]
+        L.svo_row_stats.argtypes = [i64, P, i32, ctypes.POINTER(Stats)]
+        L.svo_accept_greedy.argtypes = [ctypes.c_int, P, P, P]
+        L.svo_accept_greedy.restype = ctypes.c_int
+        L.svo_accept_sample.argtypes = [ctypes.c_int, P, P, P, P, P]
+        L.svo_accept_sample.restype = ctypes.c_int
+        L.svo_sample_residual.argtypes = [i64, P, f64, P, P, ctypes.POINTER(f64)]
+        L.svo_sample_residual.restype = ctypes.c_int
+        L.svo_sample_bonus.argtypes = [i64, P, P, ctypes.POINTER(f64)]
+        L.svo_sample_bonus.restype = ctypes.c_int
+        L.svo_toy_spec_trials.argtypes = [i64, ctypes.c_int, i64, P, P, P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().svo_num_threads())
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _weight(w: np.ndarray):
+    """(array, is_bf16): fp32 arrays pass as they are, uint16 arrays are bf16 bits."""
+    if w.dtype == np.uint16:
+        return np.ascontiguousarray(w), 1
+    return _f32(w), 0
+
+
+# --------------------------------------------------------------------------
+# elementwise pieces
+# --------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    y = _f64(x).copy()
+    lib().svo_bf16_round_array(_ptr(y), y.size)
+    return y
+
+
+def rope(x, rope_dims: int, base: float, pos: float) -> np.ndarray:
+    y = _f64(x).copy()
+    lib().svo_rope(_ptr(y), int(rope_dims), float(base), float(pos))
+    return y
+
+
+def gelu_tanh(x: float) -> float:
+    return float(lib().svo_gelu_tanh(float(x)))
+
+
+def geglu(g, u) -> np.ndarray:
+    g, u = _f64(g), _f64(u)
+    f = np.empty_like(g)
+    lib().svo_geglu(g.size, _ptr(g), _ptr(u), _ptr(f))
+    return f
+
+
+def rmsnorm(x, eps: float) -> np.ndarray:
+    x = _f64(x)
+    R, d = x.shape
+    y = np.empty_like(x)
+    lib().svo_rmsnorm(R, d, float(eps), _ptr(x), _ptr(y))
+    return y
+
+
+def linear(x, w: np.ndarray) -> np.ndarray:
+    """y = x @ w.T with w [N, K] (fp32 or bf16 bits), x [R, K] -> fp64 [R, N]."""
+    x = _f64(x)
+    R, K = x.shape
+    wa, wb = _weight(w)
+    N = wa.shape[0]
+    assert wa.shape[1] == K
+    y = np.empty((R, N), dtype=np.float64)
+    lib().svo_linear(R, K, N, _ptr(x), _ptr(wa), wb, _ptr(y))
+    return y
+
+
+def lmhead(h, w: np.ndarray) -> np.ndarray:
+    """Full logits z = h @ w.T, fp64 [R, V]."""
+    h = _f64(h)
+    R, d = h.shape
+    wa, wb = _weight(w)
+    V = wa.shape[0]
+    assert wa.shape[1] == d
+    z = np.empty((R, V), dtype=np.float64)
+    lib().svo_lmhead(R, d, V, _ptr(h), _ptr(wa), wb, _ptr(z))
+    return z
+
+
+def row_stats(z_row, draft_id: int = -1) -> dict:
+    z = _f64(z_row)
+    st = Stats()
+    lib().svo_row_stats(z.size, _ptr(z), int(draft_id), ctypes.byref(st))
+    return dict(top1_id=st.top1_id, top2_id=st.top2_id, top1=st.top1, top2=st.top2,
+                lse=st.lse, draft_logit=st.draft_logit)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def attn_group(*, q, k_new, v_new, k_cache, v_cache, L: int, window: int, rope_dims: int,
+               rope_base: float, scale: float, k_is_v: bool, append: bool,
+               q_pos_offset: int = 0, round_bf16: bool) -> np.ndarray:
+    """One sequence, one KV head.  q [n_q, group, D]; k_new/v_new [n_q, D];
+    k_cache/v_cache [cap, D] float32 (modified in place when append).
+    Returns out [n_q, group, D] fp64."""
+    q = _f32(q)
+    n_q, group, D = q.shape
+    assert k_cache.dtype == np.float32 and k_cache.flags["C_CONTIGUOUS"]
+    if v_cache is not None:
+        assert v_cache.dtype == np.float32 and v_cache.flags["C_CONTIGUOUS"]
+    kn = _f32(k_new) if append else None
+    vn = _f32(v_new) if (append and not k_is_v) else None
+    out = np.zeros((n_q, group, D), dtype=np.float64)
+    a = AttnArgs(n_q=n_q, group=group, head_dim=D, window=int(window), rope_dims=int(rope_dims),
+                 k_is_v=int(bool(k_is_v)), append=int(bool(append)),
+                 q_pos_offset=int(q_pos_offset), round_bf16=int(bool(round_bf16)), pad_=0,
+                 rope_base=float(rope_base), scale=float(scale), cap=k_cache.shape[0], L=int(L),
+                 q=_ptr(q), k_new=_ptr(kn), v_new=_ptr(vn), k_cache=_ptr(k_cache),
+                 v_cache=_ptr(v_cache) if not k_is_v else None, out=_ptr(out))
+    rc = lib().svo_attn_group(ctypes.byref(a))
+    if rc != 0:
+        raise ValueError("oracle attention: appended rows exceed the cache capacity")
+    return out
+
+
+def verify_attn(*, q, k_new, v_new, k_cache, v_cache, cache_len, window: int, rope_dims: int,
+                rope_base: float, scale: float, k_is_v: bool, append: bool = True,
+                q_pos_offset: int = 0, round_bf16: bool) -> np.ndarray:
+    """Whole batch.  q [B, n_q, Hq, D]; k_new/v_new [B, n_q, Hkv, D];
+    k_cache/v_cache [B, Hkv, cap, D] float32 (modified in place).
+    Returns out [B, n_q, Hq, D] fp64."""
+    q = np.asarray(q)
+    B, n_q, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, n_q, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            kc = k_cache[b, g]
+            vc = None if k_is_v else v_cache[b, g]
+            o = attn_group(q=q[b, :, g * G:(g + 1) * G, :],
+                           k_new=None if k_new is None else k_new[b, :, g, :],
+                           v_new=None if (v_new is None or k_is_v) else v_new[b, :, g, :],
+                           k_cache=kc, v_cache=vc, L=int(cache_len[b]), window=window,
+                           rope_dims=rope_dims, rope_base=rope_base, scale=scale,
+                           k_is_v=k_is_v, append=append, q_pos_offset=q_pos_offset,
+                           round_bf16=round_bf16)
+            out[b, :, g * G:(g + 1) * G, :] = o
+    return out
+
+
+# --------------------------------------------------------------------------
+# acceptance
+# --------------------------------------------------------------------------
+
+def accept_greedy(drafts, top1) -> tuple[int, np.ndarray]:
+    """One sequence: drafts [k], top1 [k+1] -> (n, tokens[k+1] padded with -1)."""
+    d, t = _i32(drafts), _i32(top1)
+    k = d.size
+    assert t.size == k + 1
+    out = np.empty(k + 1, dtype=np.int32)
+    n = lib().svo_accept_greedy(k, _ptr(d), _ptr(t), _ptr(out))
+    return int(n), out
+
+
+def accept_sample(lse, draft_logit, q_at_draft, u_accept) -> tuple[int, np.ndarray]:
+    """One sequence: lse/draft_logit of rows 0..k-1, q_i(d_i), u_i -> (n, margins[k])."""
+    lse, dl = _f64(lse), _f64(draft_logit)
+    qd, ua = _f32(q_at_draft), _f32(u_accept)
+    k = lse.size
+    margin = np.full(k, np.nan, dtype=np.float64)
+    n = lib().svo_accept_sample(k, _ptr(lse), _ptr(dl), _ptr(qd), _ptr(ua), _ptr(margin))
+    return int(n), margin
+
+
+def sample_residual(z_row, lse: float, q_row, u_row) -> tuple[int, float]:
+    z, q, u = _f64(z_row), _f32(q_row), _f32(u_row)
+    m = ctypes.c_double()
+    y = lib().svo_sample_residual(z.size, _ptr(z), float(lse), _ptr(q), _ptr(u), ctypes.byref(m))
+    return int(y), float(m.value)
+
+
+def sample_bonus(z_row, u_row) -> tuple[int, float]:
+    z, u = _f64(z_row), _f32(u_row)
+    m = ctypes.c_double()
+    y = lib().svo_sample_bonus(z.size, _ptr(z), _ptr(u), ctypes.byref(m))
+    return int(y), float(m.value)
+
+
+def toy_spec_trials(z, q, drafts, u_acc, u_tok) -> tuple[np.ndarray, np.ndarray]:
+    """Many sampling-mode steps of a context-free toy (see svo_toy_spec_trials).
+    z [V] logits, q [V] drafter probabilities, drafts [T, k], u_acc [T, k], u_tok [T, V].
+    Returns (n [T], y [T])."""
+    z, q = _f64(z), _f32(q)
+    d, ua, ut = _i32(drafts), _f32(u_acc), _f32(u_tok)
+    T, k = d.shape
+    V = z.size
+    assert ut.shape == (T, V) and ua.shape == (T, k)
+    n = np.empty(T, dtype=np.int32)
+    y = np.empty(T, dtype=np.int32)
+    lib().svo_toy_spec_trials(T, k, V, _ptr(z), _ptr(q), _ptr(d), _ptr(ua), _ptr(ut), _ptr(n), _ptr(y))
+    return n, y
