@@ -1,0 +1,274 @@
+/*
+ * specverify.h -- C ABI of libspecverify: the verify step of MTP speculative
+ * decoding on one AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the pages' statement of the problem:
+ *   verify(draft_tokens, main_kv) -> logits, then accept_longest_prefix(draft_tokens,
+ *   logits): "Gemma 4 拆解 | 多模态怎么塞进端侧，MTP drafter 又是怎么自带投机采样的"
+ *   (marsggbo.github.io), section 4.2 (speculative_step).  The k drafts and one
+ *   bonus position are scored in ONE target pass ("Accelerating Gemma 4: faster
+ *   inference with multi-token prediction drafters" (Lighthouse), section 3)
+ *   against a KV cache the drafter also reads ("Gemma 4 拆解", section 4.2:
+ *   the drafter cross-attends the target's last local / global layer cache).
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE pointers; the caller allocates and owns
+ *     all memory (inputs, outputs and the workspace).  Descriptor pointers are
+ *     HOST pointers, read before the call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t, NULL = the null
+ *     stream): no host<->device copy, no synchronisation, no allocation.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call launches nothing and returns a negative sv_status.  A failed
+ *     launch returns SV_ERR_LAUNCH.
+ *   - Data-dependent errors found on the device (a cache that would overflow,
+ *     a token id outside the vocabulary) OR bits into *dev_status (a device
+ *     int32; NULL disables reporting) and the affected sequence is skipped or
+ *     handled as documented; read the word after synchronising.
+ *   - Tensors are dense row-major with the last dimension contiguous.
+ *     Positions: query row j of sequence b sits at absolute position
+ *     cache_len[b] + q_pos_offset + j.
+ *   - The library holds no mutable global state: calls on different streams
+ *     that touch disjoint memory may overlap.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_ARG = -1,          /* a null pointer, a bad size, an inconsistent descriptor */
+  SV_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. a head_dim with no kernel) */
+  SV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace() query */
+  SV_ERR_LAUNCH = -4,       /* the HIP runtime rejected a kernel launch */
+  SV_ERR_DEVICE = -5        /* no usable gfx950 device is current */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* device status bits */
+#define SV_DEV_CACHE_OVERFLOW 0x1  /* cache_len[b] + appended rows > cache_capacity */
+#define SV_DEV_BAD_TOKEN 0x2       /* a token id outside [0, vocab) */
+#define SV_DEV_BAD_LENGTH 0x4      /* cache_len[b] < 0 */
+
+const char* sv_status_string(int status);
+/* "libspecverify <version> gfx950" */
+const char* sv_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Verify attention                                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t batch;         /* B sequences */
+  int32_t n_q;           /* query rows per sequence: k+1 in a verify step */
+  int32_t n_heads_q;     /* Hq, a multiple of n_heads_kv */
+  int32_t n_heads_kv;    /* Hkv */
+  int32_t head_dim;      /* D: 128, 256 or 512 in bf16; <= 512 in fp32 */
+  int32_t window;        /* 0: global layer; W > 0: sliding window, key t is visible
+                            to the query at position p iff p - W < t <= p */
+  int32_t rope_dims;     /* rotated leading dims: 0 (none), D (full RoPE) or a fraction
+                            of D (p-RoPE; D/4 on global layers) -- even, <= D */
+  int32_t k_is_v;        /* 1: the layer stores one tensor used as key AND value
+                            (v_cache, v_new must be NULL) */
+  int32_t append;        /* 1: verify call -- rotate and write the n_q new key (value)
+                            rows at cache rows [L, L+n_q) first; 0: read-only call (the
+                            drafter's cross-attention), k_new/v_new must be NULL */
+  int32_t q_pos_offset;  /* must be 0 when append == 1 */
+  sv_dtype dtype;        /* of q, k_new, v_new, caches and out */
+  int32_t reserved;      /* must be 0 */
+  double rope_base;      /* theta_i = rope_base^(-2i/rope_dims) */
+  float softmax_scale;   /* multiplies q.k before the softmax (1/sqrt(D)) */
+  float reserved_f;      /* must be 0 */
+  int64_t cache_capacity;/* rows per (sequence, kv head) in the cache tensors */
+  int64_t q_row_stride;  /* elements between query rows (b, j) and (b, j+1); 0 = Hq*D */
+  int64_t kv_row_stride; /* same for k_new / v_new; 0 = Hkv*D.  Lets q, k_new, v_new be
+                            column slices of one fused projection output */
+} sv_attn_desc;
+
+/* Bytes of workspace sv_verify_attn needs for this descriptor (0 on an invalid
+ * descriptor).  The workspace holds the rotated queries and the split-KV
+ * partial results; its contents are scratch, nothing survives the call. */
+size_t sv_verify_attn_workspace(const sv_attn_desc* desc);
+
+/* Verify attention over a shared KV cache, local (sliding window) or global
+ * (causal; p-RoPE and K = V on Gemma-4-style global layers: "Gemma 4 拆解",
+ * section 2; "Gemma 4 发布时未包含 MTP 数据——为什么这很重要" (flowhunt),
+ * section "什么是 Gemma 4？").
+ *
+ *   q        [B, n_q, Hq, D]   queries before RoPE (row stride q_row_stride)
+ *   k_new    [B, n_q, Hkv, D]  new keys before RoPE (append), else NULL (row stride
+ *                              kv_row_stride)
+ *   v_new    [B, n_q, Hkv, D]  new values (append and !k_is_v), else NULL
+ *   k_cache  [B, Hkv, cap, D]  rotated keys; rows [L, L+n_q) written when append
+ *   v_cache  [B, Hkv, cap, D]  values (NULL when k_is_v)
+ *   cache_len[B] int32         committed rows L_b (read only)
+ *   out      [B, n_q, Hq, D]   attention output per query head
+ *
+ * Query row j, head h (KV head h / (Hq/Hkv)) is rotated at position
+ * p = L + q_pos_offset + j and attends to the keys t <= min(p, last stored
+ * row) (and t > p - W on a window layer) with softmax(scale * q.k_t) weights.
+ * RoPE pairs dim i with dim i + rope_dims/2 (rotate-half).  A query with no
+ * visible key gets a zero row.  If L + n_q > cache_capacity on an append call
+ * the sequence is skipped (out rows untouched) and SV_DEV_CACHE_OVERFLOW set. */
+int sv_verify_attn(const sv_attn_desc* desc, const void* q, const void* k_new,
+                   const void* v_new, void* k_cache, void* v_cache,
+                   const int32_t* cache_len, void* out, void* workspace,
+                   size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* LM head + select                                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef enum {
+  SV_SELECT_GREEDY = 0,    /* per-row argmax statistics */
+  SV_SELECT_SAMPLE = 1,    /* GREEDY + a Gumbel-max draw from softmax(z) on bonus rows */
+  SV_SELECT_RESIDUAL = 2   /* draw from max(p - q, 0) for sequences that rejected */
+} sv_select_mode;
+
+/* Per-row result of the LM head (logits themselves are never written). */
+typedef struct {
+  int32_t top1_id, top2_id;  /* argmax and runner-up of z (ties: lowest id) */
+  float top1, top2;          /* their logits */
+  float lse;                 /* log sum_v exp(z_v) */
+  float draft_logit;         /* z[draft of this row], NaN when the row has none */
+  int32_t sample_id;         /* SAMPLE, bonus rows: argmax_v z_v + G(u_v); else -1 */
+  float sample_s1, sample_s2;/* winning and runner-up perturbed scores */
+} sv_row_stats;
+
+/* Per-sequence result of the accept step. */
+typedef struct {
+  int32_t n_accepted;    /* n_b in [0, k]: leading drafts accepted */
+  int32_t next_token;    /* the target's own token y_b (-1 while a RESIDUAL draw is pending) */
+  int32_t new_len;       /* committed length after the step: L_b + n_b + 1 */
+  int32_t keep_begin;    /* cache rows [keep_begin, keep_end) are kept: [L_b, L_b+n_b+1) */
+  int32_t keep_end;
+  int32_t drop_begin;    /* rows [drop_begin, drop_end) = [L_b+n_b+1, L_b+k+1) are rolled
+                            back; no data moves, the next append overwrites them */
+  int32_t drop_end;
+  int32_t hidden_row;    /* b(k+1)+n_b: the verify row whose last-layer hidden state is the
+                            drafter's next prev_hidden ("Gemma 4 拆解", section 4.2) */
+  int32_t residual_row;  /* SAMPLE: the rejected row whose residual must be drawn, else -1 */
+  float draw_margin;     /* winner minus runner-up score of the draw that gave next_token */
+} sv_accept_out;
+
+typedef struct {
+  int32_t batch;         /* B */
+  int32_t k;             /* drafts per sequence; rows = B*(k+1), row b*(k+1)+i */
+  int32_t d_model;       /* d, a multiple of 32 in bf16 */
+  int32_t vocab;         /* V, a multiple of 64 */
+  sv_select_mode mode;
+  sv_dtype dtype;        /* of hidden and w */
+} sv_lmhead_desc;
+
+size_t sv_lmhead_workspace(const sv_lmhead_desc* desc);
+
+/* LM-head skinny GEMM z = h W^T fused with a split-vocabulary select
+ * ("Gemma 4 拆解", section 4.3: the d x vocab unembed; the per-position argmax
+ * of accept_longest_prefix, section 4.2).
+ *
+ *   hidden     [B*(k+1), d]  final hidden states (RESIDUAL: row acc[b].hidden_row is used)
+ *   w          [V, d]        unembedding (tied embedding) table
+ *   drafts     [B, k] int32  d_{b,1..k}; row b*(k+1)+i reports z[drafts[b][i]] (i < k)
+ *   u_tok      [B, V] fp32   SAMPLE / RESIDUAL: uniforms in [0,1) of the token draw
+ *                            (Gumbel noise G = -log(-log u)); NULL in GREEDY
+ *   q_rows     [B, k, V] fp32 RESIDUAL: the drafter's distributions q_i; else NULL
+ *   stats      [B*(k+1)]     GREEDY/SAMPLE: written; RESIDUAL: read (lse of the row)
+ *   acc        [B]           RESIDUAL: read (residual_row, hidden_row, n_accepted) and
+ *                            next_token / draw_margin written; else NULL
+ *   out_tokens [B, k+1]      RESIDUAL: out_tokens[b][n_b] = the drawn token; else NULL
+ *
+ * RESIDUAL draws, for each sequence with residual_row >= 0,
+ * argmax over {v : r_v > 0} of log r_v + G(u_v), r_v = exp(z_v - lse) - q_v,
+ * falling back to argmax z_v + G(u_v) if every r_v is 0.  Ties: lowest id. */
+int sv_lmhead_select(const sv_lmhead_desc* desc, const void* hidden, const void* w,
+                     const int32_t* drafts, const float* u_tok, const float* q_rows,
+                     sv_row_stats* stats, sv_accept_out* acc, int32_t* out_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Accept                                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t batch;
+  int32_t k;
+  int32_t vocab;
+  sv_select_mode mode;   /* GREEDY or SAMPLE */
+} sv_accept_desc;
+
+/* Longest-accepted-prefix rule with KV append / rollback indices
+ * ("Gemma 4 拆解", section 4.1 and 4.2 accept_longest_prefix; "Gemma 4 发布时
+ * 未包含 MTP 数据", section "什么是多标记预测？": cut at the first wrong draft).
+ *
+ * GREEDY: n_b = the largest m <= k with drafts[b][i] == stats[b(k+1)+i].top1_id
+ *   for all i < m; next_token = stats[b(k+1)+n_b].top1_id.
+ * SAMPLE (standard speculative rejection sampling, temperature 1; the pages
+ *   assert only that it leaves the output distribution unchanged, "Gemma 4 与
+ *   Gemini Nano：端侧智能的架构拆解" (kongchang), section "草稿模型"): draft i
+ *   (1-based) is accepted iff u_accept[b][i-1] * q_rows[b][i-1][d_i] <
+ *   exp(stats[row i-1].draft_logit - stats[row i-1].lse), stopping at the first
+ *   rejection; if all k pass, next_token = stats[b(k+1)+k].sample_id, else it is
+ *   left -1 with residual_row = b(k+1)+n_b for sv_lmhead_select(RESIDUAL).
+ *
+ *   drafts     [B, k] int32
+ *   stats      [B*(k+1)]
+ *   q_rows     [B, k, V] fp32  SAMPLE only, else NULL
+ *   u_accept   [B, k] fp32     SAMPLE only, else NULL
+ *   cache_len  [B] int32       in: L_b, out: L_b + n_b + 1
+ *   out_tokens [B, k+1] int32  d_1..d_n, y, then -1
+ *   acc        [B]             per-sequence results (see sv_accept_out)
+ * A draft id outside [0, V) counts as a mismatch and sets SV_DEV_BAD_TOKEN. */
+int sv_accept(const sv_accept_desc* desc, const int32_t* drafts, const sv_row_stats* stats,
+              const float* q_rows, const float* u_accept, int32_t* cache_len,
+              int32_t* out_tokens, sv_accept_out* acc, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decoder-stack support (embedding, RMSNorm, projections, GeGLU)            */
+/* ------------------------------------------------------------------------ */
+
+/* x[r] = scale * table[tokens[r]] as fp32; an id outside [0, vocab) gives a zero
+ * row and sets SV_DEV_BAD_TOKEN.  table [vocab, d] in `dtype`, x [rows, d] fp32. */
+int sv_embed(int32_t rows, int32_t d_model, int32_t vocab, sv_dtype dtype,
+             const int32_t* tokens, const void* table, float scale, float* x,
+             int32_t* dev_status, void* stream);
+
+/* y = x / sqrt(mean(x^2) + eps) * gain (gain NULL = unit gain); x [rows, dim] fp32,
+ * gain [dim] fp32, y [rows, dim] in `out_dtype`. */
+int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float* gain,
+               void* y, sv_dtype out_dtype, void* stream);
+
+typedef enum {
+  SV_EPI_STORE = 0,      /* y = x W^T stored in the descriptor dtype */
+  SV_EPI_ADD_F32 = 1     /* y (fp32) += x W^T: a residual add */
+} sv_epilogue;
+
+typedef struct {
+  int32_t rows;          /* R <= 64 */
+  int32_t in_features;   /* K, a multiple of 32 in bf16 */
+  int32_t out_features;  /* N, a multiple of 64 */
+  sv_dtype dtype;        /* of x and w (and y for SV_EPI_STORE) */
+  sv_epilogue epilogue;
+} sv_linear_desc;
+
+size_t sv_linear_workspace(const sv_linear_desc* desc);
+
+/* Skinny projection y = x W^T for the few verify rows: x [R, K], W [N, K]. */
+int sv_linear(const sv_linear_desc* desc, const void* x, const void* w, void* y,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* GeGLU gate: out[r][i] = gelu_tanh(gu[r][i]) * gu[r][d_ff + i] where gu [rows, 2*d_ff]
+ * holds the gate projection then the up projection; out [rows, d_ff]; both in dtype. */
+int sv_geglu(int32_t rows, int32_t d_ff, sv_dtype dtype, const void* gate_up, void* out,
+             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

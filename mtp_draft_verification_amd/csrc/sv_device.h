@@ -1,0 +1,118 @@
+// sv_device.h -- device-side helpers shared by the libspecverify kernels
+// (CDNA4 / gfx950 only: 64-lane wavefronts, bf16 MFMA, LDS).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+namespace sv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bit-level; round-to-nearest-even, NaN kept quiet)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
+
+// 16-byte vector of 8 bf16 <-> the MFMA operand type
+union V16 {
+  uint4 u;
+  uint32_t w[4];
+  bf16x8_t b;
+};
+
+// ---------------------------------------------------------------------------
+// MFMA: D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, eight k-values each
+// (lane group l / 16 selects which eight); the accumulator lane l holds column
+// (l % 16), rows 4 * (l / 16) + {0,1,2,3}.  Any fixed assignment of k-values to
+// (lane group, slot) gives the same product as long as A and B use the same one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// wavefront reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+
+// "a beats b" in the order (value descending, id ascending); id < 0 is an empty slot.
+__device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
+  if (bi < 0) return ai >= 0;
+  if (ai < 0) return false;
+  return av > bv || (av == bv && ai < bi);
+}
+
+// running best-two under `beats`
+struct Top2 {
+  float v1, v2;
+  int i1, i2;
+  __device__ __forceinline__ void init() { v1 = v2 = kNegInf; i1 = i2 = -1; }
+  __device__ __forceinline__ void push(float v, int i) {
+    if (beats(v, i, v1, i1)) { v2 = v1; i2 = i1; v1 = v; i1 = i; }
+    else if (beats(v, i, v2, i2)) { v2 = v; i2 = i; }
+  }
+  // merge another running pair whose ids are disjoint from ours
+  __device__ __forceinline__ void merge(float ov1, int oi1, float ov2, int oi2) {
+    if (beats(ov1, oi1, v1, i1)) {
+      // other's best wins; second is the better of our best and other's second
+      if (beats(v1, i1, ov2, oi2)) { v2 = v1; i2 = i1; } else { v2 = ov2; i2 = oi2; }
+      v1 = ov1; i1 = oi1;
+    } else {
+      if (beats(ov1, oi1, v2, i2)) { v2 = ov1; i2 = oi1; }
+    }
+  }
+  __device__ __forceinline__ void merge_xor(int m) {
+    float ov1 = shfl_xor_f(v1, m), ov2 = shfl_xor_f(v2, m);
+    int oi1 = shfl_xor_i(i1, m), oi2 = shfl_xor_i(i2, m);
+    merge(ov1, oi1, ov2, oi2);
+  }
+};
+
+// online log-sum-exp state in natural-log units: value = m + log(s)
+struct LSE {
+  float m, s;
+  __device__ __forceinline__ void init() { m = kNegInf; s = 0.f; }
+  __device__ __forceinline__ void merge(float om, float os) {
+    if (om == kNegInf) return;
+    if (m == kNegInf) { m = om; s = os; return; }
+    float M = fmaxf(m, om);
+    s = s * exp2f((m - M) * kLog2e) + os * exp2f((om - M) * kLog2e);
+    m = M;
+  }
+  __device__ __forceinline__ void merge_xor(int k) {
+    float om = shfl_xor_f(m, k), os = shfl_xor_f(s, k);
+    merge(om, os);
+  }
+};
+
+__device__ __forceinline__ void set_status(int32_t* st, int32_t bits) {
+  if (st) atomicOr(st, bits);
+}
+
+// Gumbel noise from a uniform in [0,1): -log(-log u); u == 0 gives -inf.
+__device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
+
+}  // namespace sv

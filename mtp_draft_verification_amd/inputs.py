@@ -125,8 +125,9 @@ def stack_weights(cfg, seed: int = 0, device="cpu") -> dict:
     """Random-init weights of a decoder stack, N(0, 1/fan_in) entries.
 
     Per layer: wqkv [Hq*D + Hkv*D (+ Hkv*D for V), d] (q, k, v projections stacked
-    along the output dimension), wo [d, Hq*D], and with an MLP wg, wu [d_ff, d]
-    and wd [d, d_ff].  The embedding table E [vocab, d] is tied to the LM head."""
+    along the output dimension), wo [d, Hq*D], and with an MLP wgu [2*d_ff, d]
+    (gate projection rows, then up projection rows) and wd [d, d_ff].  The
+    embedding table E [vocab, d] is tied to the LM head."""
     dt = cfg.dtype
     d = cfg.d_model
     W = {"E": normal((cfg.vocab, d), d ** -0.5, seed, "E", device, dt), "layers": []}
@@ -137,8 +138,7 @@ def stack_weights(cfg, seed: int = 0, device="cpu") -> dict:
         lw = {"wqkv": normal((nout, d), d ** -0.5, seed, f"L{i}.wqkv", device, dt),
               "wo": normal((d, nq), nq ** -0.5, seed, f"L{i}.wo", device, dt)}
         if cfg.d_ff:
-            lw["wg"] = normal((cfg.d_ff, d), d ** -0.5, seed, f"L{i}.wg", device, dt)
-            lw["wu"] = normal((cfg.d_ff, d), d ** -0.5, seed, f"L{i}.wu", device, dt)
+            lw["wgu"] = normal((2 * cfg.d_ff, d), d ** -0.5, seed, f"L{i}.wgu", device, dt)
             lw["wd"] = normal((d, cfg.d_ff), cfg.d_ff ** -0.5, seed, f"L{i}.wd", device, dt)
         W["layers"].append(lw)
     return W

@@ -1,0 +1,156 @@
+"""The verify step of a decoder stack on the GPU, as a sequence of C-ABI calls.
+
+speculative_step ("Gemma 4 拆解" (marsggbo), section 4.2): ONE target forward
+over the rows [last committed token, d_1..d_k] of every sequence (main_model.verify),
+then accept_longest_prefix.  Here that forward is, per layer,
+
+    a = rmsnorm(x)                 sv_rmsnorm      (x: fp32 residual stream)
+    qkv = a Wqkv^T                 sv_linear       (q, k, v in one projection)
+    o = attn(q, k, v; cache)       sv_verify_attn  (appends the k+1 new rows)
+    x += o Wo^T                    sv_linear (SV_EPI_ADD_F32)
+    m = rmsnorm(x); gu = m Wgu^T   sv_rmsnorm, sv_linear
+    f = gelu_tanh(g) * u           sv_geglu
+    x += f Wd^T                    sv_linear (SV_EPI_ADD_F32)
+
+then h = rmsnorm(x), sv_lmhead_select over the tied embedding and sv_accept.
+Every call is enqueued on one stream with no host synchronisation; all buffers
+are allocated once up front, so a step allocates nothing.  This module only
+marshals arguments: the arithmetic is the library's.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib as L
+
+
+def attn_desc(layer, batch: int, n_q: int, cap: int, dtype: str, append: bool = True,
+              q_pos_offset: int = 0, q_row_stride: int = 0, kv_row_stride: int = 0) -> L.AttnDesc:
+    return L.AttnDesc(batch=batch, n_q=n_q, n_heads_q=layer.n_heads_q, n_heads_kv=layer.n_heads_kv,
+                      head_dim=layer.head_dim, window=layer.window, rope_dims=layer.rope_dims,
+                      k_is_v=int(layer.k_is_v), append=int(append), q_pos_offset=q_pos_offset,
+                      dtype=L.SV_BF16 if dtype == "bf16" else L.SV_F32, reserved=0,
+                      rope_base=float(layer.rope_base), softmax_scale=float(layer.scale), reserved_f=0.0,
+                      cache_capacity=int(cap), q_row_stride=int(q_row_stride),
+                      kv_row_stride=int(kv_row_stride))
+
+
+class VerifyStack:
+    """Device-resident state of a stack: weights, caches, committed lengths, buffers."""
+
+    def __init__(self, cfg, weights: dict, caches: list, cache_len: torch.Tensor, device="cuda"):
+        self.cfg = cfg
+        self.W = weights
+        self.caches = caches
+        self.cache_len = cache_len
+        self.dev = torch.device(device)
+        self.bf16 = cfg.dtype == "bf16"
+        self.dt = L.SV_BF16 if self.bf16 else L.SV_F32
+        tdt = torch.bfloat16 if self.bf16 else torch.float32
+        if not cfg.norm and self.bf16:
+            raise ValueError("a bf16 stack needs the RMSNorm to produce its bf16 activations")
+        B, k, d = cfg.batch, cfg.k, cfg.d_model
+        self.R = R = B * (k + 1)
+        self.cap = caches[0]["k"].shape[2]
+        dev = self.dev
+        z = lambda *s, dtype=tdt: torch.zeros(*s, dtype=dtype, device=dev)
+        self.x = z(R, d, dtype=torch.float32)
+        self.a = z(R, d)
+        nout = max(ly.n_heads_q * ly.head_dim + (1 if ly.k_is_v else 2) * ly.n_heads_kv * ly.head_dim
+                   for ly in cfg.layers)
+        self.qkv = z(R, nout)
+        self.o = z(R, max(ly.n_heads_q * ly.head_dim for ly in cfg.layers))
+        self.gu = z(R, 2 * cfg.d_ff) if cfg.d_ff else None
+        self.f = z(R, cfg.d_ff) if cfg.d_ff else None
+        self.h = self.a  # final norm output reuses the activation buffer
+        ws = max(L.sv_verify_attn_workspace(attn_desc(ly, B, k + 1, self.cap, cfg.dtype)) for ly in cfg.layers)
+        self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.lin_ws = torch.empty(max([self._lin_ws(*s) for s in self._lin_shapes()] + [256]),
+                                  dtype=torch.uint8, device=dev)
+        self.lm_desc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=cfg.vocab, mode=L.SV_SELECT_GREEDY,
+                                    dtype=self.dt)
+        self.lm_ws = torch.empty(max(L.sv_lmhead_workspace(self.lm_desc), 256), dtype=torch.uint8, device=dev)
+        self.stats = torch.zeros(R, L.ROW_STATS_WORDS, dtype=torch.int32, device=dev)
+        self.acc = torch.zeros(B, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+        self.out_tokens = torch.zeros(B, k + 1, dtype=torch.int32, device=dev)
+        self.dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.acc_desc = L.AcceptDesc(batch=B, k=k, vocab=cfg.vocab, mode=L.SV_SELECT_GREEDY)
+        self.attn_descs = [
+            attn_desc(ly, B, k + 1, self.cap, cfg.dtype,
+                      q_row_stride=self._nout(ly), kv_row_stride=self._nout(ly)) for ly in cfg.layers]
+
+    @staticmethod
+    def _nout(ly) -> int:
+        return ly.n_heads_q * ly.head_dim + (1 if ly.k_is_v else 2) * ly.n_heads_kv * ly.head_dim
+
+    def _lin_shapes(self):
+        cfg, R = self.cfg, self.R
+        for ly in cfg.layers:
+            yield R, cfg.d_model, self._nout(ly), L.SV_EPI_STORE
+            yield R, ly.n_heads_q * ly.head_dim, cfg.d_model, L.SV_EPI_ADD_F32
+            if cfg.d_ff:
+                yield R, cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_STORE
+                yield R, cfg.d_ff, cfg.d_model, L.SV_EPI_ADD_F32
+
+    def _lin_ws(self, R, K, N, epi) -> int:
+        return L.sv_linear_workspace(L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt,
+                                                  epilogue=epi))
+
+    def _linear(self, x, w, y, epi, stream):
+        R, K = self.R, w.shape[1]
+        N = w.shape[0]
+        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi)
+        L.sv_linear(desc, x, w, y, self.lin_ws, stream)
+
+    def _norm(self, x, y, stream):
+        if self.cfg.norm:
+            L.sv_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, None, y, self.dt, stream)
+            return y
+        return x  # fp32 stack without norms feeds the residual stream directly
+
+    # ------------------------------------------------------------------
+    def forward(self, tokens: torch.Tensor, stream=None) -> torch.Tensor:
+        """Verify forward of tokens [B, k+1] int32 (device); appends the k+1 new
+        rows of every layer's cache; returns the final hidden states [R, d]."""
+        cfg = self.cfg
+        d = cfg.d_model
+        L.sv_embed(self.R, d, cfg.vocab, self.dt, tokens, self.W["E"], math.sqrt(d), self.x,
+                   self.dev_status, stream)
+        for ly, lw, cache, desc in zip(cfg.layers, self.W["layers"], self.caches, self.attn_descs):
+            a = self._norm(self.x, self.a, stream)
+            nq_f = ly.n_heads_q * ly.head_dim
+            nk_f = ly.n_heads_kv * ly.head_dim
+            nout = self._nout(ly)
+            qkv = self.qkv[:, :nout] if nout == self.qkv.shape[1] else self.qkv.view(-1)[:self.R * nout].view(self.R, nout)
+            self._linear(a, lw["wqkv"], qkv, L.SV_EPI_STORE, stream)
+            esz = qkv.element_size()
+            base = qkv.data_ptr()
+            q_ptr = base
+            k_ptr = base + nq_f * esz
+            v_ptr = None if ly.k_is_v else base + (nq_f + nk_f) * esz
+            o = self.o.view(-1)[:self.R * nq_f].view(self.R, nq_f)
+            L.sv_verify_attn(desc, q_ptr, k_ptr, v_ptr, cache["k"], cache["v"], self.cache_len, o,
+                             self.attn_ws, self.dev_status, stream)
+            self._linear(o, lw["wo"], self.x, L.SV_EPI_ADD_F32, stream)
+            if cfg.d_ff:
+                m = self._norm(self.x, self.a, stream)
+                self._linear(m, lw["wgu"], self.gu, L.SV_EPI_STORE, stream)
+                L.sv_geglu(self.R, cfg.d_ff, self.dt, self.gu, self.f, stream)
+                self._linear(self.f, lw["wd"], self.x, L.SV_EPI_ADD_F32, stream)
+        return self._norm(self.x, self.h, stream)
+
+    def select(self, h: torch.Tensor, drafts: torch.Tensor, stream=None) -> None:
+        L.sv_lmhead_select(self.lm_desc, h, self.W["E"], drafts, None, None, self.stats, None, None,
+                           self.lm_ws, stream)
+
+    def accept(self, drafts: torch.Tensor, stream=None) -> None:
+        L.sv_accept(self.acc_desc, drafts, self.stats, None, None, self.cache_len, self.out_tokens, self.acc,
+                    self.dev_status, stream)
+
+    def step(self, tokens: torch.Tensor, drafts: torch.Tensor, stream=None) -> None:
+        """One greedy verify step: forward, LM-head select, accept (commits on device)."""
+        h = self.forward(tokens, stream)
+        self.select(h, drafts, stream)
+        self.accept(drafts, stream)

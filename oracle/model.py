@@ -38,8 +38,9 @@ def _to_f64(w: np.ndarray) -> np.ndarray:
 class OracleModel:
     """Geometry (a StackConfig-like object) plus host weights.
 
-    weights: {"E": [V, d], "layers": [{"wqkv", "wo", ("wg", "wu", "wd")}]}, each
-    array fp32 or uint16 bf16 bits."""
+    weights: {"E": [V, d], "layers": [{"wqkv", "wo", ("wgu", "wd")}]}, each array
+    fp32 or uint16 bf16 bits; wqkv stacks the q, k (and v) projections along the
+    output dimension, wgu the gate then the up projection."""
 
     def __init__(self, cfg, weights: dict):
         self.cfg = cfg
@@ -84,8 +85,8 @@ class OracleModel:
             x = x + linear(o, lw["wo"])
             if cfg.d_ff:
                 m = self._r(rmsnorm(x, cfg.eps) if cfg.norm else x)
-                g = self._r(linear(m, lw["wg"]))
-                u = self._r(linear(m, lw["wu"]))
+                g = self._r(linear(m, lw["wgu"][:cfg.d_ff]))
+                u = self._r(linear(m, lw["wgu"][cfg.d_ff:]))
                 f = self._r(geglu(g, u))
                 x = x + linear(f, lw["wd"])
         h = self._r(rmsnorm(x, cfg.eps) if cfg.norm else x)

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad arguments on the host (no GPU needed: nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mtp_draft_verification_amd._lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_\w+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported():
+    lib = L.load()
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(L.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in L.sv_version()
+    for st in (L.SV_OK, L.SV_ERR_ARG, L.SV_ERR_UNSUPPORTED, L.SV_ERR_WORKSPACE, L.SV_ERR_LAUNCH,
+               L.SV_ERR_DEVICE):
+        assert L.sv_status_string(st).startswith("SV_")
+
+
+def _desc(**kw):
+    base = dict(batch=2, n_q=5, n_heads_q=16, n_heads_kv=8, head_dim=256, window=1024, rope_dims=256,
+                k_is_v=0, append=1, q_pos_offset=0, dtype=L.SV_BF16, reserved=0, rope_base=1e4,
+                softmax_scale=1 / 16, reserved_f=0.0, cache_capacity=5000, q_row_stride=0, kv_row_stride=0)
+    base.update(kw)
+    return L.AttnDesc(**base)
+
+
+def test_attention_descriptor_validation():
+    lib = L.load()
+    fake = ctypes.c_void_p(4096)
+    big = 1 << 40
+
+    def call(d, **ptrs):
+        p = dict(q=fake, kn=fake, vn=fake, kc=fake, vc=fake, cl=fake, out=fake, ws=fake)
+        p.update(ptrs)
+        return lib.sv_verify_attn(ctypes.byref(d), p["q"], p["kn"], p["vn"], p["kc"], p["vc"], p["cl"],
+                                  p["out"], p["ws"], big, None, None)
+
+    assert L.sv_verify_attn_workspace(_desc()) > 0
+    bad = [dict(batch=0), dict(n_q=0), dict(n_heads_q=12, n_heads_kv=8), dict(head_dim=200, rope_dims=200),
+           dict(rope_dims=300), dict(rope_dims=7), dict(window=-1), dict(k_is_v=2), dict(append=1, q_pos_offset=3),
+           dict(reserved=1), dict(cache_capacity=0), dict(softmax_scale=0.0), dict(dtype=7),
+           dict(q_row_stride=100), dict(rope_base=0.5)]
+    for kw in bad:
+        assert call(_desc(**kw)) in (L.SV_ERR_ARG, L.SV_ERR_UNSUPPORTED), kw
+        assert L.sv_verify_attn_workspace(_desc(**kw)) == 0, kw
+    assert call(_desc(head_dim=64, rope_dims=64)) == L.SV_ERR_UNSUPPORTED      # no bf16 kernel for D=64
+    assert call(_desc(n_q=9, n_heads_q=64, n_heads_kv=8)) == L.SV_ERR_UNSUPPORTED  # 72 rows > 64
+    assert call(_desc(), q=None) == L.SV_ERR_ARG
+    assert call(_desc(), vn=None) == L.SV_ERR_ARG                            # V needed on local layers
+    assert call(_desc(k_is_v=1)) == L.SV_ERR_ARG                             # V given on a K=V layer
+    assert call(_desc(append=0)) == L.SV_ERR_ARG                             # new rows given read-only
+    assert call(_desc(), ws=None) == L.SV_ERR_WORKSPACE
+    d = _desc()
+    small = L.sv_verify_attn_workspace(d) - 1
+    assert lib.sv_verify_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, small,
+                              None, None) == L.SV_ERR_WORKSPACE
+    assert call(_desc(dtype=L.SV_F32, cache_capacity=100000)) == L.SV_ERR_UNSUPPORTED
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = L.load()
+    fake = ctypes.c_void_p(4096)
+    lm = L.LMHeadDesc(batch=8, k=4, d_model=3840, vocab=262144, mode=L.SV_SELECT_GREEDY, dtype=L.SV_BF16)
+    assert L.sv_lmhead_workspace(lm) > 0
+    for kw in (dict(vocab=1000), dict(d_model=100), dict(batch=16), dict(mode=9), dict(batch=0)):
+        d = L.LMHeadDesc(**{**dict(batch=8, k=4, d_model=3840, vocab=262144, mode=0, dtype=1), **kw})
+        assert lib.sv_lmhead_select(ctypes.byref(d), fake, fake, fake, None, None, fake, None, None, fake,
+                                    1 << 40, None) in (L.SV_ERR_ARG, L.SV_ERR_UNSUPPORTED), kw
+    samp = L.LMHeadDesc(batch=8, k=4, d_model=3840, vocab=262144, mode=L.SV_SELECT_SAMPLE, dtype=L.SV_BF16)
+    assert lib.sv_lmhead_select(ctypes.byref(samp), fake, fake, fake, None, None, fake, None, None, fake,
+                                1 << 40, None) == L.SV_ERR_ARG            # no uniforms
+    assert lib.sv_lmhead_select(ctypes.byref(lm), fake, fake, fake, None, None, fake, None, None, fake,
+                                16, None) == L.SV_ERR_WORKSPACE
+    ad = L.AcceptDesc(batch=4, k=4, vocab=1000, mode=L.SV_SELECT_SAMPLE)
+    assert lib.sv_accept(ctypes.byref(ad), fake, fake, None, None, fake, fake, fake, None, None) == L.SV_ERR_ARG
+    ld = L.LinearDesc(rows=20, in_features=3840, out_features=100, dtype=L.SV_BF16, epilogue=0)
+    assert lib.sv_linear(ctypes.byref(ld), fake, fake, fake, fake, 1 << 40, None) == L.SV_ERR_ARG
+    ld = L.LinearDesc(rows=80, in_features=3840, out_features=128, dtype=L.SV_BF16, epilogue=0)
+    assert lib.sv_linear(ctypes.byref(ld), fake, fake, fake, fake, 1 << 40, None) == L.SV_ERR_UNSUPPORTED
+    assert lib.sv_embed(0, 128, 10, L.SV_BF16, fake, fake, 1.0, fake, None, None) == L.SV_ERR_ARG
+    assert lib.sv_rmsnorm(4, 128, -1.0, fake, None, fake, L.SV_BF16, None) == L.SV_ERR_ARG
+    assert lib.sv_geglu(4, 128, 5, fake, fake, None) == L.SV_ERR_ARG
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = L.load()
+    fake = ctypes.c_void_p(4096)
+    d = _desc()
+    assert lib.sv_verify_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40,
+                              None, None) == L.SV_ERR_DEVICE

@@ -1,0 +1,244 @@
+"""GPU parity of sv_lmhead_select and sv_accept against the oracle.
+
+Logits are never stored by the kernel; its per-row statistics are compared with
+the oracle's full-logit statistics: top-1/top-2 logits, log-sum-exp and the
+draft's logit within 2e-2 absolute; token ids and accept lengths bit-exact
+wherever the oracle's deciding margin exceeds 1e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mtp_draft_verification_amd._lib as L
+from mtp_draft_verification_amd import configs, inputs
+from gpu_util import gpu, host, need_gpu, say
+from test_golden import load_accept_cases
+
+ATOL = 2e-2
+MARGIN = 1e-2
+
+
+def lm_inputs(B, k, d, V, seed, dev, dtype="bf16"):
+    R = B * (k + 1)
+    h = inputs.normal((R, d), 1.0, seed, "h", dev, dtype)
+    W = inputs.normal((V, d), d ** -0.5, seed, "W", dev, dtype)
+    return h, W
+
+
+def w_host(W):
+    return inputs.bf16_bits(W) if W.dtype == torch.bfloat16 else host(W)
+
+
+def run_select(h, W, drafts, B, k, mode, dev, u_tok=None, q_rows=None, stats=None, acc=None,
+               out_tokens=None):
+    V, d = W.shape
+    dt = L.SV_BF16 if W.dtype == torch.bfloat16 else L.SV_F32
+    desc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=mode, dtype=dt)
+    ws = torch.empty(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
+    if stats is None:
+        stats = torch.full((B * (k + 1), L.ROW_STATS_WORDS), -7, dtype=torch.int32, device=dev)
+    L.sv_lmhead_select(desc, h, W, drafts, u_tok, q_rows, stats, acc, out_tokens, ws)
+    return stats
+
+
+def check_stats(g, o, tag):
+    assert abs(float(g["top1"]) - o["top1"]) <= ATOL, (tag, g, o)
+    assert abs(float(g["top2"]) - o["top2"]) <= ATOL, (tag, g, o)
+    assert abs(float(g["lse"]) - o["lse"]) <= ATOL, (tag, g, o)
+    if np.isnan(o["draft_logit"]):
+        assert np.isnan(float(g["draft_logit"])), (tag, g, o)
+    else:
+        assert abs(float(g["draft_logit"]) - o["draft_logit"]) <= ATOL, (tag, g, o)
+    if o["top1"] - o["top2"] > MARGIN:
+        assert int(g["top1_id"]) == o["top1_id"], (tag, g, o)
+
+
+def greedy_case(B, k, d, V, seed, dtype="bf16", rows=None):
+    dev = need_gpu()
+    say(f"[lmhead greedy] B={B} k={k} d={d} V={V} dtype={dtype} seed={seed}")
+    h, W = lm_inputs(B, k, d, V, seed, dev, dtype)
+    drafts = inputs.randint((B, k), 0, V - 1, seed, "drafts", dev)
+    stats = run_select(h, W, drafts, B, k, L.SV_SELECT_GREEDY, dev)
+    torch.cuda.synchronize()
+    gs = L.decode_row_stats(stats)
+    rows = rows if rows is not None else range(B * (k + 1))
+    hh = host(h)
+    z = oracle.lmhead(hh[list(rows)], w_host(W))
+    dh = drafts.cpu().numpy()
+    for zi, r in enumerate(rows):
+        b, i = divmod(r, k + 1)
+        o = oracle.row_stats(z[zi], int(dh[b, i]) if i < k else -1)
+        check_stats(gs[r], o, f"row {r}")
+        assert int(gs[r]["sample_id"]) == -1
+    return gs
+
+
+@gpu
+def test_greedy_small_bf16():
+    greedy_case(2, 4, 256, 4096, 1)
+    greedy_case(8, 4, 128, 2048, 2)       # 40 rows: three row tiles
+    greedy_case(1, 0, 64, 512, 3)         # plain decoding row
+    greedy_case(12, 4, 96, 1024, 4)       # 60 rows: four row tiles
+
+
+@gpu
+def test_greedy_fp32_tiny():
+    greedy_case(1, 3, 128, 1024, 0, dtype="f32")
+
+
+@gpu
+def test_greedy_ties_lowest_id():
+    dev = need_gpu()
+    B, k, d, V = 1, 1, 64, 1024
+    W = inputs.normal((V, d), d ** -0.5, 5, "W", dev)
+    W[700] = W[300]
+    W[900] = W[300]
+    h = W[300:302].clone() * 4.0
+    drafts = torch.tensor([[900]], dtype=torch.int32, device=dev)
+    gs = L.decode_row_stats(run_select(h, W, drafts, B, k, L.SV_SELECT_GREEDY, dev))
+    assert int(gs[0]["top1_id"]) == 300 and int(gs[0]["top2_id"]) == 700
+    assert float(gs[0]["top1"]) == float(gs[0]["top2"]) == float(gs[0]["draft_logit"])
+
+
+@gpu
+def test_full_size_greedy_sampled_rows():
+    """262,144-entry vocabulary, d = 3840, B = 8, k = 4 (40 rows); the oracle
+    recomputes four rows in full."""
+    cfg = configs.LMHEAD_B8
+    greedy_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0, rows=[0, 4, 21, 39])
+
+
+def stats_tensor(top1, dev):
+    """Row statistics with the given argmax ids (other fields filled plausibly)."""
+    R = len(top1)
+    a = np.zeros(R, dtype=L.ROW_STATS_DTYPE)
+    a["top1_id"] = top1
+    a["top2_id"] = -1
+    a["top1"] = 1.0
+    a["top2"] = 0.0
+    a["sample_id"] = -1
+    return torch.from_numpy(a.view(np.int32).reshape(R, L.ROW_STATS_WORDS).copy()).to(dev)
+
+
+@gpu
+def test_accept_golden_cases():
+    dev = need_gpu()
+    for drafts, top1, n, emitted, src in load_accept_cases():
+        k = len(drafts)
+        d = torch.tensor([drafts], dtype=torch.int32, device=dev)
+        st = stats_tensor(top1, dev)
+        cl = torch.tensor([1000], dtype=torch.int32, device=dev)
+        out = torch.full((1, k + 1), -9, dtype=torch.int32, device=dev)
+        acc = torch.zeros(1, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+        L.sv_accept(L.AcceptDesc(batch=1, k=k, vocab=100, mode=L.SV_SELECT_GREEDY), d, st, None, None, cl,
+                    out, acc)
+        torch.cuda.synchronize()
+        a = L.decode_accept_out(acc)[0]
+        assert int(a["n_accepted"]) == n, (drafts, top1, src)
+        assert out[0, :n + 1].tolist() == emitted
+        assert all(x == -1 for x in out[0, n + 1:].tolist())
+        assert int(cl.item()) == 1000 + n + 1 == int(a["new_len"])
+        assert (int(a["keep_begin"]), int(a["keep_end"])) == (1000, 1000 + n + 1)
+        assert (int(a["drop_begin"]), int(a["drop_end"])) == (1000 + n + 1, 1000 + k + 1)
+        assert int(a["hidden_row"]) == n and int(a["residual_row"]) == -1
+
+
+@gpu
+def test_accept_bad_token_is_a_mismatch():
+    dev = need_gpu()
+    d = torch.tensor([[3, 500]], dtype=torch.int32, device=dev)
+    st = stats_tensor([3, 500, 7], dev)
+    cl = torch.tensor([5], dtype=torch.int32, device=dev)
+    out = torch.zeros((1, 3), dtype=torch.int32, device=dev)
+    acc = torch.zeros(1, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    L.sv_accept(L.AcceptDesc(batch=1, k=2, vocab=100, mode=L.SV_SELECT_GREEDY), d, st, None, None, cl, out,
+                acc, status)
+    torch.cuda.synchronize()
+    assert int(L.decode_accept_out(acc)[0]["n_accepted"]) == 1
+    assert int(status.item()) & L.SV_DEV_BAD_TOKEN
+
+
+def sampling_case(B, k, d, V, seed, rows_check=None, alpha=0.1, q_from_p=None):
+    """Pass 1 (stats + bonus draws), accept, pass 2 (residual draws) vs the oracle."""
+    dev = need_gpu()
+    say(f"[lmhead sample] B={B} k={k} d={d} V={V} seed={seed} q_from_p={q_from_p}")
+    h, W = lm_inputs(B, k, d, V, seed, dev)
+    R = B * (k + 1)
+    Wh = w_host(W)
+    hh = host(h)
+    seqs = rows_check if rows_check is not None else list(range(B))
+    if q_from_p is not None:
+        # drafter distributions close to the target's own rows, so drafts are often accepted
+        zz = oracle.lmhead(hh, Wh).reshape(B, k + 1, V)
+        p = np.exp(zz - zz.max(axis=2, keepdims=True))
+        p /= p.sum(axis=2, keepdims=True)
+        noise = inputs.dirichlet_rows(B * k, V, 1.0, seed, "qnoise", "cpu").numpy().reshape(B, k, V)
+        q = (1 - q_from_p) * p[:, :k] + q_from_p * noise
+        q_rows = torch.from_numpy(q.astype(np.float32)).to(dev)
+    else:
+        q_rows = inputs.dirichlet_rows(B * k, V, alpha, seed, "q", dev).view(B, k, V)
+    drafts = inputs.categorical(q_rows.view(B * k, V), seed, "drafts").view(B, k)
+    u_acc = inputs.uniform((B, k), seed, "u_acc", dev)
+    u_tok = inputs.uniform((B, V), seed, "u_tok", dev)
+    stats = run_select(h, W, drafts, B, k, L.SV_SELECT_SAMPLE, dev, u_tok=u_tok)
+    cl = torch.full((B,), 100, dtype=torch.int32, device=dev)
+    out = torch.full((B, k + 1), -9, dtype=torch.int32, device=dev)
+    acc = torch.zeros(B, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+    L.sv_accept(L.AcceptDesc(batch=B, k=k, vocab=V, mode=L.SV_SELECT_SAMPLE), drafts, stats, q_rows, u_acc,
+                cl, out, acc)
+    res_desc_stats = stats
+    run_select(h, W, drafts, B, k, L.SV_SELECT_RESIDUAL, dev, u_tok=u_tok, q_rows=q_rows,
+               stats=res_desc_stats, acc=acc, out_tokens=out)
+    torch.cuda.synchronize()
+    gs = L.decode_row_stats(stats)
+    ga = L.decode_accept_out(acc)
+    outh = out.cpu().numpy()
+    qh, dh, uah, uth = host(q_rows), drafts.cpu().numpy(), host(u_acc), host(u_tok)
+    n_checked = excused = 0
+    for b in seqs:
+        z = oracle.lmhead(hh[b * (k + 1):(b + 1) * (k + 1)], Wh)
+        st = [oracle.row_stats(z[i], int(dh[b, i]) if i < k else -1) for i in range(k + 1)]
+        for i in range(k + 1):
+            check_stats(gs[b * (k + 1) + i], st[i], f"b{b} row{i}")
+        lse = np.array([s["lse"] for s in st[:k]])
+        dl = np.array([s["draft_logit"] for s in st[:k]])
+        qd = np.array([qh[b, i, dh[b, i]] for i in range(k)], dtype=np.float32)
+        n, margins = oracle.accept_sample(lse, dl, qd, uah[b])
+        tested = margins[:min(n + 1, k)]
+        if np.any(np.abs(tested) <= MARGIN):
+            excused += 1
+            continue
+        assert int(ga[b]["n_accepted"]) == n, (b, n, ga[b], margins)
+        if n == k:
+            y, m = oracle.sample_bonus(z[k], uth[b])
+        else:
+            y, m = oracle.sample_residual(z[n], st[n]["lse"], qh[b, n], uth[b])
+        if m > MARGIN:
+            assert int(ga[b]["next_token"]) == y, (b, y, ga[b])
+            assert outh[b, n] == y
+            assert list(outh[b, :n]) == list(dh[b, :n])
+            n_checked += 1
+        else:
+            excused += 1
+        assert int(ga[b]["residual_row"]) == (-1 if n == k else b * (k + 1) + n)
+    say(f"[lmhead sample] checked {n_checked} sequences, excused {excused}; "
+        f"n = {ga['n_accepted'].tolist()}")
+    return ga
+
+
+@gpu
+def test_sampling_small_rejects():
+    sampling_case(4, 4, 128, 2048, 1)
+
+
+@gpu
+def test_sampling_small_accepts():
+    ga = sampling_case(8, 4, 128, 2048, 2, q_from_p=0.05)
+    assert ga["n_accepted"].max() >= 2          # the bonus and mid-prefix paths are exercised
+
+
+@gpu
+def test_full_size_sampling_sampled_sequences():
+    cfg = configs.LMHEAD_B8
+    sampling_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0, rows_check=[0, 5])
