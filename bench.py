@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Verify-step throughput of libspecverify on one MI355X.
+
+Workload: the full verify step of a synthetic random-init decoder stack
+(6 layers, 5 sliding-window : 1 global, d = 3840, d_ff = 15360 GeGLU, RMSNorm,
+tied 262,144-token LM head, committed context 131,072, k = 4 drafts), batch 8 by
+default (batch 1 is measured in the same run as a sweep point).
+
+A step is one pass of the whole hot path: embedding, every layer's
+projections, verify attention with KV append (local window and global K=V
+p-RoPE layers), the fused LM-head select and the accept kernel with KV
+commit/rollback.  Drafts follow the workload recipe: the target's own greedy
+continuation with each draft replaced by a random token with probability 0.2.
+They are recorded in an untimed pass (k single-row passes per step produce the
+continuation) and the recorded steps are then replayed back to back in the
+timed region from the same starting state, which reproduces the same
+trajectory (the kernels are deterministic; this is checked).
+
+value = committed tokens (sum over steps and sequences of n_b + 1) / time.
+roofline: the kernel call that takes the most time per step, its algorithmic
+bytes / its mean duration (HIP events on the step's stream, timed region).
+cpu_baseline: the fp64 oracle on one sequence of the same step (host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify-step tokens/s (k=4, batch 1/8) + attn/LM-head HBM GB/s as % of peak"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--ctx", type=int, default=131072)
+    ap.add_argument("--sweep", default="1", help="extra batch sizes, comma separated ('' for none)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="short run for profilers: no sweep, no oracle")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mtp_draft_verification_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes of the calls of one step (what the method must move)
+# ---------------------------------------------------------------------------
+def call_bytes(cfg, lens) -> dict:
+    """Bytes each named call must move once, for committed lengths `lens` (per sequence)."""
+    B, k, d, R = cfg.batch, cfg.k, cfg.d_model, cfg.batch * (cfg.k + 1)
+    nq = k + 1
+    e = 2  # bf16
+    out = {"lmhead": cfg.vocab * d * e + R * d * e}
+    for i, ly in enumerate(cfg.layers):
+        H, Hk, D = ly.n_heads_q, ly.n_heads_kv, ly.head_dim
+        tensors = 1 if ly.k_is_v else 2
+        keys = 0
+        for L in lens:
+            n = L + nq
+            keys += min(n, ly.window + k) if ly.window else n
+        kv = keys * Hk * D * e * tensors
+        qio = B * nq * H * D * e * 2 + B * nq * Hk * D * e * tensors
+        out[f"L{i}.attn"] = kv + qio
+        nout = H * D + Hk * D * tensors
+        out[f"L{i}.qkv"] = nout * d * e + R * d * e + R * nout * e
+        out[f"L{i}.o"] = d * H * D * e + R * H * D * e + R * d * 4 * 2
+        if cfg.d_ff:
+            out[f"L{i}.gu"] = 2 * cfg.d_ff * d * e + R * d * e + R * 2 * cfg.d_ff * e
+            out[f"L{i}.down"] = d * cfg.d_ff * e + R * cfg.d_ff * e + R * d * 4 * 2
+    return out
+
+
+def load_traffic(kernel_call: str) -> float | None:
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (otherwise None)."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get("calls", {}).get(kernel_call)
+    if not ent or t.get("source_digest") != source_digest():
+        return None
+    return float(ent["bytes_per_call"])
+
+
+# ---------------------------------------------------------------------------
+def run_workload(cfg, W, steps, warmup, seed, dev, time_calls=None):
+    import numpy as np
+    import torch
+
+    from mtp_draft_verification_amd import _lib as L
+    from mtp_draft_verification_amd import inputs
+    from mtp_draft_verification_amd.step import VerifyStack
+
+    B, k = cfg.batch, cfg.k
+    cap = cfg.ctx + (k + 1) * (steps + 2) + 16
+    log(f"B={B}: caches (capacity {cap})")
+    caches = inputs.stack_caches(cfg, seed, dev, capacity=cap, fill_from=0)
+    cl = torch.full((B,), cfg.ctx, dtype=torch.int32, device=dev)
+    vs = VerifyStack(cfg, W, caches, cl, dev)
+    cfg0 = dataclasses.replace(cfg, k=0)
+    cl_ar = torch.empty_like(cl)
+    ar = VerifyStack(cfg0, W, caches, cl_ar, dev)
+    no_drafts = torch.empty((B, 0), dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(seed)
+
+    # warm-up: random drafts, then back to the starting state
+    for _ in range(warmup):
+        tok = torch.randint(0, cfg.vocab, (B, k + 1), dtype=torch.int32, device=dev)
+        vs.step(tok, tok[:, 1:].contiguous())
+    torch.cuda.synchronize()
+    cl.fill_(cfg.ctx)
+
+    # record the trajectory (untimed)
+    last = torch.randint(0, cfg.vocab, (B,), dtype=torch.int32, device=dev)
+    rec_tok, rec_dr, rec_n, rec_len = [], [], [], []
+    for s in range(steps):
+        cl_ar.copy_(cl)
+        cont = torch.empty((B, k), dtype=torch.int32, device=dev)
+        cur = last.view(B, 1).clone()
+        for i in range(k):
+            ar.step(cur, no_drafts)
+            cur = ar.out_tokens[:, :1].clone()
+            cont[:, i] = cur[:, 0]
+        keep = torch.from_numpy(rng.random((B, k)) < cfg.draft_match).to(dev)
+        other = torch.from_numpy(rng.integers(0, cfg.vocab - 1, (B, k)).astype(np.int32)).to(dev)
+        other = torch.where(other >= cont, other + 1, other)
+        drafts = torch.where(keep, cont, other).contiguous()
+        tokens = torch.cat([last.view(B, 1), drafts], dim=1).contiguous()
+        rec_len.append(cl.cpu().numpy().copy())
+        vs.step(tokens, drafts)
+        acc = L.decode_accept_out(vs.acc)
+        rec_tok.append(tokens)
+        rec_dr.append(drafts)
+        rec_n.append(acc["n_accepted"].copy())
+        last = vs.acc[:, 1].clone()
+    torch.cuda.synchronize()
+    assert int(vs.dev_status.item()) == 0, "device status set while recording"
+    committed = int(sum(int((n + 1).sum()) for n in rec_n))
+    mean_lens = np.mean(np.stack(rec_len), axis=0)
+
+    def replay(timers):
+        cl.fill_(cfg.ctx)
+        vs.timers = timers
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            vs.step(rec_tok[s], rec_dr[s])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vs.timers = None
+        return e0.elapsed_time(e1)
+
+    # per-call durations (instrumented replay, all calls)
+    names = ["embed", "lmhead", "accept", "final_norm"]
+    for i, _ in enumerate(cfg.layers):
+        names += [f"L{i}.{c}" for c in ("qkv", "attn", "o", "gu", "geglu", "down")]
+    timers = {n: [] for n in names}
+    replay(timers)
+    call_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in timers.items() if v}
+    byts = call_bytes(cfg, mean_lens)
+    dominant = max((n for n in call_ms if n in byts), key=lambda n: call_ms[n])
+    if time_calls:
+        dominant = time_calls
+
+    # timed replay: the whole step, plus events around the dominant call only
+    dom_t = {dominant: []}
+    ms = replay(dom_t)
+    ok = all(np.array_equal(L.decode_accept_out(vs.acc)["n_accepted"], rec_n[-1]) for _ in [0])
+    assert ok, "replay diverged from the recorded trajectory"
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_t[dominant]]))
+    res = dict(B=B, steps=steps, ms_total=ms, ms_per_step=ms / steps, committed=committed,
+               tokens_per_s=committed / (ms / 1e3), mean_accepted=float(np.mean(np.stack(rec_n))),
+               call_ms=call_ms, call_bytes=byts, dominant=dominant, dominant_ms=dom_ms,
+               first_tokens=rec_tok[0], first_len=rec_len[0], caches=caches)
+    return res
+
+
+def cpu_baseline(cfg, W, caches, tokens, lens, dev):
+    """Time the oracle on a bounded sample: one verify step of sequence 0."""
+    import numpy as np
+
+    import oracle
+    from oracle import model as om
+    from mtp_draft_verification_amd import inputs
+
+    log("cpu baseline: host copies for sequence 0")
+    hw = {"E": inputs.bf16_bits(W["E"]),
+          "layers": [{k: inputs.bf16_bits(v) for k, v in lw.items()} for lw in W["layers"]]}
+    cap = caches[0]["k"].shape[2]
+    hc = []
+    L0 = int(lens[0])
+    for ly, c in zip(cfg.layers, caches):
+        ent = {}
+        for nm in ("k", "v"):
+            t = c[nm]
+            if t is None:
+                ent[nm] = None
+                continue
+            a = np.zeros((1, t.shape[1], cap, t.shape[3]), dtype=np.float32)
+            lo = max(0, L0 - ly.window - 8) if ly.window else 0
+            a[0, :, lo:L0] = t[0, :, lo:L0].float().cpu().numpy()
+            ent[nm] = a
+        hc.append(ent)
+    cfg1 = dataclasses.replace(cfg, batch=1)
+    model = om.OracleModel(cfg1, hw)
+    state = om.new_state(hc, [L0])
+    tok = tokens[:1].cpu().numpy()
+    log(f"cpu baseline: oracle step on {oracle.num_threads()} threads")
+    t0 = time.perf_counter()
+    r = model.greedy_step(state, tok)
+    dt = time.perf_counter() - t0
+    n = int(r["n"][0]) + 1
+    return dict(value=n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"one verify step of sequence 0 ({cfg.k + 1} rows, all 6 layers, LM head, accept) "
+                       f"of the same workload at its first recorded step: {n} tokens committed in {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of "
+              f"this build: the verify step shards by sequence with no exchange (see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from mtp_draft_verification_amd import _lib as L
+    from mtp_draft_verification_amd import configs, inputs
+
+    L.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.profile:
+        args.sweep = ""
+        args.no_cpu_baseline = True
+    cfg = dataclasses.replace(configs.STACK, batch=args.batch, k=args.k, ctx=args.ctx, steps=args.steps)
+    log(f"weights (d={cfg.d_model}, d_ff={cfg.d_ff}, vocab={cfg.vocab})")
+    W = inputs.stack_weights(cfg, args.seed, dev)
+    main_res = run_workload(cfg, W, args.steps, args.warmup, args.seed, dev)
+    log(f"B={cfg.batch}: {main_res['tokens_per_s']:.1f} tokens/s, {main_res['ms_per_step']:.3f} ms/step, "
+        f"mean accepted {main_res['mean_accepted']:.2f}")
+
+    sweep = {f"B{cfg.batch}": round(main_res["tokens_per_s"], 1)}
+    for b in [int(x) for x in args.sweep.split(",") if x.strip()]:
+        if b == cfg.batch:
+            continue
+        c2 = dataclasses.replace(cfg, batch=b)
+        r = run_workload(c2, W, args.steps, args.warmup, args.seed, dev)
+        sweep[f"B{b}"] = round(r["tokens_per_s"], 1)
+        log(f"B={b}: {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step")
+        del r
+        torch.cuda.empty_cache()
+
+    dom = main_res["dominant"]
+    dom_bytes = main_res["call_bytes"][dom]
+    ach = dom_bytes / (main_res["dominant_ms"] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom), "kernel": dom,
+            "alg_bytes_per_launch": int(dom_bytes), "mean_launch_us": round(main_res["dominant_ms"] * 1e3, 2)}
+    kern = {}
+    for n, ms in sorted(main_res["call_ms"].items(), key=lambda kv: -kv[1]):
+        b = main_res["call_bytes"].get(n)
+        kern[n] = {"us": round(ms * 1e3, 2)}
+        if b:
+            kern[n]["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
+            kern[n]["frac"] = round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, W, main_res["caches"], main_res["first_tokens"], main_res["first_len"], dev)
+        log(f"cpu baseline: {cpu['value']:.4f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": round(main_res["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and caches; drafts = the target's greedy "
+                "continuation kept with probability 0.8)",
+        "config": {"workload": f"stack_verify: 6-layer 5:1 local/global decoder stack, d={cfg.d_model}, "
+                               f"d_ff={cfg.d_ff}, vocab {cfg.vocab}, committed context {cfg.ctx}, k={cfg.k}, "
+                               f"batch {cfg.batch}, greedy verify with KV append/rollback",
+                   "batch": cfg.batch, "k": cfg.k, "ctx": cfg.ctx, "d_model": cfg.d_model,
+                   "vocab": cfg.vocab, "layers": "LLLLLG"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep_tokens_per_s": sweep,
+        "mean_accepted": round(main_res["mean_accepted"], 3),
+        "kernels": kern,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

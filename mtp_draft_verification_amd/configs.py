@@ -126,7 +126,7 @@ STACK = StackConfig(
 
 def scaled_stack(base: StackConfig = STACK, *, name: str = "stack_small", d_model=256,
                  vocab=4096, d_ff=512, ctx=2048, batch=2, k=4, steps=16, window=64,
-                 local_heads=(4, 2, 64), global_heads=(4, 1, 128)) -> StackConfig:
+                 local_heads=(4, 2, 128), global_heads=(4, 1, 256)) -> StackConfig:
     """The same layer pattern at sizes the oracle finishes in seconds."""
     hq, hkv, d = local_heads
     gq, gkv, gd = global_heads

@@ -77,9 +77,26 @@ class VerifyStack:
         self.out_tokens = torch.zeros(B, k + 1, dtype=torch.int32, device=dev)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.acc_desc = L.AcceptDesc(batch=B, k=k, vocab=cfg.vocab, mode=L.SV_SELECT_GREEDY)
+        self.timers = None   # {call name: [(start event, end event), ...]} when timing
         self.attn_descs = [
             attn_desc(ly, B, k + 1, self.cap, cfg.dtype,
                       q_row_stride=self._nout(ly), kv_row_stride=self._nout(ly)) for ly in cfg.layers]
+
+    def _ev(self, name: str, stream):
+        """Record a HIP event pair around a named call when that call is being timed."""
+        if self.timers is None or name not in self.timers:
+            return None
+        st = stream if stream is not None else torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        self.timers[name].append((e0, e1))
+        return e1, st
+
+    @staticmethod
+    def _end(tok):
+        if tok is not None:
+            tok[0].record(tok[1])
 
     @staticmethod
     def _nout(ly) -> int:
@@ -113,41 +130,64 @@ class VerifyStack:
     # ------------------------------------------------------------------
     def forward(self, tokens: torch.Tensor, stream=None) -> torch.Tensor:
         """Verify forward of tokens [B, k+1] int32 (device); appends the k+1 new
-        rows of every layer's cache; returns the final hidden states [R, d]."""
+        rows of every layer's cache; returns the final hidden states [R, d].
+        Call names for timing: embed, L{i}.qkv, L{i}.attn, L{i}.o, L{i}.gu,
+        L{i}.geglu, L{i}.down, final_norm."""
         cfg = self.cfg
         d = cfg.d_model
+        t = self._ev("embed", stream)
         L.sv_embed(self.R, d, cfg.vocab, self.dt, tokens, self.W["E"], math.sqrt(d), self.x,
                    self.dev_status, stream)
-        for ly, lw, cache, desc in zip(cfg.layers, self.W["layers"], self.caches, self.attn_descs):
+        self._end(t)
+        for i, (ly, lw, cache, desc) in enumerate(zip(cfg.layers, self.W["layers"], self.caches,
+                                                      self.attn_descs)):
             a = self._norm(self.x, self.a, stream)
             nq_f = ly.n_heads_q * ly.head_dim
             nk_f = ly.n_heads_kv * ly.head_dim
             nout = self._nout(ly)
-            qkv = self.qkv[:, :nout] if nout == self.qkv.shape[1] else self.qkv.view(-1)[:self.R * nout].view(self.R, nout)
+            qkv = self.qkv.view(-1)[:self.R * nout].view(self.R, nout)
+            t = self._ev(f"L{i}.qkv", stream)
             self._linear(a, lw["wqkv"], qkv, L.SV_EPI_STORE, stream)
+            self._end(t)
             esz = qkv.element_size()
             base = qkv.data_ptr()
-            q_ptr = base
             k_ptr = base + nq_f * esz
             v_ptr = None if ly.k_is_v else base + (nq_f + nk_f) * esz
             o = self.o.view(-1)[:self.R * nq_f].view(self.R, nq_f)
-            L.sv_verify_attn(desc, q_ptr, k_ptr, v_ptr, cache["k"], cache["v"], self.cache_len, o,
+            t = self._ev(f"L{i}.attn", stream)
+            L.sv_verify_attn(desc, base, k_ptr, v_ptr, cache["k"], cache["v"], self.cache_len, o,
                              self.attn_ws, self.dev_status, stream)
+            self._end(t)
+            t = self._ev(f"L{i}.o", stream)
             self._linear(o, lw["wo"], self.x, L.SV_EPI_ADD_F32, stream)
+            self._end(t)
             if cfg.d_ff:
                 m = self._norm(self.x, self.a, stream)
+                t = self._ev(f"L{i}.gu", stream)
                 self._linear(m, lw["wgu"], self.gu, L.SV_EPI_STORE, stream)
+                self._end(t)
+                t = self._ev(f"L{i}.geglu", stream)
                 L.sv_geglu(self.R, cfg.d_ff, self.dt, self.gu, self.f, stream)
+                self._end(t)
+                t = self._ev(f"L{i}.down", stream)
                 self._linear(self.f, lw["wd"], self.x, L.SV_EPI_ADD_F32, stream)
-        return self._norm(self.x, self.h, stream)
+                self._end(t)
+        t = self._ev("final_norm", stream)
+        h = self._norm(self.x, self.h, stream)
+        self._end(t)
+        return h
 
     def select(self, h: torch.Tensor, drafts: torch.Tensor, stream=None) -> None:
+        t = self._ev("lmhead", stream)
         L.sv_lmhead_select(self.lm_desc, h, self.W["E"], drafts, None, None, self.stats, None, None,
                            self.lm_ws, stream)
+        self._end(t)
 
     def accept(self, drafts: torch.Tensor, stream=None) -> None:
+        t = self._ev("accept", stream)
         L.sv_accept(self.acc_desc, drafts, self.stats, None, None, self.cache_len, self.out_tokens, self.acc,
                     self.dev_status, stream)
+        self._end(t)
 
     def step(self, tokens: torch.Tensor, drafts: torch.Tensor, stream=None) -> None:
         """One greedy verify step: forward, LM-head select, accept (commits on device)."""
