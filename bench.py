@@ -57,7 +57,70 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for profilers: no sweep, no oracle")
+    ap.add_argument("--only", choices=["attn_global", "attn_local", "lmhead", "lmhead_sample"], default=None,
+                    help="time one call of the step in isolation at the workload's shapes")
+    ap.add_argument("--iters", type=int, default=50, help="iterations of --only")
     return ap.parse_args()
+
+
+def bench_only(args):
+    """One call of the verify step, timed alone at the workload's shapes (batch,
+    k, context): the global-layer attention (16q/4kv, D=512, K=V, p-RoPE), a local
+    layer's attention (16q/8kv, D=256, window 1024) or the LM-head select."""
+    import torch
+
+    from mtp_draft_verification_amd import _lib as L
+    from mtp_draft_verification_amd import configs, inputs
+    from mtp_draft_verification_amd.step import attn_desc
+
+    dev = torch.device("cuda:0")
+    cfg = dataclasses.replace(configs.STACK, batch=args.batch, k=args.k, ctx=args.ctx)
+    B, nq = cfg.batch, cfg.k + 1
+    stream = torch.cuda.current_stream()
+    if args.only.startswith("attn"):
+        ly = cfg.layers[-1] if args.only == "attn_global" else cfg.layers[0]
+        cap = cfg.ctx + nq + 8
+        lo = 0 if ly.window == 0 else max(0, cfg.ctx - ly.window - 8)
+        kc = torch.zeros((B, ly.n_heads_kv, cap, ly.head_dim), dtype=torch.bfloat16, device=dev)
+        kc[:, :, lo:cfg.ctx] = inputs.normal((B, ly.n_heads_kv, cfg.ctx - lo, ly.head_dim), 1.0, 0, "kc", dev)
+        vc = None if ly.k_is_v else kc.clone()
+        q = inputs.normal((B, nq, ly.n_heads_q, ly.head_dim), 1.0, 0, "q", dev)
+        kn = inputs.normal((B, nq, ly.n_heads_kv, ly.head_dim), 1.0, 0, "kn", dev)
+        vn = None if ly.k_is_v else kn.clone()
+        cl = torch.full((B,), cfg.ctx, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        desc = attn_desc(ly, B, nq, cap, "bf16")
+        ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
+        call = lambda: L.sv_verify_attn(desc, q, kn, vn, kc, vc, cl, out, ws, None, stream)
+        lens = [cfg.ctx] * B
+        byts = call_bytes(cfg, lens)["L5.attn" if ly.window == 0 else "L0.attn"]
+    else:
+        mode = L.SV_SELECT_GREEDY if args.only == "lmhead" else L.SV_SELECT_SAMPLE
+        R = B * nq
+        h = inputs.normal((R, cfg.d_model), 1.0, 0, "h", dev)
+        W = inputs.normal((cfg.vocab, cfg.d_model), cfg.d_model ** -0.5, 0, "E", dev)
+        drafts = torch.randint(0, cfg.vocab, (B, cfg.k), dtype=torch.int32, device=dev)
+        u_tok = torch.rand((B, cfg.vocab), device=dev) if mode == L.SV_SELECT_SAMPLE else None
+        desc = L.LMHeadDesc(batch=B, k=cfg.k, d_model=cfg.d_model, vocab=cfg.vocab, mode=mode, dtype=L.SV_BF16)
+        ws = torch.empty(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
+        stats = torch.empty((R, L.ROW_STATS_WORDS), dtype=torch.int32, device=dev)
+        call = lambda: L.sv_lmhead_select(desc, h, W, drafts, u_tok, None, stats, None, None, ws, stream)
+        byts = call_bytes(cfg, [cfg.ctx] * B)["lmhead"]
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.iters):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.iters
+    gbs = byts / (us * 1e-6) / 1e9
+    print(json.dumps({"call": args.only, "batch": B, "k": cfg.k, "ctx": cfg.ctx, "us_per_call": round(us, 2),
+                      "alg_bytes": int(byts), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                      "source_digest": source_digest()}), flush=True)
 
 
 def source_digest() -> str:
@@ -264,6 +327,9 @@ def main():
 
     L.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.only:
+        bench_only(args)
+        return
     dev = torch.device("cuda:0")
     if args.profile:
         args.sweep = ""

@@ -69,7 +69,7 @@ typedef struct {
   int32_t n_q;           /* query rows per sequence: k+1 in a verify step */
   int32_t n_heads_q;     /* Hq, a multiple of n_heads_kv */
   int32_t n_heads_kv;    /* Hkv */
-  int32_t head_dim;      /* D: 128, 256 or 512 in bf16; <= 512 in fp32 */
+  int32_t head_dim;      /* D: 128, 256 or 512 in bf16 (512 only with k_is_v); <= 512 in fp32 */
   int32_t window;        /* 0: global layer; W > 0: sliding window, key t is visible
                             to the query at position p iff p - W < t <= p */
   int32_t rope_dims;     /* rotated leading dims: 0 (none), D (full RoPE) or a fraction

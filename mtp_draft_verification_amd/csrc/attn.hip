@@ -79,10 +79,10 @@ __device__ __forceinline__ int64_t total_keys(const AttnParams& p) {
   return t;
 }
 
-// keys per workgroup piece (a multiple of 32)
+// keys per workgroup piece (a multiple of the 64-key tile)
 __device__ __forceinline__ int64_t piece_chunk(const AttnParams& p, int64_t total) {
   int64_t c = (total + p.nwg - 1) / p.nwg;
-  c = (c + 31) & ~int64_t(31);
+  c = (c + 63) & ~int64_t(63);
   return c < p.min_chunk ? p.min_chunk : c;
 }
 
@@ -109,75 +109,165 @@ __device__ __forceinline__ double rope_elem(const void* src, int64_t head_off, i
   if (d >= r) return x;
   const int half = r >> 1;
   const int i = d < half ? d : d - half;
+  // angle in fp64 (positions reach ~1e5 rad), reduced to [-pi, pi] before the fp32 sincos
   const double theta = exp2(-(2.0 * (double)i / (double)r) * log2_base);
-  double sn, cs;
-  sincos(pos * theta, &sn, &cs);
+  const double ang = pos * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  const float red = (float)(ang - two_pi * rint(ang / two_pi));
+  float snf, csf;
+  sincosf(red, &snf, &csf);
+  const double sn = snf, cs = csf;
   if (d < half) return x * cs - ld_elem<T>(src, head_off + d + half) * sn;
   return x * cs + ld_elem<T>(src, head_off + d - half) * sn;
 }
 
+// one workgroup per (sequence, row, head); one thread per element of the head
 template <typename T>
-__global__ __launch_bounds__(256) void rope_append_kernel(AttnParams p) {
-  const int j = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
+  const int b = blockIdx.x / p.nq, j = blockIdx.x % p.nq;
+  const int hs = blockIdx.y;  // [0, Hq): query head, then key heads, then value heads
+  const int d = threadIdx.x;
   const int64_t L = p.cache_len[b];
   if (!seq_ok(p, L)) {
-    if (threadIdx.x == 0 && j == 0) set_status(p.dev_status, L < 0 ? SV_DEV_BAD_LENGTH : SV_DEV_CACHE_OVERFLOW);
+    if (d == 0 && j == 0 && hs == 0) set_status(p.dev_status, L < 0 ? SV_DEV_BAD_LENGTH : SV_DEV_CACHE_OVERFLOW);
     return;
   }
   const int D = p.D;
+  if (d >= D) return;
   const double pos = (double)(L + p.qoff + j);
-  const int nqe = p.Hq * D;
-  const int nke = p.n_new > 0 ? p.Hkv * D : 0;
-  const int nve = (p.n_new > 0 && !p.k_is_v) ? p.Hkv * D : 0;
-  for (int e = threadIdx.x; e < nqe + nke + nve; e += blockDim.x) {
-    if (e < nqe) {
-      const int h = e / D, d = e % D;
-      const int64_t src = ((int64_t)b * p.nq + j) * p.q_stride + (int64_t)h * D;
-      const int64_t dst = (((int64_t)b * p.nq + j) * p.Hq + h) * D;
-      st_elem<T>(p.q_rot, dst + d, rope_elem<T>(p.q, src, d, p.rope_dims, p.log2_base, pos));
-    } else if (e < nqe + nke) {
-      const int e2 = e - nqe, h = e2 / D, d = e2 % D;
-      const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
-      const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-      st_elem<T>(p.k_cache, dst + d, rope_elem<T>(p.k_new, src, d, p.rope_dims, p.log2_base, pos));
-    } else {
-      const int e2 = e - nqe - nke, h = e2 / D, d = e2 % D;
-      const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
-      const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-      st_elem<T>(p.v_cache, dst + d, ld_elem<T>(p.v_new, src + d));
-    }
+  if (hs < p.Hq) {
+    const int64_t src = ((int64_t)b * p.nq + j) * p.q_stride + (int64_t)hs * D;
+    const int64_t dst = (((int64_t)b * p.nq + j) * p.Hq + hs) * D;
+    st_elem<T>(p.q_rot, dst + d, rope_elem<T>(p.q, src, d, p.rope_dims, p.log2_base, pos));
+  } else if (hs < p.Hq + p.Hkv) {
+    const int h = hs - p.Hq;
+    const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
+    const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
+    st_elem<T>(p.k_cache, dst + d, rope_elem<T>(p.k_new, src, d, p.rope_dims, p.log2_base, pos));
+  } else {
+    const int h = hs - p.Hq - p.Hkv;
+    const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
+    const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
+    st_elem<T>(p.v_cache, dst + d, ld_elem<T>(p.v_new, src + d));
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2a. bf16 multi-query attention on MFMA
 //
-// Workgroup = 4 waves; wave w owns the dims [w*D/4, (w+1)*D/4) of the head.
-// Per tile of 32 keys:
-//   QK : each wave forms the partial scores S^T[key, row] over its dims with
-//        16x16x32 MFMAs (A = key rows straight from HBM, B = rotated queries),
-//        the four partials meet in LDS and every wave sums them in the same
-//        order (one barrier per tile, double-buffered);
-//   softmax: per row, running max m and sum l in log2 units; the row of a
-//        lane is fixed (lane % 16) so the rescale of its accumulators is local;
-//   PV : O^T[dim, row] += V^T[dim, key] P^T[key, row]; V^T comes from the
-//        wave's own key/value registers transposed through a private LDS tile,
-//        P^T straight from the score registers (same lane layout).
+// Workgroup = 4 waves, one workgroup per CU.  Key tiles of 64 keys (and values,
+// unless the layer reuses the keys) stream HBM -> LDS by direct-to-LDS DMA
+// through a ring of NS stages.  Per tile:
+//   QK : wave w scores its own 16 keys against all rows over the full head
+//        dimension (16x16x32 MFMAs; A = key rows read from the staged tile, B =
+//        the rotated queries, held in registers for the whole piece), so every
+//        score is produced and exponentiated by exactly one wave;
+//   max: the waves exchange their per-row tile maxima; the reference max of a
+//        row only moves when the tile max exceeds it by more than 2^8 (lazy
+//        rescaling), so p = 2^(s - m) <= 256 and the accumulators are rescaled
+//        only when some row needs it;
+//   P  : each wave writes its bf16 weights to LDS in exactly the lane layout the
+//        PV product reads them in (an 8-byte same-lane transfer);
+//   PV : wave w owns the dims [w*D/4, (w+1)*D/4): O^T[dim, row] += V^T[dim, key]
+//        P^T[key, row]; V^T is read from the staged row-major tile with the LDS
+//        transpose read.
+// Staged rows are unpadded; 16-byte chunk c of key row r lives in slot
+// c ^ swz(r), which spreads both the row-wise and the transposed reads over the
+// LDS banks.
 // ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
+
+// 16 bytes per lane from global memory straight into LDS at (lds_base + 16 * lane),
+// gaddr = base (wave-uniform) + off (per lane, bytes).  Issued from inline asm so
+// the compiler, which cannot tell which ring stage a DMA writes, does not stall
+// every LDS read on it; completion is waited for explicitly with wait_vm.  M0 (the
+// LDS base) is saved and restored around the instruction.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+// wait until at most n of this wave's vector memory operations are outstanding
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS writes have completed,
+// but DMA into LDS still in flight is not waited for (each tile waits for its own
+// DMA explicitly), which keeps the ring's prefetches going across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int MT, bool KV_SAME>
+struct AttnCfg {
+  static constexpr int DS = D / 4;              // PV dims per wave
+  static constexpr int KS = D / 32;             // 32-dim k-steps of QK (full head)
+  static constexpr int DT = DS / 16;            // 16-dim output tiles of PV per wave
+  static constexpr int TK = 64;                 // keys per tile (16 per wave)
+  static constexpr int ROWB = D * 2;            // bytes per key row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per DMA instruction
+  static constexpr int NTEN = KV_SAME ? 1 : 2;  // staged tensors
+  static constexpr int TILEB = TK * ROWB;
+  static constexpr int STAGEB = TILEB * NTEN;
+  static constexpr int NI = (TK / RPI) * NTEN / 4;  // DMA instructions per wave per tile
+  static constexpr int SMALLB = 4 * MT * 64 * 8 + 2 * 4 * MT * 16 * 4;  // P and max/sum exchange
+  static constexpr int NS_FIT = (160 * 1024 - SMALLB) / STAGEB;
+  static constexpr int NS = NS_FIT < 4 ? NS_FIT : 4;  // ring stages
+  static_assert(NS >= 2, "tile does not fit twice in LDS");
+  static_assert(DT >= 1 && RPI >= 1 && NI >= 1, "unsupported head_dim");
+  static_assert(NI == 4 || NI == 8 || NI == 16, "wait_vm needs these counts");
+};
+
 template <int D, int MT, bool KV_SAME>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
-  constexpr int DS = D / 4;   // dims per wave
-  constexpr int KS = DS / 32; // 32-dim k-steps of QK per wave
-  constexpr int DT = DS / 16; // 16-dim output tiles of PV per wave
-  constexpr int TK = 32;      // keys per tile
-  constexpr int VTS = TK + 8; // bf16 per V^T row in LDS (16-byte aligned rows)
-  static_assert(KS >= 1 && DT >= 1, "head_dim too small");
+  using C = AttnCfg<D, MT, KV_SAME>;
+  constexpr int DS = C::DS, KS = C::KS, DT = C::DT, TK = C::TK, ROWB = C::ROWB, CPR = C::CPR,
+                RPI = C::RPI, TILEB = C::TILEB, STAGEB = C::STAGEB, NI = C::NI, NS = C::NS;
 
-  __shared__ __attribute__((aligned(16))) float s_part[2][4][MT * 2][64 * 4];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[4][DS * VTS];
+  // one LDS object per ring stage: with the tile loop unrolled by NS every access
+  // names its stage statically
+  __shared__ __attribute__((aligned(16))) unsigned char s_st0[STAGEB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st1[STAGEB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st2[NS > 2 ? STAGEB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st3[NS > 3 ? STAGEB : 16];
+  __shared__ __attribute__((aligned(16))) uint2 s_p[4][MT][64];      // bf16 weights, PV lane layout
+  __shared__ float s_max[4][MT][16];                                 // per-wave row maxima of a tile
+  __shared__ float s_sum[4][MT][16];                                 // per-wave row sums of a piece
+  auto stage_of = [&](int u) -> unsigned char* {
+    return u == 0 ? s_st0 : u == 1 ? s_st1 : u == 2 ? s_st2 : s_st3;
+  };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int M = p.M, G = p.G;
 
@@ -189,9 +279,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int64_t end = start + chunk < total ? start + chunk : total;
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
-  const uint16_t* kc = (const uint16_t*)p.k_cache;
+  const uint16_t* kcache = (const uint16_t*)p.k_cache;
   const uint16_t* vcache = (const uint16_t*)p.v_cache;
-  int buf = 0;
 
   int64_t seg_off = 0;
   for (int b = 0; b < p.B && seg_off < end; ++b) {
@@ -207,8 +296,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       const int64_t a0 = (start > s0 ? start : s0) - s0 + lo;  // first key of the piece
       const int64_t a1 = (end < s1 ? end : s1) - s0 + lo;      // one past its last key
       const int slot = blockIdx.x + b * p.Hkv + kvh;
+      const int ntiles = (int)((a1 - a0 + TK - 1) / TK);
 
-      // ---- queries of this (sequence, kv head) as MFMA B operands
+      // ---- queries of this (sequence, kv head), full head dim, as MFMA B operands
       V16 qreg[MT][KS];
       int64_t row_hi[MT], row_lo[MT];
 #pragma unroll
@@ -216,7 +306,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         const int r = mt * 16 + lr;
         if (r < M) {
           const int j = r / G, hg = r - (r / G) * G;
-          const uint16_t* src = qrot + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + wave * DS + lg * 8;
+          const uint16_t* src = qrot + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + lg * 8;
 #pragma unroll
           for (int s = 0; s < KS; ++s) qreg[mt][s].u = *(const uint4*)(src + s * 32);
           const int64_t pos = L + p.qoff + j;
@@ -229,6 +319,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           row_lo[mt] = INT64_MIN;
         }
       }
+      // consume the query loads here (the compiler then waits for them once, not
+      // inside the tile loop where the ring's DMA is in flight), and start from an
+      // idle memory pipe and a free ring
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qreg[mt][s].b));
+      wait_vm(0);
+      __syncthreads();
 
       f32x4_t O[DT][MT];
       float m_run[MT], l_run[MT];
@@ -240,155 +339,188 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         for (int dt = 0; dt < DT; ++dt) O[dt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
 
-      const int64_t head_base = ((int64_t)b * p.Hkv + kvh) * p.cap * D + wave * DS + lg * 8;
-      auto load_tile = [&](int64_t t0, V16 (&kr)[2][KS], V16 (&vr)[2][KS]) {
+      // every real row sees keys [seg_max_lo, seg_min_hi] (row 0 has the lowest causal
+      // limit, the last row the highest window start)
+      const int64_t seg_min_hi = (L + p.qoff) < last ? (L + p.qoff) : last;
+      const int64_t seg_max_lo = p.window > 0 ? L + p.qoff + p.nq - p.window : INT64_MIN;
+      const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.cap;  // row index of key 0
+      // DMA of tile t into its ring stage: wave w moves NI instructions of 1 KB each;
+      // lane l carries 16 B of row (l / CPR) of the instruction's row block.  The row
+      // block's address is wave-uniform; the per-lane byte offsets (row within the
+      // block, swizzled chunk) repeat every tile and are computed once.  Only a tile
+      // that runs past the piece clamps rows to its last row (finite data, masked out
+      // of the softmax) with per-lane offsets.
+      uint32_t off_pre[NI];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int64_t key = t0 + kt * 16 + lr;
-          const bool ok = key < a1;
-          const int64_t off = head_base + key * D;
+      for (int jj = 0; jj < NI; ++jj) {
+        const int rb = (wave * NI + jj) % (TK / RPI);
+        const int row = rb * RPI + lane / CPR;
+        off_pre[jj] = (uint32_t)((lane / CPR) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
+      }
+      auto issue = [&](int t, unsigned char* stage) {
+        const int64_t t0 = a0 + (int64_t)t * TK;
+        const bool partial = t0 + TK > a1;
 #pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            kr[kt][s].u = ok ? *(const uint4*)(kc + off + s * 32) : make_uint4(0, 0, 0, 0);
-            if constexpr (!KV_SAME)
-              vr[kt][s].u = ok ? *(const uint4*)(vcache + off + s * 32) : make_uint4(0, 0, 0, 0);
+        for (int jj = 0; jj < NI; ++jj) {
+          const int ii = wave * NI + jj;
+          const int ten = ii / (TK / RPI);
+          const int rb = ii % (TK / RPI);
+          const uint16_t* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
+          const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + ten * TILEB + rb * RPI * ROWB));
+          int64_t brow = t0 + rb * RPI;  // first row of the block
+          uint32_t off = off_pre[jj];
+          if (partial) {
+            if (brow > a1 - 1) brow = a1 - 1;
+            const int row = rb * RPI + lane / CPR;
+            int64_t key = t0 + row;
+            if (key > a1 - 1) key = a1 - 1;
+            off = (uint32_t)((key - brow) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
           }
+          dma16((const void*)(tbase + (head_row0 + brow) * D), off, lds);
         }
       };
 
-      V16 kcur[2][KS], vcur[2][KS], knext[2][KS], vnext[2][KS];
-      load_tile(a0, kcur, vcur);
+#pragma unroll
+      for (int u = 0; u < NS - 1; ++u)
+        if (u < ntiles) issue(u, stage_of(u));
 
-      for (int64_t t0 = a0; t0 < a1; t0 += TK) {
-        // ---- partial scores over this wave's dims
-        f32x4_t sp[MT][2];
+      for (int tb = 0; tb < ntiles; tb += NS) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mfma16x16x32(kcur[kt][s].b, qreg[mt][s].b, acc);
-            sp[mt][kt] = acc;
-          }
-        float* myp = &s_part[buf][wave][0][0];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) *(f32x4_t*)(myp + ((mt * 2 + kt) * 64 + lane) * 4) = sp[mt][kt];
+      for (int u = 0; u < NS; ++u) {
+        const int t = tb + u;  // tile t lives in stage u
+        if (t >= ntiles) break;
+        const int64_t t0 = a0 + (int64_t)t * TK;
+        const int ahead = (NS - 2) < (ntiles - 1 - t) ? (NS - 2) : (ntiles - 1 - t);
+        wait_vm(ahead * NI);
+        lds_barrier();  // tile t is in LDS for every wave; tile t-1 is no longer read
+        if (t + NS - 1 < ntiles) issue(t + NS - 1, stage_of((u + NS - 1) % NS));
 
-        // ---- this wave's values, transposed into its private LDS tile:
-        // key 16*kt + lr goes to column 8*(lr/4) + 2*(lr%4) + kt of row `dim`
+        const unsigned char* kst = stage_of(u);
+        const unsigned char* vst = kst + (KV_SAME ? 0 : TILEB);
+
+        // ---- scores of this wave's 16 keys: S^T[key, row], lane holds row lr of each
+        // row tile and keys 16*wave + 4*lg + {0..3}
+        f32x4_t sacc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         {
-          uint16_t* vt = s_vt[wave];
-          const int col = 8 * (lr >> 2) + 2 * (lr & 3);
+          const int r = wave * 16 + lr;
+          const unsigned char* krow = kst + r * ROWB;
+          const int sw = swz(r);
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            const V16& v0 = KV_SAME ? kcur[0][s] : vcur[0][s];
-            const V16& v1 = KV_SAME ? kcur[1][s] : vcur[1][s];
+            V16 kreg;
+            kreg.u = *(const uint4*)(krow + (((4 * s + lg) ^ sw) << 4));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t w0 = v0.w[e >> 1], w1 = v1.w[e >> 1];
-              const uint32_t h0 = (e & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-              const uint32_t h1 = (e & 1) ? (w1 >> 16) : (w1 & 0xffffu);
-              const int dim = s * 32 + lg * 8 + e;
-              *(uint32_t*)(vt + dim * VTS + col) = h0 | (h1 << 16);
-            }
+            for (int mt = 0; mt < MT; ++mt) sacc[mt] = mfma16x16x32(kreg.b, qreg[mt][s].b, sacc[mt]);
           }
         }
-
-        // ---- prefetch the next tile
-        const bool more = t0 + TK < a1;
-        if (more) load_tile(t0 + TK, knext, vnext);
-
-        __syncthreads();
-
-        // ---- full scores, softmax update, P operands
-        V16 preg[MT];
+        const bool full = (t0 + TK <= a1) && (t0 + TK - 1 <= seg_min_hi) && (t0 >= seg_max_lo);
+        float sc[MT][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          float sc[2][4];
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            f32x4_t a = *(const f32x4_t*)(&s_part[buf][0][mt * 2 + kt][lane * 4]);
-#pragma unroll
-            for (int w = 1; w < 4; ++w) {
-              const f32x4_t o = *(const f32x4_t*)(&s_part[buf][w][mt * 2 + kt][lane * 4]);
-              a[0] += o[0]; a[1] += o[1]; a[2] += o[2]; a[3] += o[3];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int64_t key = t0 + kt * 16 + lg * 4 + i;
-              const bool vis = key < a1 && key <= row_hi[mt] && key >= row_lo[mt];
-              sc[kt][i] = vis ? a[i] * p.scale_log2 : kNegInf;
-            }
+          int lo_l = -1, hi_l = TK;
+          if (!full) {
+            const int64_t hi = (row_hi[mt] < a1 - 1 ? row_hi[mt] : a1 - 1) - t0;
+            const int64_t lo2 = row_lo[mt] - t0;
+            hi_l = hi < -1 ? -1 : (hi > TK ? TK : (int)hi);
+            lo_l = lo2 < -1 ? -1 : (lo2 > TK ? TK : (int)lo2);
           }
           float mx = kNegInf;
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kt][i]);
+          for (int i = 0; i < 4; ++i) {
+            const int kl = wave * 16 + lg * 4 + i;
+            sc[mt][i] = (full || (kl >= lo_l && kl <= hi_l)) ? sacc[mt][i] * p.scale_log2 : kNegInf;
+            mx = fmaxf(mx, sc[mt][i]);
+          }
           mx = fmaxf(mx, shfl_xor_f(mx, 16));
           mx = fmaxf(mx, shfl_xor_f(mx, 32));
-          const float m_new = fmaxf(m_run[mt], mx);
-          float alpha = 1.f;
-          float pv[2][4];
-          if (m_new == kNegInf) {
+          if (lg == 0) s_max[wave][mt][lr] = mx;
+        }
+        lds_barrier();
+
+        // ---- tile maxima of all waves -> lazy reference update (same on every wave)
+        bool need = false;
+        float tmax[MT];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+        for (int mt = 0; mt < MT; ++mt) {
+          tmax[mt] = fmaxf(fmaxf(s_max[0][mt][lr], s_max[1][mt][lr]), fmaxf(s_max[2][mt][lr], s_max[3][mt][lr]));
+          need |= tmax[mt] > m_run[mt] + 8.f;
+        }
+        if (__any(need)) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) pv[kt][i] = 0.f;
-          } else {
-            alpha = exp2f(m_run[mt] - m_new);
+          for (int mt = 0; mt < MT; ++mt) {
+            const float m_new = fmaxf(m_run[mt], tmax[mt]);
+            const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[mt] - m_new);
+            l_run[mt] *= alpha;
+            m_run[mt] = m_new;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) pv[kt][i] = round_bf16(exp2f(sc[kt][i] - m_new));
+            for (int dt = 0; dt < DT; ++dt) {
+              O[dt][mt][0] *= alpha; O[dt][mt][1] *= alpha;
+              O[dt][mt][2] *= alpha; O[dt][mt][3] *= alpha;
+            }
           }
-          float rs = 0.f;
+        }
+        // ---- weights of this wave's keys, bf16, to LDS in the PV operand layout
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+        for (int mt = 0; mt < MT; ++mt) {
+          const float m = m_run[mt];
+          float pv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rs += pv[kt][i];
+          for (int i = 0; i < 4; ++i) pv[i] = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[mt][i] - m);
+          uint2 w2;
+          w2.x = pack_bf16x2(pv[0], pv[1]);
+          w2.y = pack_bf16x2(pv[2], pv[3]);
+          s_p[wave][mt][lane] = w2;
+          // the normaliser sums exactly the (bf16) weights the PV product uses
+          float rs = bf16_lo(w2.x) + bf16_hi(w2.x) + bf16_lo(w2.y) + bf16_hi(w2.y);
           rs += shfl_xor_f(rs, 16);
           rs += shfl_xor_f(rs, 32);
-          l_run[mt] = l_run[mt] * alpha + rs;
-          m_run[mt] = m_new;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            O[dt][mt][0] *= alpha; O[dt][mt][1] *= alpha;
-            O[dt][mt][2] *= alpha; O[dt][mt][3] *= alpha;
-          }
-          // slot 2*i + kt of lane group lg holds key 16*kt + 4*lg + i
-#pragma unroll
-          for (int i = 0; i < 4; ++i) preg[mt].w[i] = pack_bf16x2(pv[0][i], pv[1][i]);
+          l_run[mt] += rs;
         }
+        lds_barrier();
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T over the tile's two 32-key halves.  Lane i of a 16-lane
+        // group feeds row 32*ks + 16*h + 4*lg + i/4, dims 4*(i%4)..+3 of the tile; the
+        // transpose read returns dim (lane % 16) of rows 32*ks + 16*h + 4*lg + {0..3},
+        // matching P slots 4*h + e (written by wave 2*ks + h).
         {
-          const uint16_t* vt = s_vt[wave];
+          const int i = lane & 15;
+          const int a = i & 3;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            V16 a;
-            a.u = *(const uint4*)(vt + (dt * 16 + lr) * VTS + lg * 8);
+          for (int ks = 0; ks < 2; ++ks) {
+            V16 pb[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) O[dt][mt] = mfma16x16x32(a.b, preg[mt].b, O[dt][mt]);
-          }
-        }
-
-        buf ^= 1;
-        if (more) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-              kcur[kt][s] = knext[kt][s];
-              if constexpr (!KV_SAME) vcur[kt][s] = vnext[kt][s];
+            for (int mt = 0; mt < MT; ++mt) {
+              const uint2 p0 = s_p[2 * ks][mt][lane], p1 = s_p[2 * ks + 1][mt][lane];
+              pb[mt].u = make_uint4(p0.x, p0.y, p1.x, p1.y);
             }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const int c = wave * (DS / 8) + 2 * dt + (a >> 1);
+              V16 av;
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int r = 32 * ks + 16 * h + 4 * lg + (i >> 2);
+                const unsigned char* ad = vst + r * ROWB + ((c ^ swz(r)) << 4) + ((a & 1) << 3);
+                const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)ad);
+                av.w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+                av.w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+              }
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) O[dt][mt] = mfma16x16x32(av.b, pb[mt].b, O[dt][mt]);
+            }
+          }
         }
       }
+      }
 
-      // ---- unnormalised partial of this piece
+      // ---- unnormalised partial of this piece: the row sums of the four waves
+      // (each over its own keys, all on the same reference) add up
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        if (lg == 0) s_sum[wave][mt][lr] = l_run[mt];
+      __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + lr;
@@ -398,7 +530,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(dst + dt * 16) = O[dt][mt];
           if (wave == 0 && lg == 0) {
             p.part_ml[((int64_t)slot * M + r) * 2 + 0] = m_run[mt];
-            p.part_ml[((int64_t)slot * M + r) * 2 + 1] = l_run[mt];
+            p.part_ml[((int64_t)slot * M + r) * 2 + 1] =
+                (s_sum[0][mt][lr] + s_sum[1][mt][lr]) + (s_sum[2][mt][lr] + s_sum[3][mt][lr]);
           }
         }
       }
@@ -559,6 +692,8 @@ static int validate_attn(const sv_attn_desc* d) {
   if (!(d->softmax_scale > 0.f)) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
     if (d->head_dim != 128 && d->head_dim != 256 && d->head_dim != 512) return SV_ERR_UNSUPPORTED;
+    // a 64-key tile of separate 512-wide keys and values (128 KB) cannot be double-buffered in LDS
+    if (d->head_dim == 512 && !d->k_is_v) return SV_ERR_UNSUPPORTED;
     if ((d->n_heads_q / d->n_heads_kv) * d->n_q > 64) return SV_ERR_UNSUPPORTED;
   } else if (d->dtype == SV_F32) {
     if (d->head_dim > 512) return SV_ERR_UNSUPPORTED;
@@ -575,13 +710,13 @@ static void launch_mfma(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL((attn_mfma_kernel<D, MT, KVS>), dim3(p.nwg), dim3(256), 0, s, p);
 }
 
-template <int D>
-static int dispatch_mfma(const AttnParams& p, int MT, bool kvs, hipStream_t s) {
+template <int D, bool KVS>
+static int dispatch_mfma(const AttnParams& p, int MT, hipStream_t s) {
   switch (MT) {
-    case 1: kvs ? launch_mfma<D, 1, true>(p, s) : launch_mfma<D, 1, false>(p, s); break;
-    case 2: kvs ? launch_mfma<D, 2, true>(p, s) : launch_mfma<D, 2, false>(p, s); break;
-    case 3: kvs ? launch_mfma<D, 3, true>(p, s) : launch_mfma<D, 3, false>(p, s); break;
-    case 4: kvs ? launch_mfma<D, 4, true>(p, s) : launch_mfma<D, 4, false>(p, s); break;
+    case 1: launch_mfma<D, 1, KVS>(p, s); break;
+    case 2: launch_mfma<D, 2, KVS>(p, s); break;
+    case 3: launch_mfma<D, 3, KVS>(p, s); break;
+    case 4: launch_mfma<D, 4, KVS>(p, s); break;
     default: return SV_ERR_UNSUPPORTED;
   }
   return SV_OK;
@@ -644,24 +779,28 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
   p.n_new = d->append ? d->n_q : 0;
   p.qoff = d->q_pos_offset;
   p.k_is_v = d->k_is_v;
-  p.nwg = 512;
+  p.nwg = device_cus();
   p.min_chunk = 64;
 
   hipStream_t s = (hipStream_t)stream;
+  const int heads = d->n_heads_q + (d->append ? d->n_heads_kv * (d->k_is_v ? 1 : 2) : 0);
+  const int rope_threads = (d->head_dim + 63) / 64 * 64;
   if (d->dtype == SV_BF16) {
-    hipLaunchKernelGGL(rope_append_kernel<uint16_t>, dim3(d->n_q, d->batch), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(rope_append_kernel<uint16_t>, dim3(d->batch * d->n_q, heads), dim3(rope_threads), 0, s, p);
     const int MT = (pl.M + 15) / 16;
-    switch (d->head_dim) {
-      case 128: rc = dispatch_mfma<128>(p, MT, d->k_is_v, s); break;
-      case 256: rc = dispatch_mfma<256>(p, MT, d->k_is_v, s); break;
-      case 512: rc = dispatch_mfma<512>(p, MT, d->k_is_v, s); break;
+    switch (d->head_dim * 2 + (d->k_is_v ? 1 : 0)) {
+      case 256: rc = dispatch_mfma<128, false>(p, MT, s); break;
+      case 257: rc = dispatch_mfma<128, true>(p, MT, s); break;
+      case 512: rc = dispatch_mfma<256, false>(p, MT, s); break;
+      case 513: rc = dispatch_mfma<256, true>(p, MT, s); break;
+      case 1025: rc = dispatch_mfma<512, true>(p, MT, s); break;
       default: rc = SV_ERR_UNSUPPORTED;
     }
     if (rc != SV_OK) return rc;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(pl.M, d->batch * d->n_heads_kv), dim3(d->head_dim / 4),
                        0, s, p);
   } else {
-    hipLaunchKernelGGL(rope_append_kernel<float>, dim3(d->n_q, d->batch), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(rope_append_kernel<float>, dim3(d->batch * d->n_q, heads), dim3(rope_threads), 0, s, p);
     hipLaunchKernelGGL(attn_f32_kernel, dim3(d->n_heads_q, d->n_q, d->batch), dim3(256), 0, s, p);
   }
   return launch_status();

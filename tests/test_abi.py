@@ -61,6 +61,7 @@ def test_attention_descriptor_validation():
         assert call(_desc(**kw)) in (L.SV_ERR_ARG, L.SV_ERR_UNSUPPORTED), kw
         assert L.sv_verify_attn_workspace(_desc(**kw)) == 0, kw
     assert call(_desc(head_dim=64, rope_dims=64)) == L.SV_ERR_UNSUPPORTED      # no bf16 kernel for D=64
+    assert call(_desc(head_dim=512, rope_dims=128)) == L.SV_ERR_UNSUPPORTED    # D=512 needs K = V
     assert call(_desc(n_q=9, n_heads_q=64, n_heads_kv=8)) == L.SV_ERR_UNSUPPORTED  # 72 rows > 64
     assert call(_desc(), q=None) == L.SV_ERR_ARG
     assert call(_desc(), vn=None) == L.SV_ERR_ARG                            # V needed on local layers

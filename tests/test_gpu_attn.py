@@ -61,8 +61,13 @@ def run_case(layer, B, nq, lens, cap, seed, dtype="bf16", std=None, append=True,
             Lb = int(lens[b])
             got_rows = host(kc[b, g, Lb:Lb + nq])
             ref_rows = kcg[Lb:Lb + nq]
-            ulp = np.abs(ref_rows) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -22) + 1e-30
-            assert np.all(np.abs(got_rows - ref_rows) <= ulp), f"appended keys differ (b={b}, g={g})"
+            # bf16: one ulp of the stored value; fp32: a few ulps plus a floor of 1e-6 of the
+            # row's largest entry (a rotated entry x cos - y sin can cancel to ~0)
+            if dtype == "bf16":
+                bound = np.abs(ref_rows) * 2.0 ** -7
+            else:
+                bound = np.abs(ref_rows) * 2.0 ** -20 + 1e-6 * np.abs(ref_rows).max(axis=1, keepdims=True)
+            assert np.all(np.abs(got_rows - ref_rows) <= bound + 1e-30), f"appended keys differ (b={b}, g={g})"
             if vc is not None:
                 np.testing.assert_array_equal(host(vc[b, g, Lb:Lb + nq]), vcg[Lb:Lb + nq])
     for b, (gs, os_) in per_seq.items():
@@ -101,6 +106,8 @@ def test_head_dims_and_row_tiles(D):
     for (hq, hkv, nq) in ((4, 4, 5), (8, 2, 5), (16, 2, 5), (16, 2, 8)):
         ly = configs.AttnLayer("global", hq, hkv, D, 0, D // 4, 1e6, True)
         run_case(ly, 2, nq, [45, 300], 320, 3, tag=f"tiles-{D}-{hq}/{hkv}x{nq}")
+        if D == 512:
+            continue  # separate 512-wide values are not supported (see test_abi)
         ly = configs.AttnLayer("local", hq, hkv, D, 77, D, 1e4, False)
         run_case(ly, 2, nq, [45, 300], 320, 4, tag=f"tiles-local-{D}-{hq}/{hkv}x{nq}")
 

@@ -123,7 +123,7 @@ def lockstep(cfg, steps, seed=0, check_drafter=False):
         e = rel_l2(hg, ref["h"])
         worst_h = max(worst_h, e)
         assert e <= (1e-2 if cfg.dtype == "bf16" else 1e-5), f"step {s}: final hidden rel L2 {e:.2e}"
-        commit = compare_step(vs, ref, k, B, range(B), f"step {s}")
+        commit = compare_step(vs, ref, k, B, range(B), f"step {s} (final hidden rel L2 {e:.2e})")
         # lockstep: both sides continue from the oracle's decision
         new_len = np.array([old[b] + commit[b][0] + 1 for b in range(B)], dtype=np.int32)
         state["L"] = new_len.copy()
