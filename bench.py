@@ -57,16 +57,30 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for profilers: no sweep, no oracle")
-    ap.add_argument("--only", choices=["attn_global", "attn_local", "lmhead", "lmhead_sample"], default=None,
-                    help="time one call of the step in isolation at the workload's shapes")
+    ap.add_argument("--only", default=None,
+                    help="time calls of the step in isolation at the workload's shapes; comma-separated "
+                         f"from {', '.join(ONLY_CALLS)}")
     ap.add_argument("--iters", type=int, default=50, help="iterations of --only")
     return ap.parse_args()
 
 
+ONLY_CALLS = ("attn_global", "attn_local", "lmhead", "lmhead_sample", "qkv_local", "qkv_global", "o_local",
+              "o_global", "gu", "down")
+
+
 def bench_only(args):
+    for name in args.only.split(","):
+        if name not in ONLY_CALLS:
+            raise SystemExit(f"unknown --only call {name!r}; choose from {', '.join(ONLY_CALLS)}")
+    for name in args.only.split(","):
+        bench_one(args, name)
+
+
+def bench_one(args, only):
     """One call of the verify step, timed alone at the workload's shapes (batch,
     k, context): the global-layer attention (16q/4kv, D=512, K=V, p-RoPE), a local
-    layer's attention (16q/8kv, D=256, window 1024) or the LM-head select."""
+    layer's attention (16q/8kv, D=256, window 1024), the LM-head select, or one of
+    a layer's projections (fused q/k/v, output, gate/up, down)."""
     import torch
 
     from mtp_draft_verification_amd import _lib as L
@@ -77,8 +91,8 @@ def bench_only(args):
     cfg = dataclasses.replace(configs.STACK, batch=args.batch, k=args.k, ctx=args.ctx)
     B, nq = cfg.batch, cfg.k + 1
     stream = torch.cuda.current_stream()
-    if args.only.startswith("attn"):
-        ly = cfg.layers[-1] if args.only == "attn_global" else cfg.layers[0]
+    if only.startswith("attn"):
+        ly = cfg.layers[-1] if only == "attn_global" else cfg.layers[0]
         cap = cfg.ctx + nq + 8
         lo = 0 if ly.window == 0 else max(0, cfg.ctx - ly.window - 8)
         kc = torch.zeros((B, ly.n_heads_kv, cap, ly.head_dim), dtype=torch.bfloat16, device=dev)
@@ -94,18 +108,35 @@ def bench_only(args):
         call = lambda: L.sv_verify_attn(desc, q, kn, vn, kc, vc, cl, out, ws, None, stream)
         lens = [cfg.ctx] * B
         byts = call_bytes(cfg, lens)["L5.attn" if ly.window == 0 else "L0.attn"]
-    else:
-        mode = L.SV_SELECT_GREEDY if args.only == "lmhead" else L.SV_SELECT_SAMPLE
+    elif only.startswith("lmhead"):
+        mode = L.SV_SELECT_GREEDY if only == "lmhead" else L.SV_SELECT_SAMPLE
         R = B * nq
         h = inputs.normal((R, cfg.d_model), 1.0, 0, "h", dev)
         W = inputs.normal((cfg.vocab, cfg.d_model), cfg.d_model ** -0.5, 0, "E", dev)
         drafts = torch.randint(0, cfg.vocab, (B, cfg.k), dtype=torch.int32, device=dev)
         u_tok = torch.rand((B, cfg.vocab), device=dev) if mode == L.SV_SELECT_SAMPLE else None
         desc = L.LMHeadDesc(batch=B, k=cfg.k, d_model=cfg.d_model, vocab=cfg.vocab, mode=mode, dtype=L.SV_BF16)
-        ws = torch.empty(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
         stats = torch.empty((R, L.ROW_STATS_WORDS), dtype=torch.int32, device=dev)
         call = lambda: L.sv_lmhead_select(desc, h, W, drafts, u_tok, None, stats, None, None, ws, stream)
         byts = call_bytes(cfg, [cfg.ctx] * B)["lmhead"]
+    else:
+        R = B * nq
+        loc, glo = cfg.layers[0], cfg.layers[-1]
+        nout = lambda ly: ly.n_heads_q * ly.head_dim + (1 if ly.k_is_v else 2) * ly.n_heads_kv * ly.head_dim
+        K, N, epi = {"qkv_local": (cfg.d_model, nout(loc), L.SV_EPI_STORE),
+                     "qkv_global": (cfg.d_model, nout(glo), L.SV_EPI_STORE),
+                     "o_local": (loc.n_heads_q * loc.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
+                     "o_global": (glo.n_heads_q * glo.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
+                     "gu": (cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_STORE),
+                     "down": (cfg.d_ff, cfg.d_model, L.SV_EPI_ADD_F32)}[only]
+        x = inputs.normal((R, K), 1.0, 0, "x", dev)
+        W = inputs.normal((N, K), K ** -0.5, 0, "W", dev)
+        y = torch.zeros((R, N), dtype=torch.float32 if epi == L.SV_EPI_ADD_F32 else torch.bfloat16, device=dev)
+        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi)
+        ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
+        call = lambda: L.sv_linear(desc, x, W, y, ws, stream)
+        byts = 2 * (N * K + R * K) + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 2)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -118,7 +149,7 @@ def bench_only(args):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.iters
     gbs = byts / (us * 1e-6) / 1e9
-    print(json.dumps({"call": args.only, "batch": B, "k": cfg.k, "ctx": cfg.ctx, "us_per_call": round(us, 2),
+    print(json.dumps({"call": only, "batch": B, "k": cfg.k, "ctx": cfg.ctx, "us_per_call": round(us, 2),
                       "alg_bytes": int(byts), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
                       "source_digest": source_digest()}), flush=True)
 
@@ -253,7 +284,8 @@ def run_workload(cfg, W, steps, warmup, seed, dev, time_calls=None):
         names += [f"L{i}.{c}" for c in ("qkv", "attn", "o", "gu", "geglu", "down")]
     timers = {n: [] for n in names}
     replay(timers)
-    call_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in timers.items() if v}
+    # median: a call's time in the instrumented pass can include an occasional host-side stall
+    call_ms = {n: float(np.median([a.elapsed_time(b) for a, b in v])) for n, v in timers.items() if v}
     byts = call_bytes(cfg, mean_lens)
     dominant = max((n for n in call_ms if n in byts), key=lambda n: call_ms[n])
     if time_calls:

@@ -166,6 +166,12 @@ typedef struct {
   sv_dtype dtype;        /* of hidden and w */
 } sv_lmhead_desc;
 
+/* Workspace of sv_lmhead_select, 0 for an invalid descriptor.  bf16: arrival
+ * counters, split partials and per-workgroup select partials.  The workspace must be
+ * zero-filled before its first use; every call leaves its counters zero again, so
+ * one fill serves any sequence of calls (of any descriptor) on the same workspace.
+ * Calls that overlap in time must not share a workspace.  The counters occupy the
+ * first 256 KiB in every layout (shared with sv_linear's). */
 size_t sv_lmhead_workspace(const sv_lmhead_desc* desc);
 
 /* LM-head skinny GEMM z = h W^T fused with a split-vocabulary select
@@ -256,9 +262,15 @@ typedef struct {
   sv_epilogue epilogue;
 } sv_linear_desc;
 
+/* Workspace of sv_linear (0 in fp32): arrival counters and split partials.  Same
+ * contract as sv_lmhead_workspace: zero-filled before first use, left zero by
+ * every call, one call at a time. */
 size_t sv_linear_workspace(const sv_linear_desc* desc);
 
-/* Skinny projection y = x W^T for the few verify rows: x [R, K], W [N, K]. */
+/* Skinny projection y = x W^T for the few verify rows: x [R, K], W [N, K].
+ * bf16: one persistent workgroup per CU over (64T-feature block, 64-dim chunk)
+ * units; a block split across workgroups is summed in a fixed order, so results
+ * are deterministic for a given device. */
 int sv_linear(const sv_linear_desc* desc, const void* x, const void* w, void* y,
               void* workspace, size_t workspace_bytes, void* stream);
 

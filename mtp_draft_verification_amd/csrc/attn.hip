@@ -180,51 +180,6 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
 
-// 16 bytes per lane from global memory straight into LDS at (lds_base + 16 * lane),
-// gaddr = base (wave-uniform) + off (per lane, bytes).  Issued from inline asm so
-// the compiler, which cannot tell which ring stage a DMA writes, does not stall
-// every LDS read on it; completion is waited for explicitly with wait_vm.  M0 (the
-// LDS base) is saved and restored around the instruction.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-// wait until at most n of this wave's vector memory operations are outstanding
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
-    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
-
-// Workgroup barrier for LDS traffic only: this wave's LDS writes have completed,
-// but DMA into LDS still in flight is not waited for (each tile waits for its own
-// DMA explicitly), which keeps the ring's prefetches going across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int D, int MT, bool KV_SAME>
 struct AttnCfg {
   static constexpr int DS = D / 4;              // PV dims per wave
@@ -243,7 +198,7 @@ struct AttnCfg {
   static constexpr int NS = NS_FIT < 4 ? NS_FIT : 4;  // ring stages
   static_assert(NS >= 2, "tile does not fit twice in LDS");
   static_assert(DT >= 1 && RPI >= 1 && NI >= 1, "unsupported head_dim");
-  static_assert(NI == 4 || NI == 8 || NI == 16, "wait_vm needs these counts");
+  static_assert((NS - 2) * NI <= 63, "vmcnt range");
 };
 
 template <int D, int MT, bool KV_SAME>
@@ -326,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qreg[mt][s].b));
-      wait_vm(0);
+      wait_vm_n<0>();
       __syncthreads();
 
       f32x4_t O[DT][MT];
@@ -391,7 +346,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         if (t >= ntiles) break;
         const int64_t t0 = a0 + (int64_t)t * TK;
         const int ahead = (NS - 2) < (ntiles - 1 - t) ? (NS - 2) : (ntiles - 1 - t);
-        wait_vm(ahead * NI);
+        wait_stages<NI>(ahead);
         lds_barrier();  // tile t is in LDS for every wave; tile t-1 is no longer read
         if (t + NS - 1 < ntiles) issue(t + NS - 1, stage_of((u + NS - 1) % NS));
 

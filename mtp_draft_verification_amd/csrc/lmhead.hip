@@ -6,19 +6,18 @@
 //     and never written to memory; each workgroup leaves one partial per row
 //     and lmhead_merge combines them in a fixed order (deterministic).
 //   * plain projections of a decoder layer (store bf16, or add into the fp32
-//     residual stream), optionally split along K with an ordered reduction.
+//     residual stream).
 //
 // Tiling (bf16): the vocabulary / output features are the MFMA M side (16 per
-// tile), the <= 64 verify rows the N side.  Each wave streams T tiles of W
-// straight from HBM into MFMA A operands (16 B per lane, one k-step of 32
-// columns per load), the rows of x come from L2 as B operands, and the
-// accumulators stay in registers for the whole K range.
+// tile), the <= 64 verify rows the N side.  One persistent workgroup per CU
+// streams its share of W (and the rows of x) through an LDS ring fed by direct
+// HBM -> LDS DMA; the accumulators stay in registers across the K range.
 #include "sv_device.h"
 #include "sv_host.h"
 
 namespace sv {
 
-enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_PARTIAL = 5 };
+enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4 };
 
 struct SelPart {   // per (workgroup, row) partial of the select epilogue
   float t1v, t2v;  // top-2 logits (RESIDUAL: residual-draw scores)
@@ -34,8 +33,7 @@ struct GemmParams {
   const uint16_t* x;     // [R, K] rows (RESIDUAL: the hidden states, gathered per slot)
   const uint16_t* w;     // [N, K]
   int R, K, N;
-  int k0_stride;         // K per split (split-K)
-  int nblk;              // N blocks of the workgroup tile
+  int nblk, kch;         // feature blocks, 64-wide K chunks
   // select
   int batch, kdr;        // sequences and drafts per sequence
   const int32_t* drafts; // [batch, kdr]
@@ -43,10 +41,12 @@ struct GemmParams {
   const float* q_rows;   // [batch, kdr, N]
   const sv_row_stats* stats_in;
   sv_accept_out* acc;
-  SelPart* sel;          // [gridDim.x][R]
+  SelPart* sel;          // [grid][rows]
   // projections
   void* y;               // [R, N] bf16 or fp32
-  float* part;           // [splits][R][N]
+  // stream-K
+  float* part;           // [grid][2][rows][NB] partial sums
+  int32_t* cnt;          // [nblk][4] arrival counters, zero between calls
 };
 
 // ---------------------------------------------------------------------------
@@ -178,87 +178,203 @@ __device__ __forceinline__ RowState from_part(const SelPart& p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA skinny GEMM with fused epilogue
+// bf16 MFMA skinny GEMM, stream-K over a DMA ring, with fused epilogues
 // ---------------------------------------------------------------------------
-template <int MT, int T, int MODE>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
-  constexpr bool SELECT = MODE <= GM_RESIDUAL;
-  constexpr int NB = 4 * T * 16;       // output features per workgroup block
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int K = p.K;
-  const int split = blockIdx.y;
-  const int kbeg = split * p.k0_stride;
-  const int nks = min(p.k0_stride, K - kbeg) / 32;
+// Work units are (block of NB = 64 T output features, chunk of 64 input dims).
+// The nblk * kch units are cut into `grid` contiguous ranges, one per persistent
+// workgroup (one per CU: the ring takes the whole LDS).  Each chunk of W (NB rows
+// x 128 B) and of x (16 MT rows x 128 B) is copied HBM/L2 -> LDS by direct DMA,
+// NS chunks deep, and read back as MFMA operands.  A block whose chunk range
+// spans several workgroups leaves one fp32 partial per workgroup; per wave slice
+// an arrival counter picks the last arriver, which adds the partials in
+// workgroup order (deterministic) and runs the epilogue.
+template <int MT, int T>
+struct RingCfg {
+  static constexpr int NB = 64 * T;            // output features per block
+  static constexpr int WI = 2 * T;             // W DMA instructions per wave per chunk
+  static constexpr int XI = 2 * MT;            // x DMA instructions per chunk (workgroup)
+  static constexpr int NX = (XI + 3) / 4;      // x DMA instructions per wave
+  static constexpr int NI = WI + NX;           // DMA instructions per wave per chunk
+  static constexpr int WSTAGE = NB * 128;
+  static constexpr int STAGEB = WSTAGE + XI * 1024;
+  static constexpr int NS_FIT = (160 * 1024) / STAGEB;
+  static constexpr int NS = NS_FIT < 6 ? NS_FIT : 6;
+  static_assert(NS >= 3, "ring needs three stages");
+  static_assert((NS - 2) * NI <= 63, "vmcnt range");
+  static_assert(4 * MT * 16 * (int)sizeof(SelPart) <= NS * STAGEB, "select merge reuses the ring");
+};
 
-  // B operands: rows of x (gathered per slot in RESIDUAL mode)
-  const uint16_t* xrow[MT];
+// 16-byte slot swizzle inside a 128-byte row chunk (r = row % 16): 16 consecutive
+// rows at the same chunk land in distinct bank groups.
+__device__ __forceinline__ int gswz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// hardware places consecutive workgroups on consecutive XCDs; renumber so that
+// consecutive ranges (which share blocks and their partials) sit on one XCD
+__device__ __forceinline__ int logical_wg(int b, int P) {
+  if (P & 7) return b;
+  return (b & 7) * (P >> 3) + (b >> 3);
+}
+
+// raw buffer descriptor word 3 for gfx950 (32-bit elements, no swizzle) and the
+// sc1 cache policy: stores write through to, and loads read from, the device's
+// coherence point
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCoherent = 16;
+
+template <int MT, int T, int MODE>
+__global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
+  using C = RingCfg<MT, T>;
+  constexpr bool SELECT = MODE <= GM_RESIDUAL;
+  constexpr int NB = C::NB, NS = C::NS, WROWS = 16 * T;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGEB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA bases live in SGPRs
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = p.K, KCH = p.kch, P = gridDim.x;
+  const int me = logical_wg(blockIdx.x, P);
+  const int64_t tot = (int64_t)p.nblk * KCH;
+  const int c_begin = (int)(tot * me / P);
+  const int n_it = (int)(tot * (me + 1) / P) - c_begin;
+  const bool ragged = (K & 63) != 0;  // last chunk holds one k-step of 32
+  const int nx = MODE == GM_RESIDUAL ? p.batch : p.R;
+  const uint32_t ring_lds = lds_addr(ring);
+
+  // ---- per-lane DMA offsets (loop invariant) ----
+  const int dl8 = lane >> 3;
+  const int cq[2] = {(lane & 7) ^ gswz(dl8), (lane & 7) ^ gswz(8 + dl8)};  // chunk fetched, by row parity
+  const uint32_t adj[2] = {cq[0] >= 4 ? 64u : 0u, cq[1] >= 4 ? 64u : 0u};
+  uint32_t woff[C::WI];
+#pragma unroll
+  for (int i = 0; i < C::WI; ++i) woff[i] = (uint32_t)((i * 8 + dl8) * K * 2 + cq[i & 1] * 16);
+  uint32_t xoff[C::NX], xlds[C::NX];
+  int xpar[C::NX];
+#pragma unroll
+  for (int ii = 0; ii < C::NX; ++ii) {
+    const int j = (wave + 4 * ii) < C::XI ? (wave + 4 * ii) : C::XI - 1;
+    const int r = j * 8 + dl8;
+    int xr = 0;
+    if (r < nx) {
+      if constexpr (MODE == GM_RESIDUAL) {
+        const int h = p.acc[r].hidden_row;
+        xr = (h >= 0 && h < p.R) ? h : 0;
+      } else {
+        xr = r;
+      }
+    }
+    xpar[ii] = j & 1;
+    xoff[ii] = (uint32_t)(xr * K * 2 + cq[j & 1] * 16);
+    xlds[ii] = (uint32_t)(C::WSTAGE + j * 1024);
+  }
+
+  // ---- select state ----
   RowCtx ctx[MT];
   RowState st[MT];
+  if constexpr (SELECT) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = mt * 16 + lr;
-    xrow[mt] = nullptr;
-    if constexpr (SELECT) {
-      ctx[mt] = make_ctx<MODE>(p, r);
+    for (int mt = 0; mt < MT; ++mt) {
+      ctx[mt] = make_ctx<MODE>(p, mt * 16 + lr);
       st[mt].init();
-      if (ctx[mt].valid) {
-        const int hr = MODE == GM_RESIDUAL ? p.acc[r].hidden_row : r;
-        xrow[mt] = p.x + (int64_t)hr * K + kbeg + lg * 8;
-      }
-    } else {
-      if (r < p.R) xrow[mt] = p.x + (int64_t)r * K + kbeg + lg * 8;
     }
   }
 
-  for (int blk = blockIdx.x; blk < p.nblk; blk += gridDim.x) {
-    const int n0 = blk * NB + wave * T * 16;
-    const uint16_t* wrow[T];
-    bool tv[T];
+  // ---- DMA issue of chunk unit (b, kc) into ring stage s ----
+  auto issue = [&](int b, int kc, int s) {
+    const bool tail = ragged && kc == KCH - 1;
+    const int row0 = b * NB + wave * WROWS;
+    const uint8_t* wb = (const uint8_t*)p.w + ((int64_t)(row0 < p.N ? row0 : 0) * K + kc * 64) * 2;
+    const uint32_t dst = ring_lds + (uint32_t)(s * C::STAGEB);
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      tv[t] = n0 + t * 16 < p.N;
-      wrow[t] = p.w + (int64_t)(tv[t] ? n0 + t * 16 + lr : 0) * K + kbeg + lg * 8;
-    }
-    f32x4_t acc[T][MT];
+    for (int i = 0; i < C::WI; ++i)
+      dma16(wb, woff[i] - (tail ? adj[i & 1] : 0u), dst + (uint32_t)((wave * C::WI + i) * 1024));
+    const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * 128;
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ii = 0; ii < C::NX; ++ii) dma16(xb, xoff[ii] - (tail ? adj[xpar[ii]] : 0u), dst + xlds[ii]);
+  };
 
-    V16 wc[T], xc[MT];
-#pragma unroll
-    for (int t = 0; t < T; ++t) wc[t].u = tv[t] ? *(const uint4*)(wrow[t]) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xc[mt].u = xrow[mt] ? *(const uint4*)(xrow[mt]) : make_uint4(0, 0, 0, 0);
+  // ---- stream-K bookkeeping ----
+  auto owner = [&](int64_t c) -> int { return (int)(((c + 1) * P - 1) / tot); };
+  // partials [grid][2][nx][NB] fp32 behind a buffer descriptor (byte offsets)
+  const __amdgpu_buffer_rsrc_t part_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(p.part, (short)0, (int)(P * 2 * nx * NB * 4), kBufferWord3);
+  auto part_off = [&](int w, int sl, int r) -> uint32_t { return (uint32_t)((((w * 2 + sl) * nx + r) * NB) * 4); };
+  auto first_block = [&](int w) -> int { return (int)((tot * w / P) / KCH); };
+  const int my_first = c_begin / KCH;
 
-    for (int ks = 0; ks < nks; ++ks) {
-      V16 wn[T], xn[MT];
-      const bool more = ks + 1 < nks;
-      if (more) {
-        const int o = (ks + 1) * 32;
+  f32x4_t acc[T][MT];
 #pragma unroll
-        for (int t = 0; t < T; ++t) wn[t].u = tv[t] ? *(const uint4*)(wrow[t] + o) : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xn[mt].u = xrow[mt] ? *(const uint4*)(xrow[mt] + o) : make_uint4(0, 0, 0, 0);
-      }
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // end of this workgroup's range in block b; `full` if it covered the whole block
+  auto seg_end = [&](int b, bool full) {
+    const int row0 = b * NB + wave * WROWS;
+    if (row0 >= p.N) return;  // wave slice past the last feature (uniform per wave)
+    if (!full) {
+      // Partials move through buffer stores / loads with the sc1 (device-coherent)
+      // cache policy and the counter through a device-scope atomic: no L2 writeback
+      // or invalidation (which a fence would issue) is needed.
+      const int slot = b == my_first ? 0 : 1;
+      const uint32_t lane_off = (uint32_t)((wave * WROWS + lg * 4) * 4);
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(wc[t].b, xc[mt].b, acc[t][mt]);
-      if (more) {
+        for (int mt = 0; mt < MT; ++mt) {
+          const int r = mt * 16 + lr;
+          if (r < nx)
+            __builtin_amdgcn_raw_buffer_store_b128(acc[t][mt], part_rsrc,
+                                                   part_off(me, slot, r) + lane_off + t * 64, 0, kCoherent);
+        }
+      wait_vm_n<0>();  // the partial stores have completed before the arrival is counted
+      int old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + b * 4 + wave, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __shfl(old, 0, 64);
+      const int w_lo = owner((int64_t)b * KCH), w_hi = owner((int64_t)b * KCH + KCH - 1);
+      if (old != w_hi - w_lo) return;  // another workgroup finishes this slice
+      asm volatile("" ::: "memory");
+      // sum of the partials in workgroup order (this workgroup's own included),
+      // DEPTH segments' loads in flight at a time
+      constexpr int DEPTH = T >= 4 ? 1 : 4;
 #pragma unroll
-        for (int t = 0; t < T; ++t) wc[t] = wn[t];
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xc[mt] = xn[mt];
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int w0 = w_lo; w0 <= w_hi; w0 += DEPTH) {
+        f32x4_t v[DEPTH][T][MT];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          const int w = w0 + d;
+          const int sl = (w <= w_hi && b == first_block(w)) ? 0 : 1;
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const int r = mt * 16 + lr;
+              v[d][t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              if (w <= w_hi && r < nx)
+                v[d][t][mt] = __builtin_amdgcn_raw_buffer_load_b128(part_rsrc, part_off(w, sl, r) + lane_off + t * 64,
+                                                                   0, kCoherent);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (w0 + d <= w_hi) {
+                acc[t][mt][0] += v[d][t][mt][0]; acc[t][mt][1] += v[d][t][mt][1];
+                acc[t][mt][2] += v[d][t][mt][2]; acc[t][mt][3] += v[d][t][mt][3];
+              }
       }
+      // every arrival has been counted: leave the counter zero for the next call
+      if (lane == 0) __hip_atomic_store(p.cnt + b * 4 + wave, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-
-    // accumulator lane: row (mt*16 + lr), features n0 + 16 t + 4 lg + {0..3}
+    // accumulator lane: x row (mt*16 + lr), features row0 + 16 t + 4 lg + {0..3}
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      if (!tv[t]) continue;
-      const int v0 = n0 + t * 16 + lg * 4;
+      const int v0 = row0 + t * 16 + lg * 4;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + lr;
@@ -266,41 +382,88 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
         if constexpr (SELECT) {
           select_push4<MODE>(st[mt], ctx[mt], z, v0);
         } else if constexpr (MODE == GM_STORE_BF16) {
-          if (r < p.R)
+          if (r < nx)
             *(uint2*)((uint16_t*)p.y + (int64_t)r * p.N + v0) = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
-        } else if constexpr (MODE == GM_ADD_F32) {
-          if (r < p.R) {
+        } else {  // GM_ADD_F32
+          if (r < nx) {
             f32x4_t* d = (f32x4_t*)((float*)p.y + (int64_t)r * p.N + v0);
             f32x4_t o = *d;
             o[0] += z[0]; o[1] += z[1]; o[2] += z[2]; o[3] += z[3];
             *d = o;
           }
-        } else {  // GM_PARTIAL
-          if (r < p.R)
-            *(f32x4_t*)(p.part + ((int64_t)split * p.R + r) * p.N + v0) = f32x4_t{z[0], z[1], z[2], z[3]};
         }
       }
     }
+  };
+
+  // ---- the ring ----
+  int ib = c_begin / KCH, ikc = c_begin - ib * KCH;  // next unit to issue
+  const int npro = n_it < NS - 1 ? n_it : NS - 1;
+  for (int i = 0; i < npro; ++i) {
+    issue(ib, ikc, i);
+    if (++ikc == KCH) { ikc = 0; ++ib; }
+  }
+  int cb = c_begin / KCH, ckc = c_begin - cb * KCH;  // unit being computed
+  int seg_kc0 = ckc;                                 // first chunk of the current segment
+  int s = 0, si = npro % NS;
+  const uint8_t* wrd = ring + (wave * WROWS + lr) * 128;  // + t*2048 + chunk slot
+  const uint8_t* xrd = ring + C::WSTAGE + lr * 128;        // + mt*2048 + chunk slot
+  const int fsw = gswz(lr);
+  for (int it = 0; it < n_it; ++it) {
+    const int ahead = (NS - 2) < (n_it - 1 - it) ? (NS - 2) : (n_it - 1 - it);
+    wait_stages<C::NI>(ahead);
+    lds_barrier();  // unit `it` is in LDS for every wave; unit it-1 is no longer read
+    if (it + NS - 1 < n_it) {
+      issue(ib, ikc, si);
+      if (++ikc == KCH) { ikc = 0; ++ib; }
+      si = si + 1 == NS ? 0 : si + 1;
+    }
+    const int nks = (ragged && ckc == KCH - 1) ? 1 : 2;
+    const uint8_t* ws = wrd + s * C::STAGEB;
+    const uint8_t* xs = xrd + s * C::STAGEB;
+    for (int js = 0; js < nks; ++js) {
+      const int so = ((js * 4 + lg) ^ fsw) << 4;
+      V16 a[T], bx[MT];
+#pragma unroll
+      for (int t = 0; t < T; ++t) a[t].u = *(const uint4*)(ws + t * 2048 + so);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) bx[mt].u = *(const uint4*)(xs + mt * 2048 + so);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a[t].b, bx[mt].b, acc[t][mt]);
+    }
+    s = s + 1 == NS ? 0 : s + 1;
+    if (ckc == KCH - 1 || it == n_it - 1) {
+      seg_end(cb, seg_kc0 == 0 && ckc == KCH - 1);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      seg_kc0 = 0;
+    }
+    if (++ckc == KCH) { ckc = 0; ++cb; }
   }
 
   if constexpr (SELECT) {
     // lanes lr, lr+16, lr+32, lr+48 hold the same row: combine, then the 4 waves
-    __shared__ SelPart s_sel[4][MT][16];
+    wait_vm_n<0>();
+    __syncthreads();  // the ring is idle: reuse it
+    SelPart* s_sel = (SelPart*)ring;  // [4][MT][16]
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       state_merge_xor(st[mt], 16);
       state_merge_xor(st[mt], 32);
-      if (lg == 0) s_sel[wave][mt][lr] = to_part(st[mt]);
+      if (lg == 0) s_sel[(wave * MT + mt) * 16 + lr] = to_part(st[mt]);
     }
     __syncthreads();
     if (wave == 0 && lg == 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + lr;
-        RowState a = from_part(s_sel[0][mt][lr]);
-        for (int w = 1; w < 4; ++w) state_merge(a, from_part(s_sel[w][mt][lr]));
-        const int nrows = MODE == GM_RESIDUAL ? p.batch : p.R;
-        if (r < nrows) p.sel[(int64_t)blockIdx.x * nrows + r] = to_part(a);
+        RowState a = from_part(s_sel[mt * 16 + lr]);
+        for (int w = 1; w < 4; ++w) state_merge(a, from_part(s_sel[(w * MT + mt) * 16 + lr]));
+        if (r < nx) p.sel[(int64_t)me * nx + r] = to_part(a);
       }
     }
   }
@@ -403,29 +566,6 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(GemmParams p, int npa
   }
 }
 
-// ---------------------------------------------------------------------------
-// split-K reduction of the projections (fixed split order)
-// ---------------------------------------------------------------------------
-template <int MODE>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int splits) {
-  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const int64_t n = (int64_t)p.R * p.N;
-  if (i4 >= n) return;
-  f32x4_t a = *(const f32x4_t*)(p.part + i4);
-  for (int s = 1; s < splits; ++s) {
-    const f32x4_t o = *(const f32x4_t*)(p.part + (int64_t)s * n + i4);
-    a[0] += o[0]; a[1] += o[1]; a[2] += o[2]; a[3] += o[3];
-  }
-  if constexpr (MODE == GM_STORE_BF16) {
-    *(uint2*)((uint16_t*)p.y + i4) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-  } else {
-    f32x4_t* d = (f32x4_t*)((float*)p.y + i4);
-    f32x4_t o = *d;
-    o[0] += a[0]; o[1] += a[1]; o[2] += a[2]; o[3] += a[3];
-    *d = o;
-  }
-}
-
 // fp32 projection (small shapes): one thread per output element
 __global__ __launch_bounds__(256) void linear_f32_kernel(const float* x, const float* w, float* y, int R, int K,
                                                          int N, int add) {
@@ -440,17 +580,44 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* x, const f
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static constexpr int kSelT = 8;          // W tiles per wave in the LM head
-static constexpr int kSelNB = 4 * kSelT * 16;
-static constexpr int kSelGridMax = 1024;
+static constexpr int kMaxWG = 256;   // persistent workgroups at most (workspace sizing)
+// Arrival counters sit at the start of every workspace in a region of fixed size, so
+// calls with different descriptors can share one workspace.
+static constexpr int kCntWords = 65536;
+static constexpr int kSelT = 4;      // W tiles per wave in the LM head
+// W tiles per wave in the projections: one for small weights (more, shorter blocks:
+// fewer workgroups share a block, so the ordered sum of split partials is short),
+// two otherwise (half the x re-reads per weight byte)
+static int lin_tiles(const sv_linear_desc& d) {
+  return (int64_t)d.in_features * d.out_features < ((int64_t)24 << 20) ? 1 : 2;
+}
+
+struct RingPlan {
+  int T, nx, nblk, kch, grid;
+  size_t cnt_bytes, part_bytes;
+};
+
+static RingPlan ring_plan(int T, int nx, int K, int N, int max_wg) {
+  RingPlan pl{};
+  pl.T = T;
+  pl.nx = nx;
+  pl.nblk = (N + 64 * T - 1) / (64 * T);
+  pl.kch = (K + 63) / 64;
+  const int64_t tot = (int64_t)pl.nblk * pl.kch;
+  pl.grid = (int)(tot < max_wg ? tot : max_wg);
+  pl.cnt_bytes = (size_t)kCntWords * sizeof(int32_t);
+  pl.part_bytes = align_up((size_t)kMaxWG * 2 * nx * 64 * T * sizeof(float), 256);
+  return pl;
+}
+
+static int live_wg() {
+  const int c = device_cus();
+  return c < kMaxWG ? c : kMaxWG;
+}
 
 static int lm_rows(const sv_lmhead_desc& d) { return d.batch * (d.k + 1); }
-
-static int sel_grid(const sv_lmhead_desc& d) {
-  if (d.dtype == SV_F32) return (d.vocab + 255) / 256;
-  const int nblk = (d.vocab + kSelNB - 1) / kSelNB;
-  return nblk < kSelGridMax ? nblk : kSelGridMax;
-}
+static int sel_rows(const sv_lmhead_desc& d) { return d.mode == SV_SELECT_RESIDUAL ? d.batch : lm_rows(d); }
+static int f32_grid(const sv_lmhead_desc& d) { return (d.vocab + 255) / 256; }
 
 static int validate_lmhead(const sv_lmhead_desc* d) {
   if (!d) return SV_ERR_ARG;
@@ -461,6 +628,7 @@ static int validate_lmhead(const sv_lmhead_desc* d) {
   if (d->dtype == SV_BF16) {
     if (d->d_model % 32) return SV_ERR_ARG;
     if (lm_rows(*d) > 64) return SV_ERR_UNSUPPORTED;
+    if ((int64_t)(d->vocab + 64 * kSelT - 1) / (64 * kSelT) * 4 > kCntWords) return SV_ERR_UNSUPPORTED;
   } else if (d->dtype == SV_F32) {
     if (lm_rows(*d) > 256) return SV_ERR_UNSUPPORTED;
   } else {
@@ -469,49 +637,21 @@ static int validate_lmhead(const sv_lmhead_desc* d) {
   return SV_OK;
 }
 
-template <int MT, int MODE>
-static void launch_sel(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_mfma_kernel<MT, kSelT, MODE>), dim3(grid, 1), dim3(256), 0, s, p);
+template <int MT, int T, int MODE>
+static void launch_ring(const GemmParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_ring_kernel<MT, T, MODE>), dim3(grid), dim3(256), 0, s, p);
 }
 
-template <int MODE>
-static int dispatch_sel(const GemmParams& p, int rows, int grid, hipStream_t s) {
-  switch ((rows + 15) / 16) {
-    case 1: launch_sel<1, MODE>(p, grid, s); break;
-    case 2: launch_sel<2, MODE>(p, grid, s); break;
-    case 3: launch_sel<3, MODE>(p, grid, s); break;
-    case 4: launch_sel<4, MODE>(p, grid, s); break;
+template <int T, int MODE>
+static int dispatch_ring(const GemmParams& p, int nx, int grid, hipStream_t s) {
+  switch ((nx + 15) / 16) {
+    case 1: launch_ring<1, T, MODE>(p, grid, s); break;
+    case 2: launch_ring<2, T, MODE>(p, grid, s); break;
+    case 3: launch_ring<3, T, MODE>(p, grid, s); break;
+    case 4: launch_ring<4, T, MODE>(p, grid, s); break;
     default: return SV_ERR_UNSUPPORTED;
   }
   return SV_OK;
-}
-
-// projections: tiles per wave and K splits chosen so the grid fills the chip
-static constexpr int kLinT = 2;
-static constexpr int kLinNB = 4 * kLinT * 16;
-
-struct LinPlan {
-  int nblk, splits, kstride;
-  size_t part_bytes;
-};
-
-static LinPlan lin_plan(const sv_linear_desc& d) {
-  LinPlan pl{};
-  pl.nblk = (d.out_features + kLinNB - 1) / kLinNB;
-  pl.splits = 1;
-  pl.kstride = d.in_features;
-  if (d.dtype == SV_BF16) {
-    const int ksteps = d.in_features / 32;
-    int want = (1024 + pl.nblk - 1) / pl.nblk;  // aim at ~1024 workgroups
-    if (want > ksteps / 8) want = ksteps / 8;  // keep >= 8 k-steps per split
-    if (want > 16) want = 16;
-    if (want < 1) want = 1;
-    const int per = (ksteps + want - 1) / want;
-    pl.kstride = per * 32;
-    pl.splits = (d.in_features + pl.kstride - 1) / pl.kstride;
-    if (pl.splits > 1) pl.part_bytes = align_up((size_t)pl.splits * d.rows * d.out_features * 4, 256);
-  }
-  return pl;
 }
 
 static int validate_linear(const sv_linear_desc* d) {
@@ -522,27 +662,11 @@ static int validate_linear(const sv_linear_desc* d) {
   if (d->dtype == SV_BF16) {
     if (d->in_features % 32) return SV_ERR_ARG;
     if (d->rows > 64) return SV_ERR_UNSUPPORTED;
+    if ((int64_t)(d->out_features + 63) / 64 * 4 > kCntWords) return SV_ERR_UNSUPPORTED;
   } else if (d->dtype == SV_F32) {
     if ((int64_t)d->rows * d->out_features > ((int64_t)1 << 28)) return SV_ERR_UNSUPPORTED;
   } else {
     return SV_ERR_ARG;
-  }
-  return SV_OK;
-}
-
-template <int MT, int MODE>
-static void launch_lin(const GemmParams& p, int gx, int gy, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_mfma_kernel<MT, kLinT, MODE>), dim3(gx, gy), dim3(256), 0, s, p);
-}
-
-template <int MODE>
-static int dispatch_lin(const GemmParams& p, int gx, int gy, hipStream_t s) {
-  switch ((p.R + 15) / 16) {
-    case 1: launch_lin<1, MODE>(p, gx, gy, s); break;
-    case 2: launch_lin<2, MODE>(p, gx, gy, s); break;
-    case 3: launch_lin<3, MODE>(p, gx, gy, s); break;
-    case 4: launch_lin<4, MODE>(p, gx, gy, s); break;
-    default: return SV_ERR_UNSUPPORTED;
   }
   return SV_OK;
 }
@@ -553,8 +677,10 @@ using namespace sv;
 
 extern "C" size_t sv_lmhead_workspace(const sv_lmhead_desc* d) {
   if (validate_lmhead(d) != SV_OK) return 0;
-  const int nrows = d->mode == SV_SELECT_RESIDUAL ? d->batch : lm_rows(*d);
-  return align_up((size_t)sel_grid(*d) * nrows * sizeof(SelPart), 256);
+  const int nrows = sel_rows(*d);
+  if (d->dtype == SV_F32) return align_up((size_t)f32_grid(*d) * nrows * sizeof(SelPart), 256);
+  const RingPlan pl = ring_plan(kSelT, nrows, d->d_model, d->vocab, kMaxWG);
+  return pl.cnt_bytes + pl.part_bytes + align_up((size_t)kMaxWG * nrows * sizeof(SelPart), 256);
 }
 
 extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, const void* w,
@@ -577,7 +703,6 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
   p.R = lm_rows(*d);
   p.K = d->d_model;
   p.N = d->vocab;
-  p.k0_stride = d->d_model;
   p.batch = d->batch;
   p.kdr = d->k;
   p.drafts = drafts;
@@ -585,20 +710,27 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
   p.q_rows = q_rows;
   p.stats_in = stats;
   p.acc = acc;
-  p.sel = (SelPart*)workspace;
-  const int grid = sel_grid(*d);
-  const int nrows = d->mode == SV_SELECT_RESIDUAL ? d->batch : p.R;
+  const int nrows = sel_rows(*d);
   hipStream_t s = (hipStream_t)stream;
+  int grid;
 
   if (d->dtype == SV_BF16) {
-    p.nblk = (d->vocab + kSelNB - 1) / kSelNB;
+    const RingPlan pl = ring_plan(kSelT, nrows, d->d_model, d->vocab, live_wg());
+    p.nblk = pl.nblk;
+    p.kch = pl.kch;
+    p.cnt = (int32_t*)workspace;
+    p.part = (float*)((char*)workspace + pl.cnt_bytes);
+    p.sel = (SelPart*)((char*)workspace + pl.cnt_bytes + pl.part_bytes);
+    grid = pl.grid;
     switch (d->mode) {
-      case SV_SELECT_GREEDY: rc = dispatch_sel<GM_GREEDY>(p, p.R, grid, s); break;
-      case SV_SELECT_SAMPLE: rc = dispatch_sel<GM_SAMPLE>(p, p.R, grid, s); break;
-      default: rc = dispatch_sel<GM_RESIDUAL>(p, d->batch, grid, s); break;
+      case SV_SELECT_GREEDY: rc = dispatch_ring<kSelT, GM_GREEDY>(p, nrows, grid, s); break;
+      case SV_SELECT_SAMPLE: rc = dispatch_ring<kSelT, GM_SAMPLE>(p, nrows, grid, s); break;
+      default: rc = dispatch_ring<kSelT, GM_RESIDUAL>(p, nrows, grid, s); break;
     }
     if (rc != SV_OK) return rc;
   } else {
+    p.sel = (SelPart*)workspace;
+    grid = f32_grid(*d);
     const float* xf = (const float*)hidden;
     const float* wf = (const float*)w;
     switch (d->mode) {
@@ -623,7 +755,9 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
 
 extern "C" size_t sv_linear_workspace(const sv_linear_desc* d) {
   if (validate_linear(d) != SV_OK) return 0;
-  return lin_plan(*d).part_bytes;
+  if (d->dtype == SV_F32) return 0;
+  const RingPlan pl = ring_plan(lin_tiles(*d), d->rows, d->in_features, d->out_features, kMaxWG);
+  return pl.cnt_bytes + pl.part_bytes;
 }
 
 extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, void* y,
@@ -631,8 +765,8 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   int rc = validate_linear(d);
   if (rc != SV_OK) return rc;
   if (!x || !w || !y) return SV_ERR_ARG;
-  const LinPlan pl = lin_plan(*d);
-  if (pl.part_bytes && (!workspace || workspace_bytes < pl.part_bytes)) return SV_ERR_WORKSPACE;
+  const size_t need = sv_linear_workspace(d);
+  if (need && (!workspace || workspace_bytes < need)) return SV_ERR_WORKSPACE;
   rc = check_device();
   if (rc != SV_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
@@ -643,30 +777,24 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
                        d->epilogue == SV_EPI_ADD_F32 ? 1 : 0);
     return launch_status();
   }
+  const RingPlan pl = ring_plan(lin_tiles(*d), d->rows, d->in_features, d->out_features, live_wg());
   GemmParams p{};
   p.x = (const uint16_t*)x;
   p.w = (const uint16_t*)w;
   p.R = d->rows;
   p.K = d->in_features;
   p.N = d->out_features;
-  p.k0_stride = pl.kstride;
   p.nblk = pl.nblk;
+  p.kch = pl.kch;
   p.y = y;
-  p.part = (float*)workspace;
-  const int gx = pl.nblk;
-  if (pl.splits == 1) {
-    rc = d->epilogue == SV_EPI_STORE ? dispatch_lin<GM_STORE_BF16>(p, gx, 1, s)
-                                     : dispatch_lin<GM_ADD_F32>(p, gx, 1, s);
-    if (rc != SV_OK) return rc;
-  } else {
-    rc = dispatch_lin<GM_PARTIAL>(p, gx, pl.splits, s);
-    if (rc != SV_OK) return rc;
-    const int64_t n4 = (int64_t)d->rows * d->out_features / 4;
-    const unsigned g = (unsigned)((n4 + 255) / 256);
-    if (d->epilogue == SV_EPI_STORE)
-      hipLaunchKernelGGL(splitk_reduce_kernel<GM_STORE_BF16>, dim3(g), dim3(256), 0, s, p, pl.splits);
-    else
-      hipLaunchKernelGGL(splitk_reduce_kernel<GM_ADD_F32>, dim3(g), dim3(256), 0, s, p, pl.splits);
-  }
+  p.cnt = (int32_t*)workspace;
+  p.part = (float*)((char*)workspace + pl.cnt_bytes);
+  if (pl.T == 1)
+    rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<1, GM_STORE_BF16>(p, d->rows, pl.grid, s)
+                                     : dispatch_ring<1, GM_ADD_F32>(p, d->rows, pl.grid, s);
+  else
+    rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<2, GM_STORE_BF16>(p, d->rows, pl.grid, s)
+                                     : dispatch_ring<2, GM_ADD_F32>(p, d->rows, pl.grid, s);
+  if (rc != SV_OK) return rc;
   return launch_status();
 }

@@ -118,4 +118,57 @@ __device__ __forceinline__ void set_status(int32_t* st, int32_t bits) {
 // Gumbel noise from a uniform in [0,1): -log(-log u); u == 0 gives -inf.
 __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 
+// ---------------------------------------------------------------------------
+// HBM -> LDS streaming (direct-to-LDS DMA) and LDS-only barriers
+// ---------------------------------------------------------------------------
+// 16 bytes per lane from global memory straight into LDS at (lds_base + 16 * lane),
+// gaddr = base (wave-uniform) + off (per lane, bytes).  Issued from inline asm so the
+// compiler, which cannot tell which ring stage a DMA writes, does not stall every LDS
+// read on it; completion is waited for explicitly with wait_vm.  M0 (the LDS base)
+// is saved and restored around the instruction.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+// wait until at most N of this wave's vector memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait for all but `ahead` ring stages of NI operations each (ahead < 6)
+template <int NI>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  switch (ahead) {
+    case 0: wait_vm_n<0>(); break;
+    case 1: wait_vm_n<(NI < 63 ? NI : 63)>(); break;
+    case 2: wait_vm_n<(2 * NI < 63 ? 2 * NI : 63)>(); break;
+    case 3: wait_vm_n<(3 * NI < 63 ? 3 * NI : 63)>(); break;
+    case 4: wait_vm_n<(4 * NI < 63 ? 4 * NI : 63)>(); break;
+    default: wait_vm_n<0>(); break;
+  }
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS writes have completed,
+// but DMA into LDS still in flight is not waited for (each stage waits for its own
+// DMA explicitly), which keeps the ring's prefetches going across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace sv

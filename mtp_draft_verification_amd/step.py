@@ -67,11 +67,11 @@ class VerifyStack:
         self.h = self.a  # final norm output reuses the activation buffer
         ws = max(L.sv_verify_attn_workspace(attn_desc(ly, B, k + 1, self.cap, cfg.dtype)) for ly in cfg.layers)
         self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
-        self.lin_ws = torch.empty(max([self._lin_ws(*s) for s in self._lin_shapes()] + [256]),
+        self.lin_ws = torch.zeros(max([self._lin_ws(*s) for s in self._lin_shapes()] + [256]),
                                   dtype=torch.uint8, device=dev)
         self.lm_desc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=cfg.vocab, mode=L.SV_SELECT_GREEDY,
                                     dtype=self.dt)
-        self.lm_ws = torch.empty(max(L.sv_lmhead_workspace(self.lm_desc), 256), dtype=torch.uint8, device=dev)
+        self.lm_ws = torch.zeros(max(L.sv_lmhead_workspace(self.lm_desc), 256), dtype=torch.uint8, device=dev)
         self.stats = torch.zeros(R, L.ROW_STATS_WORDS, dtype=torch.int32, device=dev)
         self.acc = torch.zeros(B, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
         self.out_tokens = torch.zeros(B, k + 1, dtype=torch.int32, device=dev)

@@ -34,7 +34,7 @@ def run_select(h, W, drafts, B, k, mode, dev, u_tok=None, q_rows=None, stats=Non
     V, d = W.shape
     dt = L.SV_BF16 if W.dtype == torch.bfloat16 else L.SV_F32
     desc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=mode, dtype=dt)
-    ws = torch.empty(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
     if stats is None:
         stats = torch.full((B * (k + 1), L.ROW_STATS_WORDS), -7, dtype=torch.int32, device=dev)
     L.sv_lmhead_select(desc, h, W, drafts, u_tok, q_rows, stats, acc, out_tokens, ws)
