@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--ctx", type=int, default=131072)
-    ap.add_argument("--sweep", default="1", help="extra batch sizes, comma separated ('' for none)")
+    ap.add_argument("--sweep", default="1,4", help="extra batch sizes, comma separated ('' for none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for profilers: no sweep, no oracle")
@@ -65,7 +65,8 @@ def parse():
 
 
 ONLY_CALLS = ("attn_global", "attn_local", "lmhead", "lmhead_sample", "qkv_local", "qkv_global", "o_local",
-              "o_global", "gu", "down")
+              "o_global", "gu", "down", "hbm_copy")
+COPY_BYTES = 1 << 30  # hbm_copy: a plain 1 GiB device-to-device copy (counter calibration)
 
 
 def bench_only(args):
@@ -120,6 +121,11 @@ def bench_one(args, only):
         stats = torch.empty((R, L.ROW_STATS_WORDS), dtype=torch.int32, device=dev)
         call = lambda: L.sv_lmhead_select(desc, h, W, drafts, u_tok, None, stats, None, None, ws, stream)
         byts = call_bytes(cfg, [cfg.ctx] * B)["lmhead"]
+    elif only == "hbm_copy":
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        call = lambda: dst.copy_(src)
+        byts = 2 * COPY_BYTES
     else:
         R = B * nq
         loc, glo = cfg.layers[0], cfg.layers[-1]
@@ -344,7 +350,59 @@ def cpu_baseline(cfg, W, caches, tokens, lens, dev):
                        f"of the same workload at its first recorded step: {n} tokens committed in {dt:.1f} s")
 
 
+def pmc_summary(dirs):
+    """Write profiles/hbm_traffic.json from four rocprofv3 --pmc runs (csv output) of
+    `bench.py --only attn_global,lmhead,hbm_copy`: FETCH_SIZE, then WRITE_SIZE, each
+    scaled by what the same counter reads for the plain 1 GiB copy."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def per_call(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        by = defaultdict(list)  # kernel family -> per-dispatch values (KiB)
+        for r in rows:
+            n = r["Kernel_Name"]
+            fam = ("attn" if "attn_" in n or "rope_append" in n else "lmhead" if "gemm_ring" in n or "lmhead_" in n
+                   else "copy" if "copy" in n.lower() or "elementwise" in n.lower() else None)
+            if fam:
+                by[fam].append((n, float(r["Counter_Value"])))
+        return by
+
+    out = {"source_digest": source_digest(), "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch)",
+           "calls": {}}
+    scale = {}
+    vals = {}
+    for key, d in (("FETCH_SIZE", dirs[0]), ("WRITE_SIZE", dirs[1])):
+        by = per_call(d, key)
+        copies = [v for n, v in by["copy"]]
+        # the copy moves COPY_BYTES each way; take the last (steady) dispatches
+        scale[key] = (COPY_BYTES / 1024) / (sum(copies[-3:]) / len(copies[-3:]))
+        vals[key] = by
+    for call, fam, per in (("L5.attn", "attn", 3), ("lmhead", "lmhead", 2)):
+        tot = 0.0
+        for key in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = [x for n, x in vals[key][fam]]
+            ncalls = len(v) // per
+            last = v[-per * 3:] if ncalls >= 3 else v
+            kib = sum(last) / (len(last) / per)
+            out["calls"].setdefault(call, {})[key + "_KiB_per_call_raw"] = round(kib, 1)
+            tot += kib * 1024 * scale[key]
+        out["calls"][call]["bytes_per_call"] = round(tot)
+    out["copy_scale"] = {k: round(v, 4) for k, v in scale.items()}
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        pmc_summary(sys.argv[2:4])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of "
