@@ -216,6 +216,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint2 s_p[4][MT][64];      // bf16 weights, PV lane layout
   __shared__ float s_max[4][MT][16];                                 // per-wave row maxima of a tile
   __shared__ float s_sum[4][MT][16];                                 // per-wave row sums of a piece
+  __shared__ int s_flag[4];                                          // wave's rows passed the reference
   auto stage_of = [&](int u) -> unsigned char* {
     return u == 0 ? s_st0 : u == 1 ? s_st1 : u == 2 ? s_st2 : s_st3;
   };
@@ -312,11 +313,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         const int row = rb * RPI + lane / CPR;
         off_pre[jj] = (uint32_t)((lane / CPR) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
       }
-      auto issue = [&](int t, unsigned char* stage) {
+      auto issue_one = [&](int t, unsigned char* stage, int jj) {
         const int64_t t0 = a0 + (int64_t)t * TK;
         const bool partial = t0 + TK > a1;
-#pragma unroll
-        for (int jj = 0; jj < NI; ++jj) {
+        {
           const int ii = wave * NI + jj;
           const int ten = ii / (TK / RPI);
           const int rb = ii % (TK / RPI);
@@ -334,6 +334,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           dma16((const void*)(tbase + (head_row0 + brow) * D), off, lds);
         }
       };
+      auto issue = [&](int t, unsigned char* stage) {
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj) issue_one(t, stage, jj);
+      };
 
 #pragma unroll
       for (int u = 0; u < NS - 1; ++u)
@@ -348,30 +352,54 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         const int ahead = (NS - 2) < (ntiles - 1 - t) ? (NS - 2) : (ntiles - 1 - t);
         wait_stages<NI>(ahead);
         lds_barrier();  // tile t is in LDS for every wave; tile t-1 is no longer read
-        if (t + NS - 1 < ntiles) issue(t + NS - 1, stage_of((u + NS - 1) % NS));
+        // the next tile's DMA goes out spread over the score MFMAs below, so the
+        // memory pipe's issue back-pressure overlaps matrix work
+        const bool more = t + NS - 1 < ntiles;
+        unsigned char* nstage = stage_of((u + NS - 1) % NS);
 
         const unsigned char* kst = stage_of(u);
         const unsigned char* vst = kst + (KV_SAME ? 0 : TILEB);
 
         // ---- scores of this wave's 16 keys: S^T[key, row], lane holds row lr of each
-        // row tile and keys 16*wave + 4*lg + {0..3}
+        // row tile and keys 16*wave + 4*lg + {0..3}.  NCH independent accumulator
+        // chains per row tile keep the MFMA pipe busy instead of waiting on one chain.
+        constexpr int NCH = MT >= 4 ? 1 : (MT >= 2 ? 2 : 4);
+        constexpr int PER = (NI + KS - 1) / KS;  // DMA instructions per k-step
         f32x4_t sacc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         {
+          f32x4_t sch[NCH][MT];
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) sch[c][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           const int r = wave * 16 + lr;
           const unsigned char* krow = kst + r * ROWB;
           const int sw = swz(r);
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
+            if (more) {
+#pragma unroll
+              for (int q = 0; q < PER; ++q)
+                if (s * PER + q < NI) issue_one(t + NS - 1, nstage, s * PER + q);
+            }
             V16 kreg;
             kreg.u = *(const uint4*)(krow + (((4 * s + lg) ^ sw) << 4));
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sacc[mt] = mfma16x16x32(kreg.b, qreg[mt][s].b, sacc[mt]);
+            for (int mt = 0; mt < MT; ++mt) sch[s % NCH][mt] = mfma16x16x32(kreg.b, qreg[mt][s].b, sch[s % NCH][mt]);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x4_t a = sch[0][mt];
+#pragma unroll
+            for (int c = 1; c < NCH; ++c) {
+              a[0] += sch[c][mt][0]; a[1] += sch[c][mt][1]; a[2] += sch[c][mt][2]; a[3] += sch[c][mt][3];
+            }
+            sacc[mt] = a;
           }
         }
         const bool full = (t0 + TK <= a1) && (t0 + TK - 1 <= seg_min_hi) && (t0 >= seg_max_lo);
         float sc[MT][4];
+        bool over = false;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           int lo_l = -1, hi_l = TK;
@@ -391,49 +419,58 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           mx = fmaxf(mx, shfl_xor_f(mx, 16));
           mx = fmaxf(mx, shfl_xor_f(mx, 32));
           if (lg == 0) s_max[wave][mt][lr] = mx;
+          over |= mx > m_run[mt] + 8.f;
         }
-        lds_barrier();
-
-        // ---- tile maxima of all waves -> lazy reference update (same on every wave)
-        bool need = false;
-        float tmax[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          tmax[mt] = fmaxf(fmaxf(s_max[0][mt][lr], s_max[1][mt][lr]), fmaxf(s_max[2][mt][lr], s_max[3][mt][lr]));
-          need |= tmax[mt] > m_run[mt] + 8.f;
-        }
-        if (__any(need)) {
+        // The reference max of a row only moves when some key exceeds it by more than
+        // 2^8 (lazy rescaling).  Each wave computes its weights against the current
+        // reference straight away and flags whether any of its rows went over; only
+        // then do the waves combine their maxima, move the reference and redo the
+        // weights (one extra barrier, rare after the first tile of a piece).
+        const bool wover = __any(over);  // vote with every lane active
+        if (lane == 0) s_flag[wave] = wover ? 1 : 0;
+        float rsum[MT];
+        auto weights = [&]() {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const float m_new = fmaxf(m_run[mt], tmax[mt]);
-            const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[mt] - m_new);
-            l_run[mt] *= alpha;
-            m_run[mt] = m_new;
+            const float m = m_run[mt];
+            float pv[4];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              O[dt][mt][0] *= alpha; O[dt][mt][1] *= alpha;
-              O[dt][mt][2] *= alpha; O[dt][mt][3] *= alpha;
+            for (int i = 0; i < 4; ++i) pv[i] = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[mt][i] - m);
+            uint2 w2;
+            w2.x = pack_bf16x2(pv[0], pv[1]);
+            w2.y = pack_bf16x2(pv[2], pv[3]);
+            s_p[wave][mt][lane] = w2;
+            // the normaliser sums exactly the (bf16) weights the PV product uses
+            float rs = bf16_lo(w2.x) + bf16_hi(w2.x) + bf16_lo(w2.y) + bf16_hi(w2.y);
+            rs += shfl_xor_f(rs, 16);
+            rs += shfl_xor_f(rs, 32);
+            rsum[mt] = rs;
+          }
+        };
+        weights();
+        lds_barrier();  // weights, maxima and flags of every wave visible
+
+        if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {  // same decision on every wave
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const float tmax = fmaxf(fmaxf(s_max[0][mt][lr], s_max[1][mt][lr]), fmaxf(s_max[2][mt][lr], s_max[3][mt][lr]));
+            if (tmax > m_run[mt] + 8.f) {
+              const float m_new = tmax;
+              const float alpha = m_run[mt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[mt] - m_new);
+              l_run[mt] *= alpha;
+              m_run[mt] = m_new;
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) {
+                O[dt][mt][0] *= alpha; O[dt][mt][1] *= alpha;
+                O[dt][mt][2] *= alpha; O[dt][mt][3] *= alpha;
+              }
             }
           }
+          weights();
+          lds_barrier();  // the redone weights visible
         }
-        // ---- weights of this wave's keys, bf16, to LDS in the PV operand layout
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const float m = m_run[mt];
-          float pv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[i] = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[mt][i] - m);
-          uint2 w2;
-          w2.x = pack_bf16x2(pv[0], pv[1]);
-          w2.y = pack_bf16x2(pv[2], pv[3]);
-          s_p[wave][mt][lane] = w2;
-          // the normaliser sums exactly the (bf16) weights the PV product uses
-          float rs = bf16_lo(w2.x) + bf16_hi(w2.x) + bf16_lo(w2.y) + bf16_hi(w2.y);
-          rs += shfl_xor_f(rs, 16);
-          rs += shfl_xor_f(rs, 32);
-          l_run[mt] += rs;
-        }
-        lds_barrier();
+        for (int mt = 0; mt < MT; ++mt) l_run[mt] += rsum[mt];
 
         // ---- O^T += V^T P^T over the tile's two 32-key halves.  Lane i of a 16-lane
         // group feeds row 32*ks + 16*h + 4*lg + i/4, dims 4*(i%4)..+3 of the tile; the

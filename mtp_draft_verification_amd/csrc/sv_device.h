@@ -129,7 +129,15 @@ __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+__device__ __forceinline__ void dma16(const void* base_in, uint32_t off, uint32_t lds_base) {
+  // the base is wave-uniform by construction; say so, so that it lives in SGPRs
+  const uint64_t bu = (uint64_t)(uintptr_t)base_in;
+  // (readfirstlane yields an int: widen each half as unsigned, never sign-extend)
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu);
+  const uint64_t b64 = (hi << 32) | lo;
+  const void* base = (const void*)(uintptr_t)b64;
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -149,15 +157,18 @@ __device__ __forceinline__ void wait_vm_n() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// wait for all but `ahead` ring stages of NI operations each (ahead < 6)
+// wait for all but `ahead` ring stages of NI operations each (ahead <= 6; callers
+// guarantee ahead * NI <= 63, larger `ahead` waits for everything)
 template <int NI>
 __device__ __forceinline__ void wait_stages(int ahead) {
   switch (ahead) {
     case 0: wait_vm_n<0>(); break;
-    case 1: wait_vm_n<(NI < 63 ? NI : 63)>(); break;
-    case 2: wait_vm_n<(2 * NI < 63 ? 2 * NI : 63)>(); break;
-    case 3: wait_vm_n<(3 * NI < 63 ? 3 * NI : 63)>(); break;
-    case 4: wait_vm_n<(4 * NI < 63 ? 4 * NI : 63)>(); break;
+    case 1: wait_vm_n<(NI < 63 ? NI : 0)>(); break;
+    case 2: wait_vm_n<(2 * NI < 63 ? 2 * NI : 0)>(); break;
+    case 3: wait_vm_n<(3 * NI < 63 ? 3 * NI : 0)>(); break;
+    case 4: wait_vm_n<(4 * NI < 63 ? 4 * NI : 0)>(); break;
+    case 5: wait_vm_n<(5 * NI < 63 ? 5 * NI : 0)>(); break;
+    case 6: wait_vm_n<(6 * NI < 63 ? 6 * NI : 0)>(); break;
     default: wait_vm_n<0>(); break;
   }
 }
