@@ -134,15 +134,16 @@ def bench_one(args, only):
                      "qkv_global": (cfg.d_model, nout(glo), L.SV_EPI_STORE),
                      "o_local": (loc.n_heads_q * loc.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
                      "o_global": (glo.n_heads_q * glo.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
-                     "gu": (cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_STORE),
+                     "gu": (cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_GEGLU),
                      "down": (cfg.d_ff, cfg.d_model, L.SV_EPI_ADD_F32)}[only]
         x = inputs.normal((R, K), 1.0, 0, "x", dev)
         W = inputs.normal((N, K), K ** -0.5, 0, "W", dev)
-        y = torch.zeros((R, N), dtype=torch.float32 if epi == L.SV_EPI_ADD_F32 else torch.bfloat16, device=dev)
+        y = torch.zeros((R, N // 2 if epi == L.SV_EPI_GEGLU else N),
+                        dtype=torch.float32 if epi == L.SV_EPI_ADD_F32 else torch.bfloat16, device=dev)
         desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi)
         ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
         call = lambda: L.sv_linear(desc, x, W, y, ws, stream)
-        byts = 2 * (N * K + R * K) + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 2)
+        byts = 2 * (N * K + R * K) + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 1 if epi == L.SV_EPI_GEGLU else 2)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -191,7 +192,7 @@ def call_bytes(cfg, lens) -> dict:
         out[f"L{i}.qkv"] = nout * d * e + R * d * e + R * nout * e
         out[f"L{i}.o"] = d * H * D * e + R * H * D * e + R * d * 4 * 2
         if cfg.d_ff:
-            out[f"L{i}.gu"] = 2 * cfg.d_ff * d * e + R * d * e + R * 2 * cfg.d_ff * e
+            out[f"L{i}.gu"] = 2 * cfg.d_ff * d * e + R * d * e + R * cfg.d_ff * e  # fused GeGLU output
             out[f"L{i}.down"] = d * cfg.d_ff * e + R * cfg.d_ff * e + R * d * 4 * 2
     return out
 

@@ -251,7 +251,13 @@ int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float
 
 typedef enum {
   SV_EPI_STORE = 0,      /* y = x W^T stored in the descriptor dtype */
-  SV_EPI_ADD_F32 = 1     /* y (fp32) += x W^T: a residual add */
+  SV_EPI_ADD_F32 = 1,    /* y (fp32) += x W^T: a residual add */
+  SV_EPI_GEGLU = 2       /* bf16 only: the GeGLU gate fused into the gate/up projection.
+                            W holds the gate and up rows interleaved by 16: rows
+                            [32j, 32j+16) are gate features 16j..16j+15 and rows
+                            [32j+16, 32j+32) the up features of the same indices;
+                            y [R, N/2] bf16 gets gelu_tanh(g) * u with g and u rounded
+                            to bf16 first (the values sv_geglu would read).  N % 128 == 0. */
 } sv_epilogue;
 
 typedef struct {

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE = 0, -1, -2, -3, -4, -5
 SV_F32, SV_BF16 = 0, 1
 SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL = 0, 1, 2
-SV_EPI_STORE, SV_EPI_ADD_F32 = 0, 1
+SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU = 0, 1, 2
 SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn",

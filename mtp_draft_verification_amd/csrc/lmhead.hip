@@ -17,7 +17,7 @@
 
 namespace sv {
 
-enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4 };
+enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_GEGLU = 5 };
 
 struct SelPart {   // per (workgroup, row) partial of the select epilogue
   float t1v, t2v;  // top-2 logits (RESIDUAL: residual-draw scores)
@@ -381,6 +381,17 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
         const float z[4] = {acc[t][mt][0], acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]};
         if constexpr (SELECT) {
           select_push4<MODE>(st[mt], ctx[mt], z, v0);
+        } else if constexpr (MODE == GM_GEGLU) {
+          // tile 0 holds the gate, tile 1 the up projection of the same 16 features
+          // (weights interleaved by 16 rows); both pass through bf16 as stored values
+          if (t == 1 && r < nx) {
+            float f[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              f[e] = gelu_tanh(round_bf16(acc[0][mt][e])) * round_bf16(acc[1][mt][e]);
+            const int c0 = row0 / 2 + lg * 4;
+            *(uint2*)((uint16_t*)p.y + (int64_t)r * (p.N / 2) + c0) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+          }
         } else if constexpr (MODE == GM_STORE_BF16) {
           if (r < nx)
             *(uint2*)((uint16_t*)p.y + (int64_t)r * p.N + v0) = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
@@ -589,6 +600,7 @@ static constexpr int kSelT = 4;      // W tiles per wave in the LM head
 // fewer workgroups share a block, so the ordered sum of split partials is short),
 // two otherwise (half the x re-reads per weight byte)
 static int lin_tiles(const sv_linear_desc& d) {
+  if (d.epilogue == SV_EPI_GEGLU) return 2;  // a wave's two tiles pair gate and up rows
   return (int64_t)d.in_features * d.out_features < ((int64_t)24 << 20) ? 1 : 2;
 }
 
@@ -657,8 +669,9 @@ static int dispatch_ring(const GemmParams& p, int nx, int grid, hipStream_t s) {
 static int validate_linear(const sv_linear_desc* d) {
   if (!d) return SV_ERR_ARG;
   if (d->rows <= 0 || d->in_features <= 0 || d->out_features <= 0) return SV_ERR_ARG;
-  if (d->epilogue != SV_EPI_STORE && d->epilogue != SV_EPI_ADD_F32) return SV_ERR_ARG;
+  if (d->epilogue != SV_EPI_STORE && d->epilogue != SV_EPI_ADD_F32 && d->epilogue != SV_EPI_GEGLU) return SV_ERR_ARG;
   if (d->out_features % 64) return SV_ERR_ARG;
+  if (d->epilogue == SV_EPI_GEGLU && (d->dtype != SV_BF16 || d->out_features % 128)) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
     if (d->in_features % 32) return SV_ERR_ARG;
     if (d->rows > 64) return SV_ERR_UNSUPPORTED;
@@ -789,7 +802,9 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   p.y = y;
   p.cnt = (int32_t*)workspace;
   p.part = (float*)((char*)workspace + pl.cnt_bytes);
-  if (pl.T == 1)
+  if (d->epilogue == SV_EPI_GEGLU)
+    rc = dispatch_ring<2, GM_GEGLU>(p, d->rows, pl.grid, s);
+  else if (pl.T == 1)
     rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<1, GM_STORE_BF16>(p, d->rows, pl.grid, s)
                                      : dispatch_ring<1, GM_ADD_F32>(p, d->rows, pl.grid, s);
   else

@@ -7,6 +7,8 @@
 
 namespace sv {
 
+// One workgroup per row.  Rows of d_model % 4 == 0 move as 4-element vectors
+// (8-byte bf16 / 16-byte fp32 loads, 16-byte fp32 stores); others element-wise.
 __global__ __launch_bounds__(256) void embed_kernel(int d_model, int vocab, int bf16, const int32_t* tokens,
                                                     const void* table, float scale, float* x,
                                                     int32_t* dev_status) {
@@ -15,6 +17,22 @@ __global__ __launch_bounds__(256) void embed_kernel(int d_model, int vocab, int 
   float* dst = x + (int64_t)r * d_model;
   const bool ok = tok >= 0 && tok < vocab;
   if (!ok && threadIdx.x == 0) set_status(dev_status, SV_DEV_BAD_TOKEN);
+  if ((d_model & 3) == 0 && (((uintptr_t)table | (uintptr_t)x) & 15) == 0) {
+    const int n4 = d_model / 4;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+      f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (ok) {
+        if (bf16) {
+          const uint2 w = *(const uint2*)((const uint16_t*)table + (int64_t)tok * d_model + 4 * i);
+          v = f32x4_t{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        } else {
+          v = *(const f32x4_t*)((const float*)table + (int64_t)tok * d_model + 4 * i);
+        }
+      }
+      *(f32x4_t*)(dst + 4 * i) = f32x4_t{scale * v[0], scale * v[1], scale * v[2], scale * v[3]};
+    }
+    return;
+  }
   for (int i = threadIdx.x; i < d_model; i += 256) {
     float v = 0.f;
     if (ok) {
@@ -25,33 +43,65 @@ __global__ __launch_bounds__(256) void embed_kernel(int d_model, int vocab, int 
   }
 }
 
+// One workgroup per row: the row is read once into registers (4-element vectors,
+// up to kNormVec per thread), squared and summed with wavefront shuffles and one
+// exchange between the four waves, then scaled and stored.
+constexpr int kNormVec = 8;  // rows up to 256 * 4 * 8 = 8192 elements take the register path
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int dim, float eps, const float* x, const float* gain,
                                                       void* y, int bf16) {
-  __shared__ float s_red[256];
+  __shared__ float s_red[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   const float* xr = x + (int64_t)r * dim;
+  const bool vec = (dim & 3) == 0 && dim <= 256 * 4 * kNormVec &&
+                   (((uintptr_t)x | (uintptr_t)y | (uintptr_t)gain) & 15) == 0;
+  f32x4_t v[kNormVec];
   float ss = 0.f;
-  for (int i = tid; i < dim; i += 256) ss = fmaf(xr[i], xr[i], ss);
-  s_red[tid] = ss;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) s_red[tid] += s_red[tid + s];
-    __syncthreads();
+  if (vec) {
+    const int n4 = dim / 4;
+#pragma unroll
+    for (int k = 0; k < kNormVec; ++k) {
+      const int i = tid + 256 * k;
+      v[k] = i < n4 ? *(const f32x4_t*)(xr + 4 * i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < kNormVec; ++k)
+      ss = fmaf(v[k][0], v[k][0], fmaf(v[k][1], v[k][1], fmaf(v[k][2], v[k][2], fmaf(v[k][3], v[k][3], ss))));
+  } else {
+    for (int i = tid; i < dim; i += 256) ss = fmaf(xr[i], xr[i], ss);
   }
-  const float inv = 1.f / sqrtf(s_red[0] / (float)dim + eps);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) ss += shfl_xor_f(ss, m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  const float inv = 1.f / sqrtf(tot / (float)dim + eps);
+  if (vec) {
+    const int n4 = dim / 4;
+#pragma unroll
+    for (int k = 0; k < kNormVec; ++k) {
+      const int i = tid + 256 * k;
+      if (i >= n4) break;
+      f32x4_t o = f32x4_t{v[k][0] * inv, v[k][1] * inv, v[k][2] * inv, v[k][3] * inv};
+      if (gain) {
+        const f32x4_t g = *(const f32x4_t*)(gain + 4 * i);
+        o = f32x4_t{o[0] * g[0], o[1] * g[1], o[2] * g[2], o[3] * g[3]};
+      }
+      if (bf16)
+        *(uint2*)((uint16_t*)y + (int64_t)r * dim + 4 * i) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      else
+        *(f32x4_t*)((float*)y + (int64_t)r * dim + 4 * i) = o;
+    }
+    return;
+  }
   for (int i = tid; i < dim; i += 256) {
-    float v = xr[i] * inv;
-    if (gain) v *= gain[i];
-    if (bf16) ((uint16_t*)y)[(int64_t)r * dim + i] = (uint16_t)f32_to_bf16_bits(v);
-    else ((float*)y)[(int64_t)r * dim + i] = v;
+    float o = xr[i] * inv;
+    if (gain) o *= gain[i];
+    if (bf16) ((uint16_t*)y)[(int64_t)r * dim + i] = (uint16_t)f32_to_bf16_bits(o);
+    else ((float*)y)[(int64_t)r * dim + i] = o;
   }
 }
 
-// gelu, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float c = 0.7978845608028654f;
-  return 0.5f * x * (1.f + tanhf(c * (x + 0.044715f * x * x * x)));
-}
 
 __global__ __launch_bounds__(256) void geglu_kernel(int rows, int dff, int bf16, const void* gu, void* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

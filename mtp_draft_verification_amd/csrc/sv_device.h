@@ -115,6 +115,12 @@ __device__ __forceinline__ void set_status(int32_t* st, int32_t bits) {
   if (st) atomicOr(st, bits);
 }
 
+// gelu, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float c = 0.7978845608028654f;
+  return 0.5f * x * (1.f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+
 // Gumbel noise from a uniform in [0,1): -log(-log u); u == 0 gives -inf.
 __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 

@@ -8,8 +8,10 @@ then accept_longest_prefix.  Here that forward is, per layer,
     qkv = a Wqkv^T                 sv_linear       (q, k, v in one projection)
     o = attn(q, k, v; cache)       sv_verify_attn  (appends the k+1 new rows)
     x += o Wo^T                    sv_linear (SV_EPI_ADD_F32)
-    m = rmsnorm(x); gu = m Wgu^T   sv_rmsnorm, sv_linear
-    f = gelu_tanh(g) * u           sv_geglu
+    m = rmsnorm(x)                 sv_rmsnorm
+    f = gelu_tanh(m Wg^T) * (m Wu^T)   sv_linear (SV_EPI_GEGLU: one launch, gate/up
+                                   rows interleaved by 16; sv_linear + sv_geglu where
+                                   that layout does not apply)
     x += f Wd^T                    sv_linear (SV_EPI_ADD_F32)
 
 then h = rmsnorm(x), sv_lmhead_select over the tied embedding and sv_accept.
@@ -37,6 +39,15 @@ def attn_desc(layer, batch: int, n_q: int, cap: int, dtype: str, append: bool = 
                       kv_row_stride=int(kv_row_stride))
 
 
+def interleave_gate_up(wgu: torch.Tensor) -> torch.Tensor:
+    """[2*d_ff, d] (gate rows, then up rows) -> the same rows interleaved by 16 (gate
+    16j..16j+15, up 16j..16j+15, ...), the layout SV_EPI_GEGLU reads.  A one-time
+    copy of the weights (layout only)."""
+    two_dff, d = wgu.shape
+    dff = two_dff // 2
+    return wgu.view(2, dff // 16, 16, d).permute(1, 0, 2, 3).contiguous().view(two_dff, d)
+
+
 class VerifyStack:
     """Device-resident state of a stack: weights, caches, committed lengths, buffers."""
 
@@ -54,6 +65,10 @@ class VerifyStack:
         B, k, d = cfg.batch, cfg.k, cfg.d_model
         self.R = R = B * (k + 1)
         self.cap = caches[0]["k"].shape[2]
+        # fused GeGLU projection where the layout applies (bf16, 2*d_ff a multiple of 128)
+        self.fused_geglu = bool(self.bf16 and cfg.d_ff and (2 * cfg.d_ff) % 128 == 0)
+        self.wgu_il = ([interleave_gate_up(lw["wgu"]) for lw in weights["layers"]]
+                       if self.fused_geglu else None)
         dev = self.dev
         z = lambda *s, dtype=tdt: torch.zeros(*s, dtype=dtype, device=dev)
         self.x = z(R, d, dtype=torch.float32)
@@ -62,7 +77,7 @@ class VerifyStack:
                    for ly in cfg.layers)
         self.qkv = z(R, nout)
         self.o = z(R, max(ly.n_heads_q * ly.head_dim for ly in cfg.layers))
-        self.gu = z(R, 2 * cfg.d_ff) if cfg.d_ff else None
+        self.gu = z(R, 2 * cfg.d_ff) if cfg.d_ff and not self.fused_geglu else None
         self.f = z(R, cfg.d_ff) if cfg.d_ff else None
         self.h = self.a  # final norm output reuses the activation buffer
         ws = max(L.sv_verify_attn_workspace(attn_desc(ly, B, k + 1, self.cap, cfg.dtype)) for ly in cfg.layers)
@@ -108,7 +123,7 @@ class VerifyStack:
             yield R, cfg.d_model, self._nout(ly), L.SV_EPI_STORE
             yield R, ly.n_heads_q * ly.head_dim, cfg.d_model, L.SV_EPI_ADD_F32
             if cfg.d_ff:
-                yield R, cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_STORE
+                yield R, cfg.d_model, 2 * cfg.d_ff, (L.SV_EPI_GEGLU if self.fused_geglu else L.SV_EPI_STORE)
                 yield R, cfg.d_ff, cfg.d_model, L.SV_EPI_ADD_F32
 
     def _lin_ws(self, R, K, N, epi) -> int:
@@ -131,8 +146,8 @@ class VerifyStack:
     def forward(self, tokens: torch.Tensor, stream=None) -> torch.Tensor:
         """Verify forward of tokens [B, k+1] int32 (device); appends the k+1 new
         rows of every layer's cache; returns the final hidden states [R, d].
-        Call names for timing: embed, L{i}.qkv, L{i}.attn, L{i}.o, L{i}.gu,
-        L{i}.geglu, L{i}.down, final_norm."""
+        Call names for timing: embed, L{i}.qkv, L{i}.attn, L{i}.o, L{i}.gu (with the
+        GeGLU gate when fused), L{i}.geglu (otherwise), L{i}.down, final_norm."""
         cfg = self.cfg
         d = cfg.d_model
         t = self._ev("embed", stream)
@@ -164,11 +179,15 @@ class VerifyStack:
             if cfg.d_ff:
                 m = self._norm(self.x, self.a, stream)
                 t = self._ev(f"L{i}.gu", stream)
-                self._linear(m, lw["wgu"], self.gu, L.SV_EPI_STORE, stream)
-                self._end(t)
-                t = self._ev(f"L{i}.geglu", stream)
-                L.sv_geglu(self.R, cfg.d_ff, self.dt, self.gu, self.f, stream)
-                self._end(t)
+                if self.fused_geglu:
+                    self._linear(m, self.wgu_il[i], self.f, L.SV_EPI_GEGLU, stream)
+                    self._end(t)
+                else:
+                    self._linear(m, lw["wgu"], self.gu, L.SV_EPI_STORE, stream)
+                    self._end(t)
+                    t = self._ev(f"L{i}.geglu", stream)
+                    L.sv_geglu(self.R, cfg.d_ff, self.dt, self.gu, self.f, stream)
+                    self._end(t)
                 t = self._ev(f"L{i}.down", stream)
                 self._linear(self.f, lw["wd"], self.x, L.SV_EPI_ADD_F32, stream)
                 self._end(t)

@@ -83,3 +83,38 @@ def test_shared_workspace_across_shapes():
         linear_case(r, k, n, e, sd, ws=ws)
     # the counter region (the first 256 KiB) is back to zero after the calls
     assert int(torch.count_nonzero(ws[:1 << 18]).item()) == 0
+
+
+@gpu
+@pytest.mark.parametrize("R,K,dff", [(40, 3840, 15360), (20, 256, 512), (7, 96, 64)])
+def test_fused_geglu(R, K, dff):
+    """SV_EPI_GEGLU against the oracle's gelu_tanh(bf16(x Wg)) * bf16(x Wu).  Bound:
+    the fp32 sums are within gamma_K sum|x w| of the exact ones, bf16 rounding of g and
+    u adds at most 2^-8 relative each, gelu_tanh has slope below 1.13, and the stored
+    f adds 2^-8 relative."""
+    dev = need_gpu()
+    from mtp_draft_verification_amd.step import interleave_gate_up
+    say(f"[linear geglu] R={R} K={K} d_ff={dff}")
+    x = inputs.normal((R, K), 1.0, 11, "x", dev)
+    Wgu = inputs.normal((2 * dff, K), K ** -0.5, 11, "Wgu", dev)
+    desc = L.LinearDesc(rows=R, in_features=K, out_features=2 * dff, dtype=L.SV_BF16, epilogue=L.SV_EPI_GEGLU)
+    ws = torch.zeros(L.sv_linear_workspace(desc), dtype=torch.uint8, device=dev)
+    f = torch.full((R, dff), float("nan"), dtype=torch.bfloat16, device=dev)
+    L.sv_linear(desc, x, interleave_gate_up(Wgu), f, ws)
+    torch.cuda.synchronize()
+    xh, wh = host(x), inputs.bf16_bits(Wgu)
+    GU = oracle.linear(xh, wh)
+    mag = oracle.linear(np.abs(xh), np.abs(host(Wgu)))
+    e_acc = K * 2.0 ** -24 * mag
+    G, U = GU[:, :dff], GU[:, dff:]
+    g, u = oracle.bf16_round(G), oracle.bf16_round(U)
+    ref = oracle.bf16_round(oracle.geglu(g, u))
+    dg = e_acc[:, :dff] + 2.0 ** -8 * np.abs(G) + 1e-30
+    du = e_acc[:, dff:] + 2.0 ** -8 * np.abs(U) + 1e-30
+    gel = np.abs(oracle.geglu(g, np.ones_like(g)))
+    bound = 1.13 * dg * (np.abs(u) + du) + gel * du + 2.0 ** -7 * np.abs(ref) + 1e-30
+    got = host(f)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
+    say(f"[linear geglu] ok, max err/bound {float((err / bound).max()):.3f}")
