@@ -82,6 +82,13 @@ def test_greedy_small_bf16():
 
 
 @gpu
+def test_greedy_more_groups_than_workgroups():
+    """1028 blocks of 256 entries: whole groups of four blocks, more groups than
+    resident workgroups (one workgroup takes two), and a ragged last 64-dim chunk."""
+    greedy_case(2, 2, 96, 263168, 6, rows=[0, 2, 5])
+
+
+@gpu
 def test_greedy_fp32_tiny():
     greedy_case(1, 3, 128, 1024, 0, dtype="f32")
 
