@@ -142,7 +142,14 @@ def bench_one(args, only):
                         dtype=torch.float32 if epi == L.SV_EPI_ADD_F32 else torch.bfloat16, device=dev)
         desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi)
         ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
-        call = lambda: L.sv_linear(desc, x, W, y, ws, stream)
+        # rotate over copies of W (1 GiB in all) so that, as inside the step, no call
+        # finds its weights in the last-level cache
+        Ws = [W] + [W.clone() for _ in range(max(0, -(-(1 << 30) // (2 * N * K)) - 1))]
+        turn = [0]
+
+        def call():
+            turn[0] += 1
+            L.sv_linear(desc, x, Ws[turn[0] % len(Ws)], y, ws, stream)
         byts = 2 * (N * K + R * K) + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 1 if epi == L.SV_EPI_GEGLU else 2)
     for _ in range(3):
         call()

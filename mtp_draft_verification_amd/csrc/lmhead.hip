@@ -617,6 +617,19 @@ static RingPlan ring_plan(int T, int nx, int K, int N, int max_wg) {
   pl.kch = (K + 63) / 64;
   const int64_t tot = (int64_t)pl.nblk * pl.kch;
   pl.grid = (int)(tot < max_wg ? tot : max_wg);
+  // Prefer a grid in which every workgroup takes one equal slice of one block
+  // (nblk * S workgroups, S dividing the chunk count) or whole blocks (a divisor
+  // of nblk): a slice boundary never falls inside a workgroup's range, so no
+  // workgroup stops its stream midway to publish a partial sum.
+  int aligned = 0;
+  if (pl.nblk <= max_wg) {
+    for (int S = max_wg / pl.nblk; S >= 1 && !aligned; --S)
+      if (pl.kch % S == 0) aligned = pl.nblk * S;
+  } else {
+    for (int g = max_wg; g > max_wg / 2 && !aligned; --g)
+      if (pl.nblk % g == 0) aligned = g;
+  }
+  if (aligned * 8 >= max_wg * 7) pl.grid = aligned;
   pl.cnt_bytes = (size_t)kCntWords * sizeof(int32_t);
   pl.part_bytes = align_up((size_t)kMaxWG * 2 * nx * 64 * T * sizeof(float), 256);
   return pl;
