@@ -17,6 +17,8 @@
 #include "sv_device.h"
 #include "sv_host.h"
 
+#include <type_traits>
+
 namespace sv {
 
 struct AttnParams {
@@ -255,33 +257,32 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       const int ntiles = (int)((a1 - a0 + TK - 1) / TK);
 
       // ---- queries of this (sequence, kv head), full head dim, as MFMA B operands
-      V16 qreg[MT][KS];
-      int64_t row_hi[MT], row_lo[MT];
+      // The 4 x MT (key tile, row tile) pairs of a tile's scores go to the waves in
+      // row-tile-major order, MT consecutive pairs per wave: a wave scores at most two
+      // row tiles (one unless MT == 3), so it holds only those rows of the queries.
+      constexpr int NQ = MT == 3 ? 2 : 1;
+      const int mq0 = (wave * MT) >> 2;  // the wave's first row tile
+      V16 qreg[NQ][KS];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int r = mt * 16 + lr;
-        if (r < M) {
+      for (int lt = 0; lt < NQ; ++lt) {
+        const int r = (mq0 + lt) * 16 + lr;
+        if (mq0 + lt < MT && r < M) {
           const int j = r / G, hg = r - (r / G) * G;
           const uint16_t* src = qrot + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + lg * 8;
 #pragma unroll
-          for (int s = 0; s < KS; ++s) qreg[mt][s].u = *(const uint4*)(src + s * 32);
-          const int64_t pos = L + p.qoff + j;
-          row_hi[mt] = pos < last ? pos : last;
-          row_lo[mt] = p.window > 0 ? pos - p.window + 1 : 0;
+          for (int s = 0; s < KS; ++s) qreg[lt][s].u = *(const uint4*)(src + s * 32);
         } else {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) qreg[mt][s].u = make_uint4(0, 0, 0, 0);
-          row_hi[mt] = INT64_MAX;  // padded rows: no causal limit (results discarded)
-          row_lo[mt] = INT64_MIN;
+          for (int s = 0; s < KS; ++s) qreg[lt][s].u = make_uint4(0, 0, 0, 0);
         }
       }
       // consume the query loads here (the compiler then waits for them once, not
       // inside the tile loop where the ring's DMA is in flight), and start from an
       // idle memory pipe and a free ring
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int lt = 0; lt < NQ; ++lt)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qreg[mt][s].b));
+        for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qreg[lt][s].b));
       wait_vm_n<0>();
       __syncthreads();
 
@@ -352,74 +353,142 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         const int ahead = (NS - 2) < (ntiles - 1 - t) ? (NS - 2) : (ntiles - 1 - t);
         wait_stages<NI>(ahead);
         lds_barrier();  // tile t is in LDS for every wave; tile t-1 is no longer read
-        // the next tile's DMA goes out spread over the score MFMAs below, so the
-        // memory pipe's issue back-pressure overlaps matrix work
+        // The next tile's DMA goes out spread over the score MFMAs below, so the
+        // memory pipe's issue back-pressure overlaps matrix work.  A full next tile
+        // takes a branch-free path (wave-uniform row base, per-lane offsets fixed); a
+        // partial one (the last of a piece) is issued up front with clamped rows.
         const bool more = t + NS - 1 < ntiles;
+        const int64_t tn0 = a0 + (int64_t)(t + NS - 1) * TK;
+        const bool nfull = more && tn0 + TK <= a1;
         unsigned char* nstage = stage_of((u + NS - 1) % NS);
+        if (more && !nfull) issue(t + NS - 1, nstage);
 
         const unsigned char* kst = stage_of(u);
         const unsigned char* vst = kst + (KV_SAME ? 0 : TILEB);
 
-        // ---- scores of this wave's 16 keys: S^T[key, row], lane holds row lr of each
-        // row tile and keys 16*wave + 4*lg + {0..3}.  NCH independent accumulator
-        // chains per row tile keep the MFMA pipe busy instead of waiting on one chain.
-        constexpr int NCH = MT >= 4 ? 1 : (MT >= 2 ? 2 : 4);
+        // ---- scores of the wave's pairs: pair j = (key tile kt, row tile mt) holds
+        // S^T[key, row] with row mt*16 + lr and keys 16*kt + 4*lg + {0..3}.  The key
+        // operands are read KPF k-steps ahead of their MFMAs; with a single pair, NCH
+        // chains over alternate k-steps keep the MFMA pipe busy.
+        constexpr int NCH = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
         constexpr int PER = (NI + KS - 1) / KS;  // DMA instructions per k-step
+        constexpr int KPF = KS < 4 ? KS : 4;
+        int pkt[MT], pmt[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          pkt[j] = (wave * MT + j) & 3;
+          pmt[j] = (wave * MT + j) >> 2;
+        }
         f32x4_t sacc[MT];
-        {
+        auto scores = [&](auto dma) {
+          constexpr bool DMA = decltype(dma)::value;
           f32x4_t sch[NCH][MT];
 #pragma unroll
           for (int c = 0; c < NCH; ++c)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sch[c][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const int r = wave * 16 + lr;
-          const unsigned char* krow = kst + r * ROWB;
-          const int sw = swz(r);
+            for (int j = 0; j < MT; ++j) sch[c][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const unsigned char* krow[MT];
+          int sw[MT];
+#pragma unroll
+          for (int j = 0; j < MT; ++j) {
+            const int r = pkt[j] * 16 + lr;
+            krow[j] = kst + r * ROWB;
+            sw[j] = swz(r);
+          }
+          V16 kq[KPF][MT];
+#pragma unroll
+          for (int s = 0; s < KPF; ++s)
+#pragma unroll
+            for (int j = 0; j < MT; ++j) kq[s][j].u = *(const uint4*)(krow[j] + (((4 * s + lg) ^ sw[j]) << 4));
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            if (more) {
+            if constexpr (DMA) {
 #pragma unroll
-              for (int q = 0; q < PER; ++q)
-                if (s * PER + q < NI) issue_one(t + NS - 1, nstage, s * PER + q);
+              for (int q = 0; q < PER; ++q) {
+                const int jj = s * PER + q;
+                if (jj < NI) {
+                  const int ii = wave * NI + jj;
+                  const int ten = ii / (TK / RPI);
+                  const int rb = ii % (TK / RPI);
+                  const uint16_t* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
+                  dma16<false>((const void*)(tbase + (head_row0 + tn0 + rb * RPI) * D), off_pre[jj],
+                               lds_addr(nstage + ten * TILEB + rb * RPI * ROWB));
+                }
+              }
             }
-            V16 kreg;
-            kreg.u = *(const uint4*)(krow + (((4 * s + lg) ^ sw) << 4));
+            V16 kreg[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sch[s % NCH][mt] = mfma16x16x32(kreg.b, qreg[mt][s].b, sch[s % NCH][mt]);
+            for (int j = 0; j < MT; ++j) {
+              kreg[j] = kq[s % KPF][j];
+              if (s + KPF < KS) kq[s % KPF][j].u = *(const uint4*)(krow[j] + (((4 * (s + KPF) + lg) ^ sw[j]) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+              const bf16x8_t qv = (NQ == 1 || pmt[j] == mq0) ? qreg[0][s].b : qreg[NQ - 1][s].b;
+              sch[s % NCH][j] = mfma16x16x32(kreg[j].b, qv, sch[s % NCH][j]);
+            }
+          }
+          {
+            // keep KPF k-steps of key reads ahead of the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, KPF * MT, 0);
+#pragma unroll
+            for (int s = 0; s < KS - KPF; ++s) {
+              __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, KPF * MT, 0);
           }
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            f32x4_t a = sch[0][mt];
+          for (int j = 0; j < MT; ++j) {
+            f32x4_t a = sch[0][j];
 #pragma unroll
             for (int c = 1; c < NCH; ++c) {
-              a[0] += sch[c][mt][0]; a[1] += sch[c][mt][1]; a[2] += sch[c][mt][2]; a[3] += sch[c][mt][3];
+              a[0] += sch[c][j][0]; a[1] += sch[c][j][1]; a[2] += sch[c][j][2]; a[3] += sch[c][j][3];
             }
-            sacc[mt] = a;
+            sacc[j] = a;
           }
-        }
+        };
+        if (nfull) scores(std::true_type{});
+        else scores(std::false_type{});
+
+        // the running max of row tile mt (a uniform index) without indexing registers
+        auto pick = [&](const float (&v)[MT], int mt) {
+          float x = v[0];
+#pragma unroll
+          for (int m = 1; m < MT; ++m) x = mt == m ? v[m] : x;
+          return x;
+        };
         const bool full = (t0 + TK <= a1) && (t0 + TK - 1 <= seg_min_hi) && (t0 >= seg_max_lo);
         float sc[MT][4];
         bool over = false;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int j = 0; j < MT; ++j) {
           int lo_l = -1, hi_l = TK;
           if (!full) {
-            const int64_t hi = (row_hi[mt] < a1 - 1 ? row_hi[mt] : a1 - 1) - t0;
-            const int64_t lo2 = row_lo[mt] - t0;
+            // causal and window limits of row pmt[j]*16 + lr (padded rows: none)
+            const int r = pmt[j] * 16 + lr;
+            int64_t rhi = INT64_MAX, rlo = INT64_MIN;
+            if (r < M) {
+              const int64_t pos = L + p.qoff + r / G;
+              rhi = pos < last ? pos : last;
+              rlo = p.window > 0 ? pos - p.window + 1 : 0;
+            }
+            const int64_t hi = (rhi < a1 - 1 ? rhi : a1 - 1) - t0;
+            const int64_t lo2 = rlo - t0;
             hi_l = hi < -1 ? -1 : (hi > TK ? TK : (int)hi);
             lo_l = lo2 < -1 ? -1 : (lo2 > TK ? TK : (int)lo2);
           }
           float mx = kNegInf;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kl = wave * 16 + lg * 4 + i;
-            sc[mt][i] = (full || (kl >= lo_l && kl <= hi_l)) ? sacc[mt][i] * p.scale_log2 : kNegInf;
-            mx = fmaxf(mx, sc[mt][i]);
+            const int kl = pkt[j] * 16 + lg * 4 + i;
+            sc[j][i] = (full || (kl >= lo_l && kl <= hi_l)) ? sacc[j][i] * p.scale_log2 : kNegInf;
+            mx = fmaxf(mx, sc[j][i]);
           }
           mx = fmaxf(mx, shfl_xor_f(mx, 16));
           mx = fmaxf(mx, shfl_xor_f(mx, 32));
-          if (lg == 0) s_max[wave][mt][lr] = mx;
-          over |= mx > m_run[mt] + 8.f;
+          if (lg == 0) s_max[pkt[j]][pmt[j]][lr] = mx;
+          over |= mx > pick(m_run, pmt[j]) + 8.f;
         }
         // The reference max of a row only moves when some key exceeds it by more than
         // 2^8 (lazy rescaling).  Each wave computes its weights against the current
@@ -431,20 +500,20 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         float rsum[MT];
         auto weights = [&]() {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const float m = m_run[mt];
+          for (int j = 0; j < MT; ++j) {
+            const float m = pick(m_run, pmt[j]);
             float pv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pv[i] = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[mt][i] - m);
+            for (int i = 0; i < 4; ++i) pv[i] = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[j][i] - m);
             uint2 w2;
             w2.x = pack_bf16x2(pv[0], pv[1]);
             w2.y = pack_bf16x2(pv[2], pv[3]);
-            s_p[wave][mt][lane] = w2;
+            s_p[pkt[j]][pmt[j]][lane] = w2;
             // the normaliser sums exactly the (bf16) weights the PV product uses
             float rs = bf16_lo(w2.x) + bf16_hi(w2.x) + bf16_lo(w2.y) + bf16_hi(w2.y);
             rs += shfl_xor_f(rs, 16);
             rs += shfl_xor_f(rs, 32);
-            rsum[mt] = rs;
+            rsum[j] = rs;
           }
         };
         weights();
@@ -470,7 +539,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           lds_barrier();  // the redone weights visible
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) l_run[mt] += rsum[mt];
+        for (int j = 0; j < MT; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (pmt[j] == mt) l_run[mt] += rsum[j];
 
         // ---- O^T += V^T P^T over the tile's two 32-key halves.  Lane i of a 16-lane
         // group feeds row 32*ks + 16*h + 4*lg + i/4, dims 4*(i%4)..+3 of the tile; the
@@ -487,8 +559,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
               const uint2 p0 = s_p[2 * ks][mt][lane], p1 = s_p[2 * ks + 1][mt][lane];
               pb[mt].u = make_uint4(p0.x, p0.y, p1.x, p1.y);
             }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
+            // value operands are read one dim tile ahead of their MFMAs
+            auto read_v = [&](int dt) {
               const int c = wave * (DS / 8) + 2 * dt + (a >> 1);
               V16 av;
 #pragma unroll
@@ -499,6 +571,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
                 av.w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
                 av.w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
               }
+              return av;
+            };
+            V16 avq[2];
+            avq[0] = read_v(0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              if (dt + 1 < DT) avq[(dt + 1) & 1] = read_v(dt + 1);
+              const V16 av = avq[dt & 1];
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt) O[dt][mt] = mfma16x16x32(av.b, pb[mt].b, O[dt][mt]);
             }

@@ -135,6 +135,12 @@ __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
+// ORDERED = false drops the memory clobber, so the compiler may move ordinary LDS
+// reads and MFMAs across the DMA.  Only for a DMA into a ring stage that no code
+// between the surrounding barriers reads: its ordering against the reads of that
+// stage is carried by the barrier and wait statements (volatile asm, which keep
+// their relative order, each with a memory clobber).
+template <bool ORDERED = true>
 __device__ __forceinline__ void dma16(const void* base_in, uint32_t off, uint32_t lds_base) {
   // the base is wave-uniform by construction; say so, so that it lives in SGPRs
   const uint64_t bu = (uint64_t)(uintptr_t)base_in;
@@ -145,16 +151,28 @@ __device__ __forceinline__ void dma16(const void* base_in, uint32_t off, uint32_
   const void* base = (const void*)(uintptr_t)b64;
   lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
+  if constexpr (ORDERED) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds_base)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds_base));
+  }
 }
 
 // wait until at most N of this wave's vector memory operations are outstanding
