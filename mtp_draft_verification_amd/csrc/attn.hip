@@ -71,21 +71,78 @@ __device__ __forceinline__ void seq_range(const AttnParams& p, int b, int64_t& l
   len = hi > l0 ? hi - l0 : 0;
 }
 
-__device__ __forceinline__ int64_t total_keys(const AttnParams& p) {
-  int64_t t = 0;
+// Work split: each (sequence, kv head) segment of keys is cut into pieces of
+// `chunk` keys (a multiple of the 64-key tile; the last piece of a segment may be
+// shorter), one workgroup per piece.  chunk is the smallest such size for which the
+// pieces number at most nwg (or one piece per segment when there are at least nwg
+// segments), so no workgroup's keys cross a segment boundary.  Every workgroup and
+// the merge derive the same plan from the cache lengths.
+struct Pieces {
+  int64_t chunk;
+  int n;
+};
+
+__device__ __forceinline__ int64_t pieces_at(const AttnParams& p, int64_t c) {
+  int64_t n = 0;
   for (int b = 0; b < p.B; ++b) {
     int64_t lo, len;
     seq_range(p, b, lo, len);
-    t += len * p.Hkv;
+    n += (int64_t)p.Hkv * ((len + c - 1) / c);
   }
-  return t;
+  return n;
 }
 
-// keys per workgroup piece (a multiple of the 64-key tile)
-__device__ __forceinline__ int64_t piece_chunk(const AttnParams& p, int64_t total) {
-  int64_t c = (total + p.nwg - 1) / p.nwg;
-  c = (c + 63) & ~int64_t(63);
-  return c < p.min_chunk ? p.min_chunk : c;
+__device__ __forceinline__ Pieces piece_plan(const AttnParams& p) {
+  int64_t total = 0, maxlen = 0, nseg = 0;
+  for (int b = 0; b < p.B; ++b) {
+    int64_t lo, len;
+    seq_range(p, b, lo, len);
+    total += len * p.Hkv;
+    if (len > 0) nseg += p.Hkv;
+    if (len > maxlen) maxlen = len;
+  }
+  if (total == 0) return {64, 0};
+  auto up64 = [](int64_t x) { return (x + 63) & ~int64_t(63); };
+  int64_t c = up64((total + p.nwg - 1) / p.nwg);
+  if (c < p.min_chunk) c = p.min_chunk;
+  if (pieces_at(p, c) > p.nwg) {
+    if (nseg >= p.nwg) {
+      c = up64(maxlen);
+    } else {
+      // sum of ceil(len / c) <= total / c + nseg, so this size is small enough
+      int64_t hi = up64((total + (p.nwg - nseg) - 1) / (p.nwg - nseg));
+      int64_t lo = c;  // too small
+      while (hi - lo > 64) {
+        const int64_t mid = up64((lo + hi) / 2 - 63);
+        const int64_t m = mid <= lo ? lo + 64 : mid;
+        if (pieces_at(p, m) <= p.nwg) hi = m; else lo = m;
+      }
+      c = hi;
+    }
+  }
+  return {c, (int)pieces_at(p, c)};
+}
+
+// piece q -> sequence b, kv head kvh and its keys [a0, a1)
+__device__ __forceinline__ void piece_locate(const AttnParams& p, int64_t chunk, int q, int& b, int& kvh,
+                                             int64_t& a0, int64_t& a1) {
+  int64_t rem = q;
+  for (b = 0; b < p.B; ++b) {
+    int64_t lo, len;
+    seq_range(p, b, lo, len);
+    const int64_t nb = (len + chunk - 1) / chunk;
+    if (rem < nb * p.Hkv) {
+      kvh = (int)(rem / nb);
+      const int64_t pi = rem - kvh * nb;
+      a0 = lo + pi * chunk;
+      a1 = lo + ((pi + 1) * chunk < len ? (pi + 1) * chunk : len);
+      return;
+    }
+    rem -= nb * p.Hkv;
+  }
+  b = p.B - 1;  // not reached for q below the piece count
+  kvh = 0;
+  a0 = a1 = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -229,32 +286,71 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int lr = lane & 15, lg = lane >> 4;
   const int M = p.M, G = p.G;
 
-  const int64_t total = total_keys(p);
-  if (total == 0) return;
-  const int64_t chunk = piece_chunk(p, total);
-  const int64_t start = (int64_t)blockIdx.x * chunk;
-  if (start >= total) return;
-  const int64_t end = start + chunk < total ? start + chunk : total;
+  const Pieces pc = piece_plan(p);
+  const int slot = blockIdx.x;  // this workgroup's piece
+  if (slot >= pc.n) return;
+  int b, kvh;
+  int64_t a0, a1;  // keys [a0, a1) of sequence b, kv head kvh
+  piece_locate(p, pc.chunk, slot, b, kvh, a0, a1);
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
   const uint16_t* kcache = (const uint16_t*)p.k_cache;
   const uint16_t* vcache = (const uint16_t*)p.v_cache;
-
-  int64_t seg_off = 0;
-  for (int b = 0; b < p.B && seg_off < end; ++b) {
-    int64_t lo, len;
-    seq_range(p, b, lo, len);
-    if (len == 0) continue;
-    const int64_t L = p.cache_len[b];
-    const int64_t last = L + p.n_new - 1;
-    for (int kvh = 0; kvh < p.Hkv; ++kvh, seg_off += len) {
-      const int64_t s0 = seg_off, s1 = seg_off + len;
-      if (s1 <= start) continue;
-      if (s0 >= end) break;
-      const int64_t a0 = (start > s0 ? start : s0) - s0 + lo;  // first key of the piece
-      const int64_t a1 = (end < s1 ? end : s1) - s0 + lo;      // one past its last key
-      const int slot = blockIdx.x + b * p.Hkv + kvh;
+  {
+    {
+      const int64_t L = p.cache_len[b];
+      const int64_t last = L + p.n_new - 1;
       const int ntiles = (int)((a1 - a0 + TK - 1) / TK);
+
+      // every real row sees keys [seg_max_lo, seg_min_hi] (row 0 has the lowest causal
+      // limit, the last row the highest window start)
+      const int64_t seg_min_hi = (L + p.qoff) < last ? (L + p.qoff) : last;
+      const int64_t seg_max_lo = p.window > 0 ? L + p.qoff + p.nq - p.window : INT64_MIN;
+      const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.cap;  // row index of key 0
+      // DMA of tile t into its ring stage: wave w moves NI instructions of 1 KB each;
+      // lane l carries 16 B of row (l / CPR) of the instruction's row block.  The row
+      // block's address is wave-uniform; the per-lane byte offsets (row within the
+      // block, swizzled chunk) repeat every tile and are computed once.  Only a tile
+      // that runs past the piece clamps rows to its last row (finite data, masked out
+      // of the softmax) with per-lane offsets.
+      uint32_t off_pre[NI];
+#pragma unroll
+      for (int jj = 0; jj < NI; ++jj) {
+        const int rb = (wave * NI + jj) % (TK / RPI);
+        const int row = rb * RPI + lane / CPR;
+        off_pre[jj] = (uint32_t)((lane / CPR) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
+      }
+      auto issue_one = [&](int t, unsigned char* stage, int jj) __attribute__((always_inline)) {
+        const int64_t t0 = a0 + (int64_t)t * TK;
+        const bool partial = t0 + TK > a1;
+        {
+          const int ii = wave * NI + jj;
+          const int ten = ii / (TK / RPI);
+          const int rb = ii % (TK / RPI);
+          const uint16_t* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
+          const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + ten * TILEB + rb * RPI * ROWB));
+          int64_t brow = t0 + rb * RPI;  // first row of the block
+          uint32_t off = off_pre[jj];
+          if (partial) {
+            if (brow > a1 - 1) brow = a1 - 1;
+            const int row = rb * RPI + lane / CPR;
+            int64_t key = t0 + row;
+            if (key > a1 - 1) key = a1 - 1;
+            off = (uint32_t)((key - brow) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
+          }
+          dma16((const void*)(tbase + (head_row0 + brow) * D), off, lds);
+        }
+      };
+      auto issue = [&](int t, unsigned char* stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj) issue_one(t, stage, jj);
+      };
+
+      // the first tiles' DMA goes out before anything else
+#pragma unroll
+      for (int u = 0; u < NS - 1; ++u)
+        if (u < ntiles) issue(u, stage_of(u));
+
 
       // ---- queries of this (sequence, kv head), full head dim, as MFMA B operands
       // The 4 x MT (key tile, row tile) pairs of a tile's scores go to the waves in
@@ -277,14 +373,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         }
       }
       // consume the query loads here (the compiler then waits for them once, not
-      // inside the tile loop where the ring's DMA is in flight), and start from an
-      // idle memory pipe and a free ring
+      // inside the tile loop, which also waits for the first tiles: their DMA went out
+      // before the queries were requested, so the two latencies overlap)
 #pragma unroll
       for (int lt = 0; lt < NQ; ++lt)
 #pragma unroll
         for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qreg[lt][s].b));
       wait_vm_n<0>();
-      __syncthreads();
 
       f32x4_t O[DT][MT];
       float m_run[MT], l_run[MT];
@@ -295,54 +390,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-
-      // every real row sees keys [seg_max_lo, seg_min_hi] (row 0 has the lowest causal
-      // limit, the last row the highest window start)
-      const int64_t seg_min_hi = (L + p.qoff) < last ? (L + p.qoff) : last;
-      const int64_t seg_max_lo = p.window > 0 ? L + p.qoff + p.nq - p.window : INT64_MIN;
-      const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.cap;  // row index of key 0
-      // DMA of tile t into its ring stage: wave w moves NI instructions of 1 KB each;
-      // lane l carries 16 B of row (l / CPR) of the instruction's row block.  The row
-      // block's address is wave-uniform; the per-lane byte offsets (row within the
-      // block, swizzled chunk) repeat every tile and are computed once.  Only a tile
-      // that runs past the piece clamps rows to its last row (finite data, masked out
-      // of the softmax) with per-lane offsets.
-      uint32_t off_pre[NI];
-#pragma unroll
-      for (int jj = 0; jj < NI; ++jj) {
-        const int rb = (wave * NI + jj) % (TK / RPI);
-        const int row = rb * RPI + lane / CPR;
-        off_pre[jj] = (uint32_t)((lane / CPR) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
-      }
-      auto issue_one = [&](int t, unsigned char* stage, int jj) {
-        const int64_t t0 = a0 + (int64_t)t * TK;
-        const bool partial = t0 + TK > a1;
-        {
-          const int ii = wave * NI + jj;
-          const int ten = ii / (TK / RPI);
-          const int rb = ii % (TK / RPI);
-          const uint16_t* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
-          const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + ten * TILEB + rb * RPI * ROWB));
-          int64_t brow = t0 + rb * RPI;  // first row of the block
-          uint32_t off = off_pre[jj];
-          if (partial) {
-            if (brow > a1 - 1) brow = a1 - 1;
-            const int row = rb * RPI + lane / CPR;
-            int64_t key = t0 + row;
-            if (key > a1 - 1) key = a1 - 1;
-            off = (uint32_t)((key - brow) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
-          }
-          dma16((const void*)(tbase + (head_row0 + brow) * D), off, lds);
-        }
-      };
-      auto issue = [&](int t, unsigned char* stage) {
-#pragma unroll
-        for (int jj = 0; jj < NI; ++jj) issue_one(t, stage, jj);
-      };
-
-#pragma unroll
-      for (int u = 0; u < NS - 1; ++u)
-        if (u < ntiles) issue(u, stage_of(u));
 
       for (int tb = 0; tb < ntiles; tb += NS) {
 #pragma unroll
@@ -686,14 +733,16 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
   const int b = seg / p.Hkv, kvh = seg % p.Hkv;
   const int64_t L = p.cache_len[b];
   if (!seq_ok(p, L)) return;
-  const int64_t total = total_keys(p);
-  const int64_t chunk = piece_chunk(p, total);
-  int64_t off = 0, lo = 0, len = 0;
+  const Pieces pc = piece_plan(p);
+  // pieces of segment (b, kvh): [w0, w0 + nb)
+  int64_t w0 = 0, lo = 0, len = 0;
   for (int bb = 0; bb <= b; ++bb) {
     seq_range(p, bb, lo, len);
-    if (bb < b) off += len * p.Hkv;
+    if (bb < b) w0 += (int64_t)p.Hkv * ((len + pc.chunk - 1) / pc.chunk);
   }
-  off += (int64_t)kvh * len;
+  const int64_t nb = (len + pc.chunk - 1) / pc.chunk;
+  w0 += kvh * nb;
+  const int64_t w1 = w0 + nb - 1;
   const int D = p.D, G = p.G;
   const int j = r / G, hg = r % G;
   uint16_t* out = (uint16_t*)p.out + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D;
@@ -703,13 +752,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
     *(uint2*)(out + d0) = make_uint2(0, 0);
     return;
   }
-  const int64_t w0 = off / chunk, w1 = (off + len - 1) / chunk;
   float Mx = kNegInf;
-  for (int64_t w = w0; w <= w1; ++w) Mx = fmaxf(Mx, p.part_ml[((w + seg) * p.M + r) * 2]);
+  for (int64_t w = w0; w <= w1; ++w) Mx = fmaxf(Mx, p.part_ml[(w * p.M + r) * 2]);
   float l = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   if (Mx != kNegInf) {
     for (int64_t w = w0; w <= w1; ++w) {
-      const int64_t slot = w + seg;
+      const int64_t slot = w;
       const float m = p.part_ml[(slot * p.M + r) * 2];
       if (m == kNegInf) continue;
       const float f = exp2f(m - Mx);
@@ -779,7 +827,9 @@ static int validate_attn(const sv_attn_desc* d) {
 
 template <int D, int MT, bool KVS>
 static void launch_mfma(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, MT, KVS>), dim3(p.nwg), dim3(256), 0, s, p);
+  // one workgroup per piece: at most nwg pieces, or one per segment when there are more segments
+  const int grid = p.nwg > p.B * p.Hkv ? p.nwg : p.B * p.Hkv;
+  hipLaunchKernelGGL((attn_mfma_kernel<D, MT, KVS>), dim3(grid), dim3(256), 0, s, p);
 }
 
 template <int D, bool KVS>
