@@ -1,19 +1,21 @@
 // attn.hip -- verify attention over a shared KV cache (CDNA4 / gfx950).
 //
-// One call = three stream-ordered kernels:
+// One call = two stream-ordered kernels:
 //   1. rope_append: rotates the queries (into the workspace) and the new keys at
 //      their absolute positions and writes the new key / value rows into the
 //      cache ("Gemma 4 拆解" (marsggbo), section 2: p-RoPE on global layers, the
 //      value reuses the key; the cache is the one the drafter also reads,
-//      section 4.2).
+//      section 4.2).  It also zeroes the per-segment arrival counters and the
+//      output rows of sequences that have no visible keys.
 //   2. attn_mfma (bf16) or attn_f32: multi-query decode attention.  All
 //      (k+1) x (Hq/Hkv) query rows of one sequence and KV head form one block of
-//      rows that shares a single coalesced stream of that head's cache; the key
-//      range of the whole batch is cut into equal pieces, one per workgroup, so
-//      every CU streams the same number of bytes whatever the per-sequence
-//      lengths (split-KV); each piece leaves an unnormalised partial (m, l, acc).
-//   3. attn_merge: online-softmax combination of the partials of each
-//      (sequence, KV head, row): O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+//      rows that shares a single coalesced stream of that head's cache; each such
+//      segment of keys is cut into tile-aligned pieces, about equal across the
+//      batch, one per workgroup (split-KV).  Each piece leaves an unnormalised
+//      partial (m, l, acc), combined by online softmax:
+//      O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s -- for a small block of
+//      rows by the last piece of the segment to finish, otherwise by
+//   3. attn_merge, one workgroup per (sequence, KV head, row).
 #include "sv_device.h"
 #include "sv_host.h"
 
@@ -32,6 +34,8 @@ struct AttnParams {
   void* q_rot;            // workspace: rotated queries [B, nq, Hq, D]
   float* part_acc;        // workspace: [slots][M][D]
   float* part_ml;         // workspace: [slots][M][2]  (m in log2 units, l)
+  int32_t* seg_cnt;       // workspace: [B * Hkv] arrivals of a segment's pieces
+  int part_acc_bytes, part_ml_bytes;
   int32_t* dev_status;
   int64_t cap;
   int64_t q_stride, kv_stride;  // elements between consecutive (b, j) rows of q / k_new, v_new
@@ -123,9 +127,10 @@ __device__ __forceinline__ Pieces piece_plan(const AttnParams& p) {
   return {c, (int)pieces_at(p, c)};
 }
 
-// piece q -> sequence b, kv head kvh and its keys [a0, a1)
+// piece q -> sequence b, kv head kvh, its keys [a0, a1), and the pieces of its
+// segment [first, first + count)
 __device__ __forceinline__ void piece_locate(const AttnParams& p, int64_t chunk, int q, int& b, int& kvh,
-                                             int64_t& a0, int64_t& a1) {
+                                             int64_t& a0, int64_t& a1, int& first, int& count) {
   int64_t rem = q;
   for (b = 0; b < p.B; ++b) {
     int64_t lo, len;
@@ -136,6 +141,8 @@ __device__ __forceinline__ void piece_locate(const AttnParams& p, int64_t chunk,
       const int64_t pi = rem - kvh * nb;
       a0 = lo + pi * chunk;
       a1 = lo + ((pi + 1) * chunk < len ? (pi + 1) * chunk : len);
+      first = (int)(q - pi);
+      count = (int)nb;
       return;
     }
     rem -= nb * p.Hkv;
@@ -143,6 +150,8 @@ __device__ __forceinline__ void piece_locate(const AttnParams& p, int64_t chunk,
   b = p.B - 1;  // not reached for q below the piece count
   kvh = 0;
   a0 = a1 = 0;
+  first = q;
+  count = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -186,6 +195,18 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
   const int b = blockIdx.x / p.nq, j = blockIdx.x % p.nq;
   const int hs = blockIdx.y;  // [0, Hq): query head, then key heads, then value heads
   const int d = threadIdx.x;
+  if constexpr (sizeof(T) == 2) {
+    // the attention kernel counts each segment's finished pieces from zero
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int i = d; i < p.B * p.Hkv; i += blockDim.x) p.seg_cnt[i] = 0;
+    // a sequence without visible keys (or one that is skipped) has no pieces: its
+    // output rows are zero
+    if (hs < p.Hq && d < p.D) {
+      int64_t lo, len;
+      seq_range(p, b, lo, len);
+      if (len == 0) ((uint16_t*)p.out)[(((int64_t)b * p.nq + j) * p.Hq + hs) * p.D + d] = 0;
+    }
+  }
   const int64_t L = p.cache_len[b];
   if (!seq_ok(p, L)) {
     if (d == 0 && j == 0 && hs == 0) set_status(p.dev_status, L < 0 ? SV_DEV_BAD_LENGTH : SV_DEV_CACHE_OVERFLOW);
@@ -239,6 +260,10 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
 
+// A small block of rows (sliding-window layers) is combined by the last piece of its
+// segment to finish; a large one by attn_merge, which spreads the work over the chip.
+constexpr bool attn_fuse_merge(int D, int MT) { return D * 16 * MT <= 4096; }
+
 template <int D, int MT, bool KV_SAME>
 struct AttnCfg {
   static constexpr int DS = D / 4;              // PV dims per wave
@@ -289,9 +314,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const Pieces pc = piece_plan(p);
   const int slot = blockIdx.x;  // this workgroup's piece
   if (slot >= pc.n) return;
-  int b, kvh;
+  int b, kvh, first, count;
   int64_t a0, a1;  // keys [a0, a1) of sequence b, kv head kvh
-  piece_locate(p, pc.chunk, slot, b, kvh, a0, a1);
+  piece_locate(p, pc.chunk, slot, b, kvh, a0, a1, first, count);
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
   const uint16_t* kcache = (const uint16_t*)p.k_cache;
@@ -640,18 +665,133 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       for (int mt = 0; mt < MT; ++mt)
         if (lg == 0) s_sum[wave][mt][lr] = l_run[mt];
       __syncthreads();
+      if constexpr (!attn_fuse_merge(D, MT)) {
+        // combined by attn_merge, a later kernel
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int r = mt * 16 + lr;
+          if (r < M) {
+            float* dst = p.part_acc + ((int64_t)slot * M + r) * D + wave * DS + lg * 4;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(dst + dt * 16) = O[dt][mt];
+            if (wave == 0 && lg == 0) {
+              p.part_ml[((int64_t)slot * M + r) * 2 + 0] = m_run[mt];
+              p.part_ml[((int64_t)slot * M + r) * 2 + 1] =
+                  (s_sum[0][mt][lr] + s_sum[1][mt][lr]) + (s_sum[2][mt][lr] + s_sum[3][mt][lr]);
+            }
+          }
+        }
+        return;
+      }
+      // partials go through the device coherence point to the segment's last piece
+      const __amdgpu_buffer_rsrc_t acc_rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(p.part_acc, (short)0, p.part_acc_bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t ml_rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(p.part_ml, (short)0, p.part_ml_bytes, kBufferWord3);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + lr;
         if (r < M) {
-          float* dst = p.part_acc + ((int64_t)slot * M + r) * D + wave * DS + lg * 4;
+          const uint32_t off = (uint32_t)((((int64_t)slot * M + r) * D + wave * DS + lg * 4) * 4);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(dst + dt * 16) = O[dt][mt];
+          for (int dt = 0; dt < DT; ++dt) __builtin_amdgcn_raw_buffer_store_b128(O[dt][mt], acc_rsrc, off + dt * 64, 0, kCoherent);
           if (wave == 0 && lg == 0) {
-            p.part_ml[((int64_t)slot * M + r) * 2 + 0] = m_run[mt];
-            p.part_ml[((int64_t)slot * M + r) * 2 + 1] =
-                (s_sum[0][mt][lr] + s_sum[1][mt][lr]) + (s_sum[2][mt][lr] + s_sum[3][mt][lr]);
+            const float l = (s_sum[0][mt][lr] + s_sum[1][mt][lr]) + (s_sum[2][mt][lr] + s_sum[3][mt][lr]);
+            const uint32_t mo = (uint32_t)((((int64_t)slot * M + r) * 2) * 4);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run[mt]), ml_rsrc, mo, 0, kCoherent);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), ml_rsrc, mo + 4, 0, kCoherent);
           }
+        }
+      }
+      // count this piece once its stores have completed; the last of the segment merges
+      wait_vm_n<0>();
+      __syncthreads();
+      const int seg = b * p.Hkv + kvh;
+      if (tid == 0) s_flag[0] = __hip_atomic_fetch_add(p.seg_cnt + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_flag[0] != count - 1) return;
+
+      // ---- merge of the segment's pieces [first, first + count): per row the
+      // largest reference, then out = sum_w 2^(m_w - Mx) O_w / sum_w 2^(m_w - Mx) l_w
+      float* s_mx = &s_max[0][0][0];  // [M] (4 * MT * 16 >= M floats)
+      float* s_inv = &s_sum[0][0][0];
+      auto ld_ml = [&](int w, int r, int e) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            ml_rsrc, (uint32_t)((((int64_t)w * M + r) * 2 + e) * 4), 0, kCoherent));
+      };
+      // pieces are read in batches of PB with all of a batch's loads in flight (a
+      // buffer load past the end of the partials returns 0 and is masked out)
+      constexpr int PB = 8;
+      const int wend = first + count;
+      for (int r = tid; r < M; r += 256) {
+        // one pass: running maximum and the sum rescaled to it
+        float mx = kNegInf, l = 0.f;
+        for (int w0 = first; w0 < wend; w0 += PB) {
+          float mv[PB], lv[PB];
+#pragma unroll
+          for (int k = 0; k < PB; ++k) {
+            mv[k] = ld_ml(w0 + k, r, 0);
+            lv[k] = ld_ml(w0 + k, r, 1);
+          }
+          float nmx = mx;
+#pragma unroll
+          for (int k = 0; k < PB; ++k) nmx = (w0 + k < wend) ? fmaxf(nmx, mv[k]) : nmx;
+          if (nmx == kNegInf) continue;
+          l *= mx == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx - nmx);
+#pragma unroll
+          for (int k = 0; k < PB; ++k)
+            if (w0 + k < wend && mv[k] != kNegInf) l += __builtin_amdgcn_exp2f(mv[k] - nmx) * lv[k];
+          mx = nmx;
+        }
+        s_mx[r] = mx;
+        s_inv[r] = l > 0.f ? 1.f / l : 0.f;
+      }
+      __syncthreads();
+      // two output quads per thread and pass, all their loads in flight together
+      constexpr int DQ = D / 4;
+      constexpr int NIT = 2;
+      for (int i0 = tid; i0 < M * DQ; i0 += 256 * NIT) {
+        float acc[NIT][4];
+        int rr[NIT], dd[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int i = i0 + it * 256 < M * DQ ? i0 + it * 256 : i0;
+          rr[it] = i / DQ;
+          dd[it] = (i - rr[it] * DQ) * 4;
+          acc[it][0] = acc[it][1] = acc[it][2] = acc[it][3] = 0.f;
+        }
+        for (int w0 = first; w0 < wend; w0 += PB) {
+          float mv[NIT][PB];
+          f32x4_t v[NIT][PB];
+#pragma unroll
+          for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int k = 0; k < PB; ++k) {
+              mv[it][k] = ld_ml(w0 + k, rr[it], 0);
+              v[it][k] = __builtin_amdgcn_raw_buffer_load_b128(
+                  acc_rsrc, (uint32_t)((((int64_t)(w0 + k) * M + rr[it]) * D + dd[it]) * 4), 0, kCoherent);
+            }
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const float mx = s_mx[rr[it]];
+#pragma unroll
+            for (int k = 0; k < PB; ++k) {
+              // a piece that saw no key of this row has m = -inf and acc = 0
+              const float f = (w0 + k < wend && mv[it][k] != kNegInf) ? __builtin_amdgcn_exp2f(mv[it][k] - mx) : 0.f;
+              acc[it][0] += f * v[it][k][0]; acc[it][1] += f * v[it][k][1];
+              acc[it][2] += f * v[it][k][2]; acc[it][3] += f * v[it][k][3];
+            }
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          if (i0 + it * 256 >= M * DQ) continue;
+          const int r = rr[it];
+          const float inv = s_inv[r];
+          const int j = r / G, hg = r - (r / G) * G;
+          uint16_t* out = (uint16_t*)p.out + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + dd[it];
+          *(uint2*)out = make_uint2(pack_bf16x2(acc[it][0] * inv, acc[it][1] * inv),
+                                    pack_bf16x2(acc[it][2] * inv, acc[it][3] * inv));
         }
       }
     }
@@ -725,7 +865,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. merge of the split-KV partials (bf16 path)
+// 3. merge of the split-KV partials (bf16 path) in a kernel of its own, for blocks of
+//    rows too large for the last arriving piece to combine quickly
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
   const int r = blockIdx.x;          // row within the (sequence, kv head) block
@@ -776,7 +917,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
 static constexpr int kAttnNwgMax = 2048;
 
 struct AttnPlan {
-  size_t q_rot_bytes, acc_bytes, ml_bytes, total;
+  size_t q_rot_bytes, acc_bytes, ml_bytes, cnt_bytes, total;
   int M, slots;
 };
 
@@ -789,8 +930,9 @@ static AttnPlan attn_plan(const sv_attn_desc& d) {
     pl.slots = kAttnNwgMax + d.batch * d.n_heads_kv;
     pl.acc_bytes = align_up((size_t)pl.slots * pl.M * d.head_dim * 4, 256);
     pl.ml_bytes = align_up((size_t)pl.slots * pl.M * 2 * 4, 256);
+    pl.cnt_bytes = align_up((size_t)d.batch * d.n_heads_kv * 4, 256);
   }
-  pl.total = pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes;
+  pl.total = pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes + pl.cnt_bytes;
   return pl;
 }
 
@@ -882,6 +1024,9 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
   p.q_rot = ws;
   p.part_acc = (float*)(ws + pl.q_rot_bytes);
   p.part_ml = (float*)(ws + pl.q_rot_bytes + pl.acc_bytes);
+  p.seg_cnt = (int32_t*)(ws + pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes);
+  p.part_acc_bytes = (int)pl.acc_bytes;
+  p.part_ml_bytes = (int)pl.ml_bytes;
   p.dev_status = dev_status;
   p.cap = d->cache_capacity;
   p.q_stride = d->q_row_stride ? d->q_row_stride : (int64_t)d->n_heads_q * d->head_dim;
@@ -919,8 +1064,8 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
       default: rc = SV_ERR_UNSUPPORTED;
     }
     if (rc != SV_OK) return rc;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(pl.M, d->batch * d->n_heads_kv), dim3(d->head_dim / 4),
-                       0, s, p);
+    if (!attn_fuse_merge(d->head_dim, MT))
+      hipLaunchKernelGGL(attn_merge_kernel, dim3(pl.M, d->batch * d->n_heads_kv), dim3(d->head_dim / 4), 0, s, p);
   } else {
     hipLaunchKernelGGL(rope_append_kernel<float>, dim3(d->batch * d->n_q, heads), dim3(rope_threads), 0, s, p);
     hipLaunchKernelGGL(attn_f32_kernel, dim3(d->n_heads_q, d->n_q, d->batch), dim3(256), 0, s, p);

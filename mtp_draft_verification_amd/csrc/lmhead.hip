@@ -215,11 +215,6 @@ __device__ __forceinline__ int logical_wg(int b, int P) {
   return (b & 7) * (P >> 3) + (b >> 3);
 }
 
-// raw buffer descriptor word 3 for gfx950 (32-bit elements, no swizzle) and the
-// sc1 cache policy: stores write through to, and loads read from, the device's
-// coherence point
-constexpr int kBufferWord3 = 0x00020000;
-constexpr int kCoherent = 16;
 
 template <int MT, int T, int MODE>
 __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {

@@ -175,6 +175,13 @@ __device__ __forceinline__ void dma16(const void* base_in, uint32_t off, uint32_
   }
 }
 
+// raw buffer descriptor word 3 for gfx950 (32-bit elements, no swizzle) and the
+// sc1 cache policy: stores write through to, and loads read from, the device's
+// coherence point, so workgroups on different XCDs (each with its own L2) can hand
+// data to each other inside one kernel
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCoherent = 16;
+
 // wait until at most N of this wave's vector memory operations are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
