@@ -249,15 +249,31 @@ int sv_embed(int32_t rows, int32_t d_model, int32_t vocab, sv_dtype dtype,
 int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float* gain,
                void* y, sv_dtype out_dtype, void* stream);
 
+/* Residual add and RMSNorm in one launch (a pre-norm block's "x = x + f(...);
+ * y = rmsnorm(x)"): x (fp32 [rows, dim], updated in place) += the sum of the
+ * `splits` slices of parts (fp32 [splits, rows, dim], as SV_EPI_SPLIT_F32 writes
+ * them; added in slice order, the sum then added to x), then y = rmsnorm(x) as
+ * sv_rmsnorm.  parts NULL or splits 0: no add.  dim % 4 == 0, x / parts / gain /
+ * y 16-byte aligned. */
+int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, const float* parts, int32_t splits,
+                   const float* gain, void* y, sv_dtype out_dtype, void* stream);
+
 typedef enum {
   SV_EPI_STORE = 0,      /* y = x W^T stored in the descriptor dtype */
   SV_EPI_ADD_F32 = 1,    /* y (fp32) += x W^T: a residual add */
-  SV_EPI_GEGLU = 2       /* bf16 only: the GeGLU gate fused into the gate/up projection.
+  SV_EPI_GEGLU = 2,      /* bf16 only: the GeGLU gate fused into the gate/up projection.
                             W holds the gate and up rows interleaved by 16: rows
                             [32j, 32j+16) are gate features 16j..16j+15 and rows
                             [32j+16, 32j+32) the up features of the same indices;
                             y [R, N/2] bf16 gets gelu_tanh(g) * u with g and u rounded
                             to bf16 first (the values sv_geglu would read).  N % 128 == 0. */
+  SV_EPI_SPLIT_F32 = 3   /* bf16 only: the product split over the input dims.  The K dims
+                            are cut into S = sv_linear_splits(desc) equal ranges of whole
+                            64-dim chunks; y (fp32 [S, R, N]) slice s receives the partial
+                            product over range s, written whole (no accumulation), and the
+                            sum over s in slice order is x W^T.  For a consumer that adds
+                            the slices itself (sv_add_rmsnorm); the call needs no workspace
+                            and writes every element of y. */
 } sv_epilogue;
 
 typedef struct {
@@ -268,7 +284,13 @@ typedef struct {
   sv_epilogue epilogue;
 } sv_linear_desc;
 
-/* Workspace of sv_linear (0 in fp32): arrival counters and split partials.  Same
+/* S of SV_EPI_SPLIT_F32 for this shape on the current device (1 <= S <= the
+ * device's compute units / ceil(N / 128)); 0 if the descriptor is invalid, not
+ * SV_EPI_SPLIT_F32, or N is too large for a split (more than one workgroup's worth
+ * of output features per compute unit). */
+int32_t sv_linear_splits(const sv_linear_desc* desc);
+
+/* Workspace of sv_linear (0 in fp32 and for SV_EPI_SPLIT_F32): arrival counters and split partials.  Same
  * contract as sv_lmhead_workspace: zero-filled before first use, left zero by
  * every call, one call at a time. */
 size_t sv_linear_workspace(const sv_linear_desc* desc);

@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE = 0, -1, -2, -3, -4, -5
 SV_F32, SV_BF16 = 0, 1
 SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL = 0, 1, 2
-SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU = 0, 1, 2
+SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU, SV_EPI_SPLIT_F32 = 0, 1, 2, 3
 SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
-           "sv_linear_workspace", "sv_linear", "sv_geglu")
+           "sv_add_rmsnorm", "sv_linear_splits", "sv_linear_workspace", "sv_linear", "sv_geglu")
 
 
 class SvError(RuntimeError):
@@ -97,6 +97,10 @@ def load():
     L.sv_embed.argtypes = [i32, i32, i32, ctypes.c_int, P, P, f32, P, P, P]
     L.sv_rmsnorm.restype = ctypes.c_int
     L.sv_rmsnorm.argtypes = [i32, i32, f32, P, P, P, ctypes.c_int, P]
+    L.sv_add_rmsnorm.restype = ctypes.c_int
+    L.sv_add_rmsnorm.argtypes = [i32, i32, f32, P, P, i32, P, P, ctypes.c_int, P]
+    L.sv_linear_splits.restype = i32
+    L.sv_linear_splits.argtypes = [ctypes.POINTER(LinearDesc)]
     L.sv_linear_workspace.restype = sz
     L.sv_linear_workspace.argtypes = [ctypes.POINTER(LinearDesc)]
     L.sv_linear.restype = ctypes.c_int
@@ -189,6 +193,17 @@ def sv_embed(rows: int, d_model: int, vocab: int, dtype: int, tokens, table, sca
 def sv_rmsnorm(rows: int, dim: int, eps: float, x, gain, y, out_dtype: int, stream=None) -> None:
     rc = load().sv_rmsnorm(rows, dim, float(eps), _ptr(x), _ptr(gain), _ptr(y), out_dtype, _stream(stream))
     _check("sv_rmsnorm", rc)
+
+
+def sv_add_rmsnorm(rows: int, dim: int, eps: float, x, parts, splits: int, gain, y, out_dtype: int,
+                   stream=None) -> None:
+    rc = load().sv_add_rmsnorm(rows, dim, float(eps), _ptr(x), _ptr(parts), int(splits), _ptr(gain), _ptr(y),
+                               out_dtype, _stream(stream))
+    _check("sv_add_rmsnorm", rc)
+
+
+def sv_linear_splits(desc: LinearDesc) -> int:
+    return int(load().sv_linear_splits(ctypes.byref(desc)))
 
 
 def sv_linear_workspace(desc: LinearDesc) -> int:

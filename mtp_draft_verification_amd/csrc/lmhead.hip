@@ -17,7 +17,8 @@
 
 namespace sv {
 
-enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_GEGLU = 5 };
+enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_GEGLU = 5,
+                      GM_SPLIT = 6 };
 
 struct SelPart {   // per (workgroup, row) partial of the select epilogue
   float t1v, t2v;  // top-2 logits (RESIDUAL: residual-draw scores)
@@ -46,6 +47,7 @@ struct GemmParams {
   void* y;               // [R, N] bf16 or fp32
   // stream-K
   float* part;           // [grid][2][rows][NB] partial sums
+  int splits;            // GM_SPLIT: K slices per block (grid = nblk * splits)
   int32_t* cnt;          // [nblk][4] arrival counters, zero between calls
 };
 
@@ -306,6 +308,19 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
   auto seg_end = [&](int b, bool full) {
     const int row0 = b * NB + wave * WROWS;
     if (row0 >= p.N) return;  // wave slice past the last feature (uniform per wave)
+    if constexpr (MODE == GM_SPLIT) {
+      // workgroup me holds K slice me % splits of its block: the partial product goes
+      // to that slice of y [splits][rows][N] for the consumer to add up
+      float* ys = (float*)p.y + (int64_t)(me % p.splits) * nx * p.N;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int r = mt * 16 + lr;
+          if (r < nx) *(f32x4_t*)(ys + (int64_t)r * p.N + row0 + t * 16 + lg * 4) = acc[t][mt];
+        }
+      return;
+    }
     if (!full) {
       // Partials move through buffer stores / loads with the sc1 (device-coherent)
       // cache policy and the counter through a device-scope atomic: no L2 writeback
@@ -630,6 +645,16 @@ static RingPlan ring_plan(int T, int nx, int K, int N, int max_wg) {
   return pl;
 }
 
+// K-split plan of SV_EPI_SPLIT_F32: nblk * S workgroups, S the largest divisor of
+// the chunk count with nblk * S <= max_wg, so workgroup me takes exactly slice
+// me % S of block me / S.  0 if the blocks alone exceed max_wg.
+static int split_count(const RingPlan& pl, int max_wg) {
+  if (pl.nblk > max_wg) return 0;
+  for (int S = max_wg / pl.nblk; S >= 1; --S)
+    if (pl.kch % S == 0) return S;
+  return 1;
+}
+
 static int live_wg() {
   const int c = device_cus();
   return c < kMaxWG ? c : kMaxWG;
@@ -677,7 +702,10 @@ static int dispatch_ring(const GemmParams& p, int nx, int grid, hipStream_t s) {
 static int validate_linear(const sv_linear_desc* d) {
   if (!d) return SV_ERR_ARG;
   if (d->rows <= 0 || d->in_features <= 0 || d->out_features <= 0) return SV_ERR_ARG;
-  if (d->epilogue != SV_EPI_STORE && d->epilogue != SV_EPI_ADD_F32 && d->epilogue != SV_EPI_GEGLU) return SV_ERR_ARG;
+  if (d->epilogue != SV_EPI_STORE && d->epilogue != SV_EPI_ADD_F32 && d->epilogue != SV_EPI_GEGLU &&
+      d->epilogue != SV_EPI_SPLIT_F32)
+    return SV_ERR_ARG;
+  if (d->epilogue == SV_EPI_SPLIT_F32 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->out_features % 64) return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_GEGLU && (d->dtype != SV_BF16 || d->out_features % 128)) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
@@ -774,9 +802,15 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
   return launch_status();
 }
 
+extern "C" int32_t sv_linear_splits(const sv_linear_desc* d) {
+  if (validate_linear(d) != SV_OK || d->epilogue != SV_EPI_SPLIT_F32) return 0;
+  if (check_device() != SV_OK) return 0;
+  return split_count(ring_plan(lin_tiles(*d), d->rows, d->in_features, d->out_features, live_wg()), live_wg());
+}
+
 extern "C" size_t sv_linear_workspace(const sv_linear_desc* d) {
   if (validate_linear(d) != SV_OK) return 0;
-  if (d->dtype == SV_F32) return 0;
+  if (d->dtype == SV_F32 || d->epilogue == SV_EPI_SPLIT_F32) return 0;
   const RingPlan pl = ring_plan(lin_tiles(*d), d->rows, d->in_features, d->out_features, kMaxWG);
   return pl.cnt_bytes + pl.part_bytes;
 }
@@ -798,8 +832,13 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
                        d->epilogue == SV_EPI_ADD_F32 ? 1 : 0);
     return launch_status();
   }
-  const RingPlan pl = ring_plan(lin_tiles(*d), d->rows, d->in_features, d->out_features, live_wg());
+  RingPlan pl = ring_plan(lin_tiles(*d), d->rows, d->in_features, d->out_features, live_wg());
   GemmParams p{};
+  if (d->epilogue == SV_EPI_SPLIT_F32) {
+    p.splits = split_count(pl, live_wg());
+    if (p.splits == 0) return SV_ERR_UNSUPPORTED;
+    pl.grid = pl.nblk * p.splits;
+  }
   p.x = (const uint16_t*)x;
   p.w = (const uint16_t*)w;
   p.R = d->rows;
@@ -812,6 +851,8 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   p.part = (float*)((char*)workspace + pl.cnt_bytes);
   if (d->epilogue == SV_EPI_GEGLU)
     rc = dispatch_ring<2, GM_GEGLU>(p, d->rows, pl.grid, s);
+  else if (d->epilogue == SV_EPI_SPLIT_F32)
+    rc = pl.T == 1 ? dispatch_ring<1, GM_SPLIT>(p, d->rows, pl.grid, s) : dispatch_ring<2, GM_SPLIT>(p, d->rows, pl.grid, s);
   else if (pl.T == 1)
     rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<1, GM_STORE_BF16>(p, d->rows, pl.grid, s)
                                      : dispatch_ring<1, GM_ADD_F32>(p, d->rows, pl.grid, s);

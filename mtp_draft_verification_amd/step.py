@@ -7,14 +7,17 @@ then accept_longest_prefix.  Here that forward is, per layer,
     a = rmsnorm(x)                 sv_rmsnorm      (x: fp32 residual stream)
     qkv = a Wqkv^T                 sv_linear       (q, k, v in one projection)
     o = attn(q, k, v; cache)       sv_verify_attn  (appends the k+1 new rows)
-    x += o Wo^T                    sv_linear (SV_EPI_ADD_F32)
-    m = rmsnorm(x)                 sv_rmsnorm
+    x += o Wo^T                    sv_linear (SV_EPI_SPLIT_F32: the K-split partial
+                                   products), added into x by the next norm
+    m = rmsnorm(x)                 sv_add_rmsnorm  (x += the partials, then the norm)
     f = gelu_tanh(m Wg^T) * (m Wu^T)   sv_linear (SV_EPI_GEGLU: one launch, gate/up
                                    rows interleaved by 16; sv_linear + sv_geglu where
                                    that layout does not apply)
-    x += f Wd^T                    sv_linear (SV_EPI_ADD_F32)
+    x += f Wd^T                    sv_linear (SV_EPI_SPLIT_F32), added by the next
+                                   layer's (or the final) sv_add_rmsnorm
 
-then h = rmsnorm(x), sv_lmhead_select over the tied embedding and sv_accept.
+then h = rmsnorm(x), sv_lmhead_select over the tied embedding and sv_accept.  The
+fp32 stack (no norms) adds into x with SV_EPI_ADD_F32 instead.
 Every call is enqueued on one stream with no host synchronisation; all buffers
 are allocated once up front, so a step allocates nothing.  This module only
 marshals arguments: the arithmetic is the library's.
@@ -80,6 +83,17 @@ class VerifyStack:
         self.gu = z(R, 2 * cfg.d_ff) if cfg.d_ff and not self.fused_geglu else None
         self.f = z(R, cfg.d_ff) if cfg.d_ff else None
         self.h = self.a  # final norm output reuses the activation buffer
+        # residual projections leave K-split partials that the next norm adds into x
+        self.split = {}
+        if self.bf16:
+            for ly in cfg.layers:
+                for K in (ly.n_heads_q * ly.head_dim, cfg.d_ff):
+                    if K:
+                        S = L.sv_linear_splits(L.LinearDesc(rows=R, in_features=K, out_features=d, dtype=self.dt,
+                                                            epilogue=L.SV_EPI_SPLIT_F32))
+                        if S > 0:
+                            self.split[K] = S
+        self.parts = z(max(self.split.values()) * R * d, dtype=torch.float32) if self.split else None
         ws = max(L.sv_verify_attn_workspace(attn_desc(ly, B, k + 1, self.cap, cfg.dtype)) for ly in cfg.layers)
         self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.lin_ws = torch.zeros(max([self._lin_ws(*s) for s in self._lin_shapes()] + [256]),
@@ -136,10 +150,26 @@ class VerifyStack:
         desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi)
         L.sv_linear(desc, x, w, y, self.lin_ws, stream)
 
-    def _norm(self, x, y, stream):
+    def _residual(self, inp, w, stream):
+        """x += inp W^T: K-split partials left for the next norm (returned as
+        (parts, S)) where the split applies, else added into x now (None)."""
+        K = w.shape[1]
+        S = self.split.get(K, 0)
+        if S:
+            self._linear(inp, w, self.parts, L.SV_EPI_SPLIT_F32, stream)
+            return (self.parts, S)
+        self._linear(inp, w, self.x, L.SV_EPI_ADD_F32, stream)
+        return None
+
+    def _norm(self, x, y, stream, pending=None):
         if self.cfg.norm:
-            L.sv_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, None, y, self.dt, stream)
+            if pending is not None:
+                L.sv_add_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, pending[0], pending[1], None, y, self.dt,
+                                 stream)
+            else:
+                L.sv_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, None, y, self.dt, stream)
             return y
+        assert pending is None
         return x  # fp32 stack without norms feeds the residual stream directly
 
     # ------------------------------------------------------------------
@@ -154,9 +184,10 @@ class VerifyStack:
         L.sv_embed(self.R, d, cfg.vocab, self.dt, tokens, self.W["E"], math.sqrt(d), self.x,
                    self.dev_status, stream)
         self._end(t)
+        pending = None  # partials of the last residual projection, not yet in x
         for i, (ly, lw, cache, desc) in enumerate(zip(cfg.layers, self.W["layers"], self.caches,
                                                       self.attn_descs)):
-            a = self._norm(self.x, self.a, stream)
+            a = self._norm(self.x, self.a, stream, pending)
             nq_f = ly.n_heads_q * ly.head_dim
             nk_f = ly.n_heads_kv * ly.head_dim
             nout = self._nout(ly)
@@ -174,10 +205,10 @@ class VerifyStack:
                              self.attn_ws, self.dev_status, stream)
             self._end(t)
             t = self._ev(f"L{i}.o", stream)
-            self._linear(o, lw["wo"], self.x, L.SV_EPI_ADD_F32, stream)
+            pending = self._residual(o, lw["wo"], stream)
             self._end(t)
             if cfg.d_ff:
-                m = self._norm(self.x, self.a, stream)
+                m = self._norm(self.x, self.a, stream, pending)
                 t = self._ev(f"L{i}.gu", stream)
                 if self.fused_geglu:
                     self._linear(m, self.wgu_il[i], self.f, L.SV_EPI_GEGLU, stream)
@@ -189,10 +220,10 @@ class VerifyStack:
                     L.sv_geglu(self.R, cfg.d_ff, self.dt, self.gu, self.f, stream)
                     self._end(t)
                 t = self._ev(f"L{i}.down", stream)
-                self._linear(self.f, lw["wd"], self.x, L.SV_EPI_ADD_F32, stream)
+                pending = self._residual(self.f, lw["wd"], stream)
                 self._end(t)
         t = self._ev("final_norm", stream)
-        h = self._norm(self.x, self.h, stream)
+        h = self._norm(self.x, self.h, stream, pending)
         self._end(t)
         return h
 

@@ -118,3 +118,35 @@ def test_fused_geglu(R, K, dff):
     err = np.abs(got - ref)
     assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
     say(f"[linear geglu] ok, max err/bound {float((err / bound).max()):.3f}")
+
+
+@gpu
+@pytest.mark.parametrize("R,K,N", [(40, 15360, 3840), (40, 4096, 3840), (7, 96, 192), (33, 8192 + 32, 640)])
+def test_split_partials(R, K, N):
+    """SV_EPI_SPLIT_F32: every slice written, their sum in slice order within
+    (K + S) 2^-24 sum |x w| of the exact product."""
+    dev = need_gpu()
+    desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=L.SV_EPI_SPLIT_F32)
+    S = L.sv_linear_splits(desc)
+    say(f"[linear split] R={R} K={K} N={N} S={S}")
+    assert S >= 1
+    assert L.sv_linear_workspace(desc) == 0
+    x = inputs.normal((R, K), 1.0, 12, "x", dev)
+    W = inputs.normal((N, K), K ** -0.5, 12, "W", dev)
+    y = torch.full((S, R, N), float("nan"), dtype=torch.float32, device=dev)
+    L.sv_linear(desc, x, W, y, None)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.all(np.isfinite(got)), "a slice was left unwritten"
+    total = got[0].astype(np.float64)
+    for s in range(1, S):
+        total = (total.astype(np.float32) + got[s]).astype(np.float64)
+    ref = oracle.linear(host(x), inputs.bf16_bits(W))
+    mag = oracle.linear(np.abs(host(x)), np.abs(host(W)))
+    bound = (K + S) * 2.0 ** -24 * mag + 1e-30
+    err = np.abs(total - ref)
+    assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
+    y2 = torch.empty_like(y)
+    L.sv_linear(desc, x, W, y2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "repeat call differs"
