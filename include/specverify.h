@@ -92,8 +92,9 @@ typedef struct {
 } sv_attn_desc;
 
 /* Bytes of workspace sv_verify_attn needs for this descriptor (0 on an invalid
- * descriptor).  The workspace holds the rotated queries and the split-KV
- * partial results; its contents are scratch, nothing survives the call. */
+ * descriptor).  The workspace holds the rotated queries, the split-KV partial
+ * results and per-(sequence, KV head) arrival counters; its contents are scratch
+ * (set by the call itself), nothing survives the call. */
 size_t sv_verify_attn_workspace(const sv_attn_desc* desc);
 
 /* Verify attention over a shared KV cache, local (sliding window) or global
@@ -115,7 +116,8 @@ size_t sv_verify_attn_workspace(const sv_attn_desc* desc);
  * row) (and t > p - W on a window layer) with softmax(scale * q.k_t) weights.
  * RoPE pairs dim i with dim i + rope_dims/2 (rotate-half).  A query with no
  * visible key gets a zero row.  If L + n_q > cache_capacity on an append call
- * the sequence is skipped (out rows untouched) and SV_DEV_CACHE_OVERFLOW set. */
+ * the sequence is skipped (out rows untouched) and SV_DEV_CACHE_OVERFLOW set.
+ * bf16: batch <= 256 and cache_capacity < 2^31 - 4096, else SV_ERR_UNSUPPORTED. */
 int sv_verify_attn(const sv_attn_desc* desc, const void* q, const void* k_new,
                    const void* v_new, void* k_cache, void* v_cache,
                    const int32_t* cache_len, void* out, void* workspace,

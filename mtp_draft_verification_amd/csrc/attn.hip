@@ -81,77 +81,152 @@ __device__ __forceinline__ void seq_range(const AttnParams& p, int b, int64_t& l
 // pieces number at most nwg (or one piece per segment when there are at least nwg
 // segments), so no workgroup's keys cross a segment boundary.  Every workgroup and
 // the merge derive the same plan from the cache lengths.
+// The plan is computed by each wave on its own, in parallel over the batch: lane l
+// holds the key counts of sequences l, l + 64, ... (up to kPlanGroups * 64 of them,
+// key counts below 2^31) and sums or scans them with cross-lane shuffles, so a
+// workgroup spends well under a microsecond on it.  All 64 lanes must be active.
+constexpr int kPlanGroups = 4;  // batch up to 256
 struct Pieces {
-  int64_t chunk;
+  int chunk;
   int n;
 };
+struct BatchLens {
+  int len[kPlanGroups];  // key count of sequence lane + 64 g (0 past the batch)
+};
 
-__device__ __forceinline__ int64_t pieces_at(const AttnParams& p, int64_t c) {
-  int64_t n = 0;
-  for (int b = 0; b < p.B; ++b) {
-    int64_t lo, len;
-    seq_range(p, b, lo, len);
-    n += (int64_t)p.Hkv * ((len + c - 1) / c);
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
   }
-  return n;
+  return v;
+}
+__device__ __forceinline__ int ceil_div_u(int n, int d) { return (int)(((unsigned)n + (unsigned)d - 1u) / (unsigned)d); }
+
+__device__ __forceinline__ BatchLens batch_lens(const AttnParams& p) {
+  const int lane = threadIdx.x & 63;
+  BatchLens bl;
+#pragma unroll
+  for (int g = 0; g < kPlanGroups; ++g) {
+    const int b = lane + 64 * g;
+    int64_t lo = 0, len = 0;
+    if (b < p.B) seq_range(p, b, lo, len);
+    bl.len[g] = (int)len;
+  }
+  return bl;
 }
 
-__device__ __forceinline__ Pieces piece_plan(const AttnParams& p) {
-  int64_t total = 0, maxlen = 0, nseg = 0;
-  for (int b = 0; b < p.B; ++b) {
-    int64_t lo, len;
-    seq_range(p, b, lo, len);
-    total += len * p.Hkv;
-    if (len > 0) nseg += p.Hkv;
-    if (len > maxlen) maxlen = len;
+__device__ __forceinline__ int pieces_at(const AttnParams& p, const BatchLens& bl, int c) {
+  int n = 0;
+#pragma unroll
+  for (int g = 0; g < kPlanGroups; ++g) n += ceil_div_u(bl.len[g], c);
+  return wave_sum_i(n) * p.Hkv;
+}
+
+__device__ __forceinline__ Pieces piece_plan(const AttnParams& p, const BatchLens& bl) {
+  int64_t total = 0;
+  int nseg = 0, maxlen = 0;
+#pragma unroll
+  for (int g = 0; g < kPlanGroups; ++g) {
+    // per-lane partial sums stay far below 2^31 before the cross-lane sum
+    total += bl.len[g];
+    nseg += bl.len[g] > 0 ? 1 : 0;
+    maxlen = max(maxlen, bl.len[g]);
   }
+  {
+    const int lo32 = wave_sum_i((int)(total & 0xffff)), hi32 = wave_sum_i((int)(total >> 16));
+    total = ((int64_t)hi32 << 16) + lo32;
+  }
+  total *= p.Hkv;
+  nseg = wave_sum_i(nseg) * p.Hkv;
+  maxlen = wave_max_i(maxlen);
   if (total == 0) return {64, 0};
-  auto up64 = [](int64_t x) { return (x + 63) & ~int64_t(63); };
-  int64_t c = up64((total + p.nwg - 1) / p.nwg);
+  auto up64 = [](int64_t x) { return (int)((x + 63) & ~int64_t(63)); };
+  int c = up64((total + p.nwg - 1) / p.nwg);
   if (c < p.min_chunk) c = p.min_chunk;
-  if (pieces_at(p, c) > p.nwg) {
+  if (pieces_at(p, bl, c) > p.nwg) {
     if (nseg >= p.nwg) {
       c = up64(maxlen);
     } else {
       // sum of ceil(len / c) <= total / c + nseg, so this size is small enough
-      int64_t hi = up64((total + (p.nwg - nseg) - 1) / (p.nwg - nseg));
-      int64_t lo = c;  // too small
+      int hi = up64((total + (p.nwg - nseg) - 1) / (p.nwg - nseg));
+      int lo = c;  // too small
       while (hi - lo > 64) {
-        const int64_t mid = up64((lo + hi) / 2 - 63);
-        const int64_t m = mid <= lo ? lo + 64 : mid;
-        if (pieces_at(p, m) <= p.nwg) hi = m; else lo = m;
+        const int mid = ((lo + hi) / 2) & ~63;
+        const int m = mid <= lo ? lo + 64 : mid;
+        if (pieces_at(p, bl, m) <= p.nwg) hi = m; else lo = m;
       }
       c = hi;
     }
   }
-  return {c, (int)pieces_at(p, c)};
+  return {c, pieces_at(p, bl, c)};
 }
 
 // piece q -> sequence b, kv head kvh, its keys [a0, a1), and the pieces of its
 // segment [first, first + count)
-__device__ __forceinline__ void piece_locate(const AttnParams& p, int64_t chunk, int q, int& b, int& kvh,
-                                             int64_t& a0, int64_t& a1, int& first, int& count) {
-  int64_t rem = q;
-  for (b = 0; b < p.B; ++b) {
-    int64_t lo, len;
-    seq_range(p, b, lo, len);
-    const int64_t nb = (len + chunk - 1) / chunk;
-    if (rem < nb * p.Hkv) {
-      kvh = (int)(rem / nb);
-      const int64_t pi = rem - kvh * nb;
-      a0 = lo + pi * chunk;
-      a1 = lo + ((pi + 1) * chunk < len ? (pi + 1) * chunk : len);
-      first = (int)(q - pi);
-      count = (int)nb;
-      return;
+__device__ __forceinline__ void piece_locate(const AttnParams& p, const BatchLens& bl, int chunk, int q, int& b,
+                                             int& kvh, int64_t& a0, int64_t& a1, int& first, int& count) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;  // pieces of the sequences before this group
+  b = -1;
+#pragma unroll
+  for (int g = 0; g < kPlanGroups; ++g) {
+    const int cnt = ceil_div_u(bl.len[g], chunk) * p.Hkv;
+    const int incl = base + wave_incl_scan_i(cnt, lane);
+    const uint64_t hit = __ballot(q < incl && q >= incl - cnt);
+    if (b < 0 && hit) {
+      const int l = __builtin_ctzll(hit);
+      b = l + 64 * g;
+      const int excl = __shfl(incl, l, 64) - __shfl(cnt, l, 64);
+      const int nb = __shfl(cnt, l, 64) / p.Hkv;
+      const int rem = q - excl;
+      kvh = rem / nb;
+      const int pi = rem - kvh * nb;
+      int64_t lo, len;
+      seq_range(p, b, lo, len);
+      a0 = lo + (int64_t)pi * chunk;
+      a1 = lo + ((int64_t)(pi + 1) * chunk < len ? (int64_t)(pi + 1) * chunk : len);
+      first = q - pi;
+      count = nb;
     }
-    rem -= nb * p.Hkv;
+    base = __shfl(incl, 63, 64);
   }
-  b = p.B - 1;  // not reached for q below the piece count
-  kvh = 0;
-  a0 = a1 = 0;
-  first = q;
-  count = 1;
+  if (b < 0) {  // not reached for q below the piece count
+    b = 0;
+    kvh = 0;
+    a0 = a1 = 0;
+    first = q;
+    count = 1;
+  }
+}
+
+// first piece and piece count of segment (b, kvh)
+__device__ __forceinline__ void segment_pieces(const AttnParams& p, const BatchLens& bl, int chunk, int b, int kvh,
+                                               int& first, int& count) {
+  const int lane = threadIdx.x & 63;
+  int before = 0, nb = 0;
+#pragma unroll
+  for (int g = 0; g < kPlanGroups; ++g) {
+    const int bb = lane + 64 * g;
+    const int c = ceil_div_u(bl.len[g], chunk);
+    if (bb < b) before += c;
+    if (bb == b) nb = c;
+  }
+  before = wave_sum_i(before) * p.Hkv;
+  nb = wave_sum_i(nb);
+  first = before + kvh * nb;
+  count = nb;
 }
 
 // ---------------------------------------------------------------------------
@@ -199,9 +274,9 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
     // the attention kernel counts each segment's finished pieces from zero
     if (blockIdx.x == 0 && blockIdx.y == 0)
       for (int i = d; i < p.B * p.Hkv; i += blockDim.x) p.seg_cnt[i] = 0;
-    // a sequence without visible keys (or one that is skipped) has no pieces: its
-    // output rows are zero
-    if (hs < p.Hq && d < p.D) {
+    // a sequence without visible keys has no pieces: its output rows are zero (a
+    // skipped sequence's rows are left untouched)
+    if (hs < p.Hq && d < p.D && seq_ok(p, p.cache_len[b])) {
       int64_t lo, len;
       seq_range(p, b, lo, len);
       if (len == 0) ((uint16_t*)p.out)[(((int64_t)b * p.nq + j) * p.Hq + hs) * p.D + d] = 0;
@@ -311,12 +386,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int lr = lane & 15, lg = lane >> 4;
   const int M = p.M, G = p.G;
 
-  const Pieces pc = piece_plan(p);
+  const BatchLens bl = batch_lens(p);
+  const Pieces pc = piece_plan(p, bl);
   const int slot = blockIdx.x;  // this workgroup's piece
   if (slot >= pc.n) return;
   int b, kvh, first, count;
   int64_t a0, a1;  // keys [a0, a1) of sequence b, kv head kvh
-  piece_locate(p, pc.chunk, slot, b, kvh, a0, a1, first, count);
+  piece_locate(p, bl, pc.chunk, slot, b, kvh, a0, a1, first, count);
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
   const uint16_t* kcache = (const uint16_t*)p.k_cache;
@@ -874,16 +950,13 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
   const int b = seg / p.Hkv, kvh = seg % p.Hkv;
   const int64_t L = p.cache_len[b];
   if (!seq_ok(p, L)) return;
-  const Pieces pc = piece_plan(p);
-  // pieces of segment (b, kvh): [w0, w0 + nb)
-  int64_t w0 = 0, lo = 0, len = 0;
-  for (int bb = 0; bb <= b; ++bb) {
-    seq_range(p, bb, lo, len);
-    if (bb < b) w0 += (int64_t)p.Hkv * ((len + pc.chunk - 1) / pc.chunk);
-  }
-  const int64_t nb = (len + pc.chunk - 1) / pc.chunk;
-  w0 += kvh * nb;
-  const int64_t w1 = w0 + nb - 1;
+  const BatchLens bl = batch_lens(p);
+  const Pieces pc = piece_plan(p, bl);
+  int first, nb;
+  segment_pieces(p, bl, pc.chunk, b, kvh, first, nb);
+  int64_t lo, len;
+  seq_range(p, b, lo, len);
+  const int64_t w0 = first, w1 = (int64_t)first + nb - 1;
   const int D = p.D, G = p.G;
   const int j = r / G, hg = r % G;
   uint16_t* out = (uint16_t*)p.out + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D;
@@ -957,6 +1030,8 @@ static int validate_attn(const sv_attn_desc* d) {
     // a 64-key tile of separate 512-wide keys and values (128 KB) cannot be double-buffered in LDS
     if (d->head_dim == 512 && !d->k_is_v) return SV_ERR_UNSUPPORTED;
     if ((d->n_heads_q / d->n_heads_kv) * d->n_q > 64) return SV_ERR_UNSUPPORTED;
+    // the work split handles up to 256 sequences with key counts below 2^31
+    if (d->batch > 64 * kPlanGroups || d->cache_capacity > INT32_MAX - 4096) return SV_ERR_UNSUPPORTED;
   } else if (d->dtype == SV_F32) {
     if (d->head_dim > 512) return SV_ERR_UNSUPPORTED;
     if (d->cache_capacity > kF32MaxKeys) return SV_ERR_UNSUPPORTED;
@@ -1065,7 +1140,9 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
     }
     if (rc != SV_OK) return rc;
     if (!attn_fuse_merge(d->head_dim, MT))
-      hipLaunchKernelGGL(attn_merge_kernel, dim3(pl.M, d->batch * d->n_heads_kv), dim3(d->head_dim / 4), 0, s, p);
+      // (at least one full wave: the piece plan works across 64 lanes)
+      hipLaunchKernelGGL(attn_merge_kernel, dim3(pl.M, d->batch * d->n_heads_kv),
+                         dim3(d->head_dim / 4 > 64 ? d->head_dim / 4 : 64), 0, s, p);
   } else {
     hipLaunchKernelGGL(rope_append_kernel<float>, dim3(d->batch * d->n_q, heads), dim3(rope_threads), 0, s, p);
     hipLaunchKernelGGL(attn_f32_kernel, dim3(d->n_heads_q, d->n_q, d->batch), dim3(256), 0, s, p);

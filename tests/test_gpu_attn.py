@@ -113,6 +113,18 @@ def test_head_dims_and_row_tiles(D):
 
 
 @gpu
+def test_many_sequences_work_split():
+    """70 sequences x 4 KV heads: more segments than compute units (one piece per
+    segment), sequences past the first 64 lanes of the work-split scan, empty and
+    short sequences."""
+    ly = configs.AttnLayer("local", 8, 4, 128, 40, 128, 1e4, False)
+    lens = inputs.randint((70,), 0, 300, 13, "lens", "cpu").tolist()
+    lens[3] = 0
+    lens[66] = 0
+    run_case(ly, 70, 3, lens, 310, 13, std=0.2, tag="many-seqs")
+
+
+@gpu
 def test_read_only_drafter_queries():
     ly = configs.global_layer(16, 4, 512)
     run_case(ly, 3, 1, [50, 0, 777], 800, 5, append=False, qoff=0, tag="read-only-global")
