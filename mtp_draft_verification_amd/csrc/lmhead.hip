@@ -145,6 +145,59 @@ __device__ __forceinline__ void select_push4(RowState& st, const RowCtx& c, cons
   }
 }
 
+// fold a wave tile's 4 T logits of one row, ids vbase + 16 t + i (t < T, i < 4),
+// into its state (GREEDY / SAMPLE): one block maximum and one exponential per logit
+// for the log-partition, the block's own top two merged into the running pair, all
+// without divergent branches.
+template <int MODE, int T>
+__device__ __forceinline__ void select_fold(RowState& st, const RowCtx& c, const f32x4_t (&z)[T], int vbase) {
+  if (!c.valid) return;
+  float m = z[0][0];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, z[t][i]);
+  const float mb = m * kLog2e;
+  float e = 0.f;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(fmaf(z[t][i], kLog2e, -mb));
+  st.l.merge(m, e);
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (vbase + t * 16 + i == c.draft) st.dl = z[t][i];
+  // the block's own best two (ids ascending, so a strictly larger value wins), then
+  // one merge into the running pair
+  float b1 = z[0][0], b2 = kNegInf;
+  int j1 = vbase, j2 = -1;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = (t == 0 ? 1 : 0); i < 4; ++i) {
+      const float v = z[t][i];
+      const int id = vbase + t * 16 + i;
+      const bool g1 = v > b1, g2 = v > b2;
+      const float nb2 = g1 ? b1 : (g2 ? v : b2);
+      const int nj2 = g1 ? j1 : (g2 ? id : j2);
+      b1 = g1 ? v : b1;
+      j1 = g1 ? id : j1;
+      b2 = nb2;
+      j2 = nj2;
+    }
+  st.a.merge(b1, j1, b2, j2);
+  if (MODE == GM_SAMPLE && c.bonus) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const f32x4_t u = *(const f32x4_t*)(c.u + vbase + t * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.s.push(z[t][i] + gumbel(u[i]), vbase + t * 16 + i);
+    }
+  }
+}
+
 __device__ __forceinline__ void state_merge(RowState& a, const RowState& b) {
   a.a.merge(b.a.v1, b.a.i1, b.a.v2, b.a.i2);
   a.l.merge(b.l.m, b.l.s);
@@ -382,6 +435,16 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
       if (lane == 0) __hip_atomic_store(p.cnt + b * 4 + wave, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // accumulator lane: x row (mt*16 + lr), features row0 + 16 t + 4 lg + {0..3}
+    if constexpr (SELECT && MODE != GM_RESIDUAL) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t zt[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) zt[t] = acc[t][mt];
+        select_fold<MODE, T>(st[mt], ctx[mt], zt, row0 + lg * 4);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int v0 = row0 + t * 16 + lg * 4;

@@ -62,10 +62,9 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
 // "a beats b" in the order (value descending, id ascending); id < 0 is an empty slot.
+// Written with bitwise operators and selects below, so that lanes never diverge.
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
-  if (bi < 0) return ai >= 0;
-  if (ai < 0) return false;
-  return av > bv || (av == bv && ai < bi);
+  return (ai >= 0) & ((bi < 0) | (av > bv) | ((av == bv) & (ai < bi)));
 }
 
 // running best-two under `beats`
@@ -74,18 +73,27 @@ struct Top2 {
   int i1, i2;
   __device__ __forceinline__ void init() { v1 = v2 = kNegInf; i1 = i2 = -1; }
   __device__ __forceinline__ void push(float v, int i) {
-    if (beats(v, i, v1, i1)) { v2 = v1; i2 = i1; v1 = v; i1 = i; }
-    else if (beats(v, i, v2, i2)) { v2 = v; i2 = i; }
+    const bool w1 = beats(v, i, v1, i1), w2 = beats(v, i, v2, i2);
+    const float nv2 = w1 ? v1 : (w2 ? v : v2);
+    const int ni2 = w1 ? i1 : (w2 ? i : i2);
+    v1 = w1 ? v : v1;
+    i1 = w1 ? i : i1;
+    v2 = nv2;
+    i2 = ni2;
   }
-  // merge another running pair whose ids are disjoint from ours
+  // merge another running pair whose ids are disjoint from ours: if the other's best
+  // wins, the second is the better of our best and the other's second; otherwise
+  // the other's best may still displace our second
   __device__ __forceinline__ void merge(float ov1, int oi1, float ov2, int oi2) {
-    if (beats(ov1, oi1, v1, i1)) {
-      // other's best wins; second is the better of our best and other's second
-      if (beats(v1, i1, ov2, oi2)) { v2 = v1; i2 = i1; } else { v2 = ov2; i2 = oi2; }
-      v1 = ov1; i1 = oi1;
-    } else {
-      if (beats(ov1, oi1, v2, i2)) { v2 = ov1; i2 = oi1; }
-    }
+    const bool a = beats(ov1, oi1, v1, i1);
+    const bool b = beats(v1, i1, ov2, oi2);
+    const bool c = beats(ov1, oi1, v2, i2);
+    const float nv2 = a ? (b ? v1 : ov2) : (c ? ov1 : v2);
+    const int ni2 = a ? (b ? i1 : oi2) : (c ? oi1 : i2);
+    v1 = a ? ov1 : v1;
+    i1 = a ? oi1 : i1;
+    v2 = nv2;
+    i2 = ni2;
   }
   __device__ __forceinline__ void merge_xor(int m) {
     float ov1 = shfl_xor_f(v1, m), ov2 = shfl_xor_f(v2, m);
