@@ -674,6 +674,7 @@ static constexpr int kSelT = 4;      // W tiles per wave in the LM head
 // two otherwise (half the x re-reads per weight byte)
 static int lin_tiles(const sv_linear_desc& d) {
   if (d.epilogue == SV_EPI_GEGLU) return 2;  // a wave's two tiles pair gate and up rows
+  if (d.epilogue == SV_EPI_SPLIT_F32) return 2;  // no fixup: fewer x re-reads per weight byte win
   return (int64_t)d.in_features * d.out_features < ((int64_t)24 << 20) ? 1 : 2;
 }
 

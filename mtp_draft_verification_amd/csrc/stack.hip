@@ -102,32 +102,34 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int dim, float eps, const 
   }
 }
 
-// Residual add of K-split partial products, then RMSNorm: one workgroup per row.
-// The slices are summed in slice order (a = ((p0 + p1) + p2) + ...), then added to
-// the row, which is written back; kSplitBatch slices are loaded at a time, all of
-// their loads in flight together.
-constexpr int kSplitBatch = 4;
+// Residual add of K-split partial products, then RMSNorm: one workgroup of 1024
+// threads per row, at most kAddVec 4-element vectors of the row per thread, so that
+// a row and kSplitBatch slices of it are in flight at once.  The slices are summed
+// in slice order (a = ((p0 + p1) + p2) + ...), then added to the row, which is
+// written back.
+constexpr int kAddThreads = 1024, kAddVec = 2, kSplitBatch = 8;
 
-__global__ __launch_bounds__(256) void add_rmsnorm_kernel(int rows, int dim, float eps, float* x, const float* parts,
-                                                          int splits, const float* gain, void* y, int bf16) {
-  __shared__ float s_red[4];
+__global__ __launch_bounds__(kAddThreads) void add_rmsnorm_kernel(int rows, int dim, float eps, float* x,
+                                                                  const float* parts, int splits,
+                                                                  const float* gain, void* y, int bf16) {
+  __shared__ float s_red[kAddThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n4 = dim / 4;
   float* xr = x + (int64_t)r * dim;
-  f32x4_t v[kNormVec], a[kNormVec];
+  f32x4_t v[kAddVec], a[kAddVec];
 #pragma unroll
-  for (int k = 0; k < kNormVec; ++k) {
-    const int i = tid + 256 * k;
+  for (int k = 0; k < kAddVec; ++k) {
+    const int i = tid + kAddThreads * k;
     v[k] = i < n4 ? *(const f32x4_t*)(xr + 4 * i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     a[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
-    f32x4_t pv[kSplitBatch][kNormVec];
+    f32x4_t pv[kSplitBatch][kAddVec];
 #pragma unroll
     for (int j = 0; j < kSplitBatch; ++j)
 #pragma unroll
-      for (int k = 0; k < kNormVec; ++k) {
-        const int i = tid + 256 * k;
+      for (int k = 0; k < kAddVec; ++k) {
+        const int i = tid + kAddThreads * k;
         pv[j][k] = (s0 + j < splits && i < n4)
                        ? *(const f32x4_t*)(parts + ((int64_t)(s0 + j) * rows + r) * dim + 4 * i)
                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -136,12 +138,12 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(int rows, int dim, flo
     for (int j = 0; j < kSplitBatch; ++j)
       if (s0 + j < splits)
 #pragma unroll
-        for (int k = 0; k < kNormVec; ++k)
+        for (int k = 0; k < kAddVec; ++k)
           a[k] = f32x4_t{a[k][0] + pv[j][k][0], a[k][1] + pv[j][k][1], a[k][2] + pv[j][k][2], a[k][3] + pv[j][k][3]};
   }
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kNormVec; ++k) {
+  for (int k = 0; k < kAddVec; ++k) {
     if (splits > 0) v[k] = f32x4_t{v[k][0] + a[k][0], v[k][1] + a[k][1], v[k][2] + a[k][2], v[k][3] + a[k][3]};
     ss = fmaf(v[k][0], v[k][0], fmaf(v[k][1], v[k][1], fmaf(v[k][2], v[k][2], fmaf(v[k][3], v[k][3], ss))));
   }
@@ -149,11 +151,13 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(int rows, int dim, flo
   for (int m = 32; m > 0; m >>= 1) ss += shfl_xor_f(ss, m);
   if ((tid & 63) == 0) s_red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kAddThreads / 64; w += 2) tot += s_red[w] + s_red[w + 1];
   const float inv = 1.f / sqrtf(tot / (float)dim + eps);
 #pragma unroll
-  for (int k = 0; k < kNormVec; ++k) {
-    const int i = tid + 256 * k;
+  for (int k = 0; k < kAddVec; ++k) {
+    const int i = tid + kAddThreads * k;
     if (i >= n4) break;
     if (splits > 0) *(f32x4_t*)(xr + 4 * i) = v[k];
     f32x4_t o = f32x4_t{v[k][0] * inv, v[k][1] * inv, v[k][2] * inv, v[k][3] * inv};
@@ -218,11 +222,11 @@ extern "C" int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, co
   if (out_dtype != SV_F32 && out_dtype != SV_BF16) return SV_ERR_ARG;
   if (!parts) splits = 0;
   if (dim % 4 || (((uintptr_t)x | (uintptr_t)parts | (uintptr_t)gain | (uintptr_t)y) & 15)) return SV_ERR_ARG;
-  if (dim > 256 * 4 * kNormVec) return SV_ERR_UNSUPPORTED;
+  if (dim > kAddThreads * 4 * kAddVec) return SV_ERR_UNSUPPORTED;
   int rc = check_device();
   if (rc != SV_OK) return rc;
-  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(rows), dim3(256), 0, (hipStream_t)stream, rows, dim, eps, x, parts,
-                     splits, gain, y, out_dtype == SV_BF16 ? 1 : 0);
+  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(rows), dim3(kAddThreads), 0, (hipStream_t)stream, rows, dim, eps, x,
+                     parts, splits, gain, y, out_dtype == SV_BF16 ? 1 : 0);
   return launch_status();
 }
 
