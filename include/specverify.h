@@ -81,7 +81,12 @@ typedef struct {
                             drafter's cross-attention), k_new/v_new must be NULL */
   int32_t q_pos_offset;  /* must be 0 when append == 1 */
   sv_dtype dtype;        /* of q, k_new, v_new, caches and out */
-  int32_t reserved;      /* must be 0 */
+  int32_t in_splits;     /* 0: q, k_new, v_new hold values in dtype.  S > 0 (bf16 only):
+                            they hold fp32 K-split partial products as SV_EPI_SPLIT_F32
+                            writes them -- S slices, slice s of q at q + s*B*n_q*q_row_stride
+                            elements (of k_new / v_new with kv_row_stride) -- and the value
+                            used is bf16(sum of the slices in slice order), exactly what
+                            an SV_EPI_STORE projection with the same slices would store */
   double rope_base;      /* theta_i = rope_base^(-2i/rope_dims) */
   float softmax_scale;   /* multiplies q.k before the softmax (1/sqrt(D)) */
   float reserved_f;      /* must be 0 */

@@ -36,7 +36,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_heads_q", ctypes.c_int32),
                 ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rope_dims", ctypes.c_int32), ("k_is_v", ctypes.c_int32), ("append", ctypes.c_int32),
-                ("q_pos_offset", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_pos_offset", ctypes.c_int32), ("dtype", ctypes.c_int32), ("in_splits", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
                 ("reserved_f", ctypes.c_float), ("cache_capacity", ctypes.c_int64),
                 ("q_row_stride", ctypes.c_int64), ("kv_row_stride", ctypes.c_int64)]

@@ -35,6 +35,7 @@ struct AttnParams {
   float* part_acc;        // workspace: [slots][M][D]
   float* part_ml;         // workspace: [slots][M][2]  (m in log2 units, l)
   int32_t* seg_cnt;       // workspace: [B * Hkv] arrivals of a segment's pieces
+  int in_splits;          // > 0: q, k_new, v_new are fp32 K-split partial products
   int part_acc_bytes, part_ml_bytes;
   int32_t* dev_status;
   int64_t cap;
@@ -244,11 +245,30 @@ __device__ __forceinline__ void st_elem(void* base, int64_t i, double v) {
   else ((float*)base)[i] = f;
 }
 
+// An input tensor (q, k_new or v_new): values in T, or (splits > 0, bf16 only) the
+// fp32 K-split partial products of a projection, `splits` slices `slice` elements
+// apart, summed in slice order and rounded to bf16 -- the value the projection would
+// have stored.
+struct InView {
+  const void* base;
+  int64_t slice;
+  int splits;
+};
+
+template <typename T>
+__device__ __forceinline__ double ld_in(const InView& v, int64_t i) {
+  if (v.splits == 0) return ld_elem<T>(v.base, i);
+  const float* f = (const float*)v.base + i;
+  float a = 0.f;
+  for (int s = 0; s < v.splits; ++s) a += f[(int64_t)s * v.slice];
+  return (double)bf16_to_f32((uint16_t)f32_to_bf16_bits(a));
+}
+
 // rotate-half RoPE of element d of a head vector x (pre-rotation values) at position pos
 template <typename T>
-__device__ __forceinline__ double rope_elem(const void* src, int64_t head_off, int d, int r,
+__device__ __forceinline__ double rope_elem(const InView& src, int64_t head_off, int d, int r,
                                             double log2_base, double pos) {
-  const double x = ld_elem<T>(src, head_off + d);
+  const double x = ld_in<T>(src, head_off + d);
   if (d >= r) return x;
   const int half = r >> 1;
   const int i = d < half ? d : d - half;
@@ -260,8 +280,8 @@ __device__ __forceinline__ double rope_elem(const void* src, int64_t head_off, i
   float snf, csf;
   sincosf(red, &snf, &csf);
   const double sn = snf, cs = csf;
-  if (d < half) return x * cs - ld_elem<T>(src, head_off + d + half) * sn;
-  return x * cs + ld_elem<T>(src, head_off + d - half) * sn;
+  if (d < half) return x * cs - ld_in<T>(src, head_off + d + half) * sn;
+  return x * cs + ld_in<T>(src, head_off + d - half) * sn;
 }
 
 // one workgroup per (sequence, row, head); one thread per element of the head
@@ -293,17 +313,20 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
   if (hs < p.Hq) {
     const int64_t src = ((int64_t)b * p.nq + j) * p.q_stride + (int64_t)hs * D;
     const int64_t dst = (((int64_t)b * p.nq + j) * p.Hq + hs) * D;
-    st_elem<T>(p.q_rot, dst + d, rope_elem<T>(p.q, src, d, p.rope_dims, p.log2_base, pos));
+    const InView qv{p.q, (int64_t)p.B * p.nq * p.q_stride, p.in_splits};
+    st_elem<T>(p.q_rot, dst + d, rope_elem<T>(qv, src, d, p.rope_dims, p.log2_base, pos));
   } else if (hs < p.Hq + p.Hkv) {
     const int h = hs - p.Hq;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-    st_elem<T>(p.k_cache, dst + d, rope_elem<T>(p.k_new, src, d, p.rope_dims, p.log2_base, pos));
+    const InView kv{p.k_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits};
+    st_elem<T>(p.k_cache, dst + d, rope_elem<T>(kv, src, d, p.rope_dims, p.log2_base, pos));
   } else {
     const int h = hs - p.Hq - p.Hkv;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-    st_elem<T>(p.v_cache, dst + d, ld_elem<T>(p.v_new, src + d));
+    const InView vv{p.v_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits};
+    st_elem<T>(p.v_cache, dst + d, ld_in<T>(vv, src + d));
   }
 }
 
@@ -1018,7 +1041,8 @@ static int validate_attn(const sv_attn_desc* d) {
   if (d->k_is_v != 0 && d->k_is_v != 1) return SV_ERR_ARG;
   if (d->append != 0 && d->append != 1) return SV_ERR_ARG;
   if (d->append && d->q_pos_offset != 0) return SV_ERR_ARG;
-  if (d->reserved != 0 || d->reserved_f != 0.f) return SV_ERR_ARG;
+  if (d->in_splits < 0 || d->reserved_f != 0.f) return SV_ERR_ARG;
+  if (d->in_splits > 0 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->cache_capacity <= 0) return SV_ERR_ARG;
   if (d->q_row_stride < 0 || d->kv_row_stride < 0) return SV_ERR_ARG;
   if (d->q_row_stride && d->q_row_stride < (int64_t)d->n_heads_q * d->head_dim) return SV_ERR_ARG;
@@ -1123,6 +1147,7 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
   p.k_is_v = d->k_is_v;
   p.nwg = device_cus();
   p.min_chunk = 64;
+  p.in_splits = d->in_splits;
 
   hipStream_t s = (hipStream_t)stream;
   const int heads = d->n_heads_q + (d->append ? d->n_heads_kv * (d->k_is_v ? 1 : 2) : 0);

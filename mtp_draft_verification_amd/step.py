@@ -5,7 +5,8 @@ over the rows [last committed token, d_1..d_k] of every sequence (main_model.ver
 then accept_longest_prefix.  Here that forward is, per layer,
 
     a = rmsnorm(x)                 sv_rmsnorm      (x: fp32 residual stream)
-    qkv = a Wqkv^T                 sv_linear       (q, k, v in one projection)
+    qkv = a Wqkv^T                 sv_linear       (q, k, v in one projection; K-split
+                                   partials, summed and rounded by the attention call)
     o = attn(q, k, v; cache)       sv_verify_attn  (appends the k+1 new rows)
     x += o Wo^T                    sv_linear (SV_EPI_SPLIT_F32: the K-split partial
                                    products), added into x by the next norm
@@ -32,11 +33,12 @@ from . import _lib as L
 
 
 def attn_desc(layer, batch: int, n_q: int, cap: int, dtype: str, append: bool = True,
-              q_pos_offset: int = 0, q_row_stride: int = 0, kv_row_stride: int = 0) -> L.AttnDesc:
+              q_pos_offset: int = 0, q_row_stride: int = 0, kv_row_stride: int = 0,
+              in_splits: int = 0) -> L.AttnDesc:
     return L.AttnDesc(batch=batch, n_q=n_q, n_heads_q=layer.n_heads_q, n_heads_kv=layer.n_heads_kv,
                       head_dim=layer.head_dim, window=layer.window, rope_dims=layer.rope_dims,
                       k_is_v=int(layer.k_is_v), append=int(append), q_pos_offset=q_pos_offset,
-                      dtype=L.SV_BF16 if dtype == "bf16" else L.SV_F32, reserved=0,
+                      dtype=L.SV_BF16 if dtype == "bf16" else L.SV_F32, in_splits=int(in_splits),
                       rope_base=float(layer.rope_base), softmax_scale=float(layer.scale), reserved_f=0.0,
                       cache_capacity=int(cap), q_row_stride=int(q_row_stride),
                       kv_row_stride=int(kv_row_stride))
@@ -94,6 +96,16 @@ class VerifyStack:
                         if S > 0:
                             self.split[K] = S
         self.parts = z(max(self.split.values()) * R * d, dtype=torch.float32) if self.split else None
+        # the q/k/v projection also leaves K-split partials, summed by the attention's rope/append
+        self.qkv_split = []
+        for ly in cfg.layers:
+            S = 0
+            if self.bf16:
+                S = max(0, L.sv_linear_splits(L.LinearDesc(rows=R, in_features=d, out_features=self._nout(ly),
+                                                           dtype=self.dt, epilogue=L.SV_EPI_SPLIT_F32)))
+            self.qkv_split.append(S)
+        nout_max = max(self._nout(ly) for ly in cfg.layers)
+        self.qkv_parts = (z(max(self.qkv_split) * R * nout_max, dtype=torch.float32) if max(self.qkv_split) else None)
         ws = max(L.sv_verify_attn_workspace(attn_desc(ly, B, k + 1, self.cap, cfg.dtype)) for ly in cfg.layers)
         self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.lin_ws = torch.zeros(max([self._lin_ws(*s) for s in self._lin_shapes()] + [256]),
@@ -108,8 +120,8 @@ class VerifyStack:
         self.acc_desc = L.AcceptDesc(batch=B, k=k, vocab=cfg.vocab, mode=L.SV_SELECT_GREEDY)
         self.timers = None   # {call name: [(start event, end event), ...]} when timing
         self.attn_descs = [
-            attn_desc(ly, B, k + 1, self.cap, cfg.dtype,
-                      q_row_stride=self._nout(ly), kv_row_stride=self._nout(ly)) for ly in cfg.layers]
+            attn_desc(ly, B, k + 1, self.cap, cfg.dtype, q_row_stride=self._nout(ly), kv_row_stride=self._nout(ly),
+                      in_splits=S) for ly, S in zip(cfg.layers, self.qkv_split)]
 
     def _ev(self, name: str, stream):
         """Record a HIP event pair around a named call when that call is being timed."""
@@ -191,9 +203,14 @@ class VerifyStack:
             nq_f = ly.n_heads_q * ly.head_dim
             nk_f = ly.n_heads_kv * ly.head_dim
             nout = self._nout(ly)
-            qkv = self.qkv.view(-1)[:self.R * nout].view(self.R, nout)
+            S = self.qkv_split[i]
             t = self._ev(f"L{i}.qkv", stream)
-            self._linear(a, lw["wqkv"], qkv, L.SV_EPI_STORE, stream)
+            if S:
+                qkv = self.qkv_parts.view(-1)[:S * self.R * nout].view(S * self.R, nout)
+                self._linear(a, lw["wqkv"], qkv, L.SV_EPI_SPLIT_F32, stream)
+            else:
+                qkv = self.qkv.view(-1)[:self.R * nout].view(self.R, nout)
+                self._linear(a, lw["wqkv"], qkv, L.SV_EPI_STORE, stream)
             self._end(t)
             esz = qkv.element_size()
             base = qkv.data_ptr()

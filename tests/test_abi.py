@@ -35,7 +35,7 @@ def test_version_and_status_strings():
 
 def _desc(**kw):
     base = dict(batch=2, n_q=5, n_heads_q=16, n_heads_kv=8, head_dim=256, window=1024, rope_dims=256,
-                k_is_v=0, append=1, q_pos_offset=0, dtype=L.SV_BF16, reserved=0, rope_base=1e4,
+                k_is_v=0, append=1, q_pos_offset=0, dtype=L.SV_BF16, in_splits=0, rope_base=1e4,
                 softmax_scale=1 / 16, reserved_f=0.0, cache_capacity=5000, q_row_stride=0, kv_row_stride=0)
     base.update(kw)
     return L.AttnDesc(**base)
@@ -55,7 +55,7 @@ def test_attention_descriptor_validation():
     assert L.sv_verify_attn_workspace(_desc()) > 0
     bad = [dict(batch=0), dict(n_q=0), dict(n_heads_q=12, n_heads_kv=8), dict(head_dim=200, rope_dims=200),
            dict(rope_dims=300), dict(rope_dims=7), dict(window=-1), dict(k_is_v=2), dict(append=1, q_pos_offset=3),
-           dict(reserved=1), dict(cache_capacity=0), dict(softmax_scale=0.0), dict(dtype=7),
+           dict(in_splits=-1), dict(in_splits=2, dtype=L.SV_F32), dict(cache_capacity=0), dict(softmax_scale=0.0), dict(dtype=7),
            dict(q_row_stride=100), dict(rope_base=0.5)]
     for kw in bad:
         assert call(_desc(**kw)) in (L.SV_ERR_ARG, L.SV_ERR_UNSUPPORTED), kw

@@ -125,6 +125,48 @@ def test_many_sequences_work_split():
 
 
 @gpu
+@pytest.mark.parametrize("kind", ["local", "global"])
+def test_split_partial_inputs(kind):
+    """q, k_new, v_new given as fp32 K-split partials (in_splits = S): the call must
+    give bit for bit what it gives for bf16(sum of the slices in slice order) -- the
+    inputs a storing projection would have written."""
+    dev = need_gpu()
+    ly = configs.local_layer(16, 8, 256, 64) if kind == "local" else configs.global_layer(16, 4, 512)
+    B, nq, S, cap = 3, 5, 4, 700
+    Hq, Hkv, D = ly.n_heads_q, ly.n_heads_kv, ly.head_dim
+    nout = Hq * D + (1 if ly.k_is_v else 2) * Hkv * D
+    say(f"[attn split inputs] {kind} S={S}")
+    parts = inputs.normal((S, B * nq, nout), 0.5, 14, "parts", dev, "f32")
+    acc = parts[0].clone()
+    for s in range(1, S):
+        acc = acc + parts[s]
+    qkv = acc.to(torch.bfloat16)
+    lens = torch.tensor([10, 300, 640], dtype=torch.int32, device=dev)
+    kc0 = inputs.normal((B, Hkv, cap, D), 1.0, 14, "kc", dev)
+    vc0 = None if ly.k_is_v else inputs.normal((B, Hkv, cap, D), 1.0, 14, "vc", dev)
+    outs, caches = [], []
+    for split in (False, True):
+        src = parts if split else qkv
+        base = src.data_ptr()
+        esz = src.element_size()
+        kp = base + Hq * D * esz
+        vp = None if ly.k_is_v else base + (Hq + Hkv) * D * esz
+        kc = kc0.clone()
+        vc = None if vc0 is None else vc0.clone()
+        out = torch.full((B, nq, Hq, D), float("nan"), dtype=torch.bfloat16, device=dev)
+        desc = attn_desc(ly, B, nq, cap, "bf16", q_row_stride=nout, kv_row_stride=nout, in_splits=S if split else 0)
+        ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
+        L.sv_verify_attn(desc, base, kp, vp, kc, vc, lens, out, ws, None)
+        outs.append(out)
+        caches.append((kc, vc))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(caches[0][0], caches[1][0])
+    if vc0 is not None:
+        assert torch.equal(caches[0][1], caches[1][1])
+
+
+@gpu
 def test_read_only_drafter_queries():
     ly = configs.global_layer(16, 4, 512)
     run_case(ly, 3, 1, [50, 0, 777], 800, 5, append=False, qoff=0, tag="read-only-global")
