@@ -171,6 +171,9 @@ typedef struct {
   int32_t vocab;         /* V, a multiple of 64 */
   sv_select_mode mode;
   sv_dtype dtype;        /* of hidden and w */
+  int32_t out_stride;    /* GREEDY / SAMPLE: when out_tokens is not NULL, the argmax of
+                            row r goes to out_tokens[r * out_stride] (0 means 1): how a
+                            drafter writes its token for step i into drafts[b][i] */
 } sv_lmhead_desc;
 
 /* Workspace of sv_lmhead_select, 0 for an invalid descriptor.  bf16: arrival
@@ -194,7 +197,8 @@ size_t sv_lmhead_workspace(const sv_lmhead_desc* desc);
  *   stats      [B*(k+1)]     GREEDY/SAMPLE: written; RESIDUAL: read (lse of the row)
  *   acc        [B]           RESIDUAL: read (residual_row, hidden_row, n_accepted) and
  *                            next_token / draw_margin written; else NULL
- *   out_tokens [B, k+1]      RESIDUAL: out_tokens[b][n_b] = the drawn token; else NULL
+ *   out_tokens [B, k+1]      RESIDUAL: out_tokens[b][n_b] = the drawn token; GREEDY /
+ *                            SAMPLE: optional, top1_id of row r at r * out_stride
  *
  * RESIDUAL draws, for each sequence with residual_row >= 0,
  * argmax over {v : r_v > 0} of log r_v + G(u_v), r_v = exp(z_v - lse) - q_v,
@@ -255,6 +259,22 @@ int sv_embed(int32_t rows, int32_t d_model, int32_t vocab, sv_dtype dtype,
  * gain [dim] fp32, y [rows, dim] in `out_dtype`. */
 int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float* gain,
                void* y, sv_dtype out_dtype, void* stream);
+
+/* Input stage of a drafter step ("Gemma 4 拆解", section 4.2: the drafter takes the
+ * target's last-layer activation and the embedding of the last token, concatenated,
+ * and projects them down to its own width).  For each sequence b:
+ *   h = hidden[hidden_row[b * row_stride]]           (bf16 [rows_h, d_main])
+ *   e = emb_scale * emb[tokens[b * tok_stride]]       (bf16 [vocab, d_draft])
+ *   cat[b] = [bf16(rmsnorm(h)), bf16(rmsnorm(e))]     (bf16 [batch, d_main + d_draft])
+ *   x[b] = 0                                          (fp32 [batch, d_draft]: the drafter's
+ *                                                     residual stream, which the down
+ *                                                     projection then adds into)
+ * rmsnorm has unit gain.  An out-of-range row or token sets SV_DEV_BAD_TOKEN and
+ * gives that part zeros. */
+int sv_draft_input(int32_t batch, int32_t d_main, int32_t d_draft, float eps, const void* hidden,
+                   int32_t rows_h, const int32_t* hidden_row, int32_t row_stride, const void* emb,
+                   int32_t vocab, const int32_t* tokens, int32_t tok_stride, float emb_scale, void* cat,
+                   float* x, int32_t* dev_status, void* stream);
 
 /* Residual add and RMSNorm in one launch (a pre-norm block's "x = x + f(...);
  * y = rmsnorm(x)"): x (fp32 [rows, dim], updated in place) += the sum of the

@@ -23,7 +23,8 @@ SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
-           "sv_add_rmsnorm", "sv_linear_splits", "sv_linear_workspace", "sv_linear", "sv_geglu")
+           "sv_add_rmsnorm", "sv_draft_input", "sv_linear_splits", "sv_linear_workspace", "sv_linear",
+           "sv_geglu")
 
 
 class SvError(RuntimeError):
@@ -44,7 +45,8 @@ class AttnDesc(ctypes.Structure):
 
 class LMHeadDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("k", ctypes.c_int32), ("d_model", ctypes.c_int32),
-                ("vocab", ctypes.c_int32), ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("vocab", ctypes.c_int32), ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_stride", ctypes.c_int32)]
 
 
 class AcceptDesc(ctypes.Structure):
@@ -99,6 +101,8 @@ def load():
     L.sv_rmsnorm.argtypes = [i32, i32, f32, P, P, P, ctypes.c_int, P]
     L.sv_add_rmsnorm.restype = ctypes.c_int
     L.sv_add_rmsnorm.argtypes = [i32, i32, f32, P, P, i32, P, P, ctypes.c_int, P]
+    L.sv_draft_input.restype = ctypes.c_int
+    L.sv_draft_input.argtypes = [i32, i32, i32, f32, P, i32, P, i32, P, i32, P, i32, f32, P, P, P, P]
     L.sv_linear_splits.restype = i32
     L.sv_linear_splits.argtypes = [ctypes.POINTER(LinearDesc)]
     L.sv_linear_workspace.restype = sz
@@ -200,6 +204,15 @@ def sv_add_rmsnorm(rows: int, dim: int, eps: float, x, parts, splits: int, gain,
     rc = load().sv_add_rmsnorm(rows, dim, float(eps), _ptr(x), _ptr(parts), int(splits), _ptr(gain), _ptr(y),
                                out_dtype, _stream(stream))
     _check("sv_add_rmsnorm", rc)
+
+
+def sv_draft_input(batch: int, d_main: int, d_draft: int, eps: float, hidden, rows_h: int, hidden_row,
+                   row_stride: int, emb, vocab: int, tokens, tok_stride: int, emb_scale: float, cat, x,
+                   dev_status=None, stream=None) -> None:
+    rc = load().sv_draft_input(batch, d_main, d_draft, float(eps), _ptr(hidden), rows_h, _ptr(hidden_row),
+                               row_stride, _ptr(emb), vocab, _ptr(tokens), tok_stride, float(emb_scale),
+                               _ptr(cat), _ptr(x), _ptr(dev_status), _stream(stream))
+    _check("sv_draft_input", rc)
 
 
 def sv_linear_splits(desc: LinearDesc) -> int:

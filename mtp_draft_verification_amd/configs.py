@@ -135,3 +135,34 @@ def scaled_stack(base: StackConfig = STACK, *, name: str = "stack_small", d_mode
     return StackConfig(name=name, d_model=d_model, vocab=vocab, layers=layers, d_ff=d_ff,
                        norm=base.norm, eps=base.eps, dtype=base.dtype, batch=batch, k=k,
                        ctx=ctx, steps=steps, draft_match=base.draft_match)
+
+
+@dataclass(frozen=True)
+class DrafterConfig:
+    """An MTP drafter that cross-attends the target's caches ("Gemma 4 拆解"
+    (marsggbo), section 4.2): its own embedder and width d_draft, the target's last
+    activation and the token embedding concatenated and projected down, blocks of
+    cross-attention into the target's last local (or global) layer cache plus a
+    GeGLU MLP, a projection back up to d_model, and the target's unembedding.
+    `blocks` names, per drafter block, the kind of target layer whose cache it
+    reads; its query heads match that layer (same heads, head dim, RoPE)."""
+    name: str
+    d_draft: int
+    d_ff: int
+    blocks: tuple = ("local", "local", "local", "global")
+    eps: float = 1e-6
+
+    def target_layers(self, target: StackConfig) -> list:
+        """Index of the target layer each block attends: the last of its kind."""
+        last = {}
+        for i, ly in enumerate(target.layers):
+            last[ly.kind] = i
+        return [last[kind] for kind in self.blocks]
+
+
+# 3 local + 1 global blocks at the larger drafter width the pages give (1024)
+DRAFTER = DrafterConfig(name="drafter_1024", d_draft=1024, d_ff=4096)
+
+
+def scaled_drafter(name: str = "drafter_small", d_draft=128, d_ff=256) -> DrafterConfig:
+    return DrafterConfig(name=name, d_draft=d_draft, d_ff=d_ff)

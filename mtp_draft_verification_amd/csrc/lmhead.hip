@@ -48,6 +48,7 @@ struct GemmParams {
   // stream-K
   float* part;           // [grid][2][rows][NB] partial sums
   int splits;            // GM_SPLIT: K slices per block (grid = nblk * splits)
+  int out_stride;        // GREEDY / SAMPLE: top-1 ids to out_tokens[r * out_stride]
   int32_t* cnt;          // [nblk][4] arrival counters, zero between calls
 };
 
@@ -647,6 +648,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(GemmParams p, int npa
     o.sample_s1 = MODE == GM_SAMPLE ? f.s.v1 : 0.f;
     o.sample_s2 = MODE == GM_SAMPLE ? f.s.v2 : 0.f;
     stats[r] = o;
+    if (out_tokens) out_tokens[(int64_t)r * p.out_stride] = f.a.i1;
   }
 }
 
@@ -733,6 +735,7 @@ static int validate_lmhead(const sv_lmhead_desc* d) {
   if (d->batch <= 0 || d->k < 0 || d->d_model <= 0 || d->vocab <= 0) return SV_ERR_ARG;
   if (d->mode != SV_SELECT_GREEDY && d->mode != SV_SELECT_SAMPLE && d->mode != SV_SELECT_RESIDUAL) return SV_ERR_ARG;
   if (d->mode == SV_SELECT_RESIDUAL && d->k == 0) return SV_ERR_ARG;
+  if (d->out_stride < 0) return SV_ERR_ARG;
   if (d->vocab % 64) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
     if (d->d_model % 32) return SV_ERR_ARG;
@@ -823,6 +826,7 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
   p.q_rows = q_rows;
   p.stats_in = stats;
   p.acc = acc;
+  p.out_stride = d->out_stride > 0 ? d->out_stride : 1;
   const int nrows = sel_rows(*d);
   hipStream_t s = (hipStream_t)stream;
   int grid;

@@ -172,6 +172,51 @@ __global__ __launch_bounds__(kAddThreads) void add_rmsnorm_kernel(int rows, int 
   }
 }
 
+// Drafter input stage: one workgroup per sequence; the gathered hidden row and the
+// scaled embedding row are each RMS-normalised (sums of squares in fp32, one
+// wavefront-shuffle and one LDS exchange per part) and written side by side in bf16.
+__device__ __forceinline__ float block_sum_256(float v, float* s_red) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += shfl_xor_f(v, m);
+  __syncthreads();  // s_red free from any previous use
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+}
+
+__global__ __launch_bounds__(256) void draft_input_kernel(int d_main, int d_draft, float eps, const uint16_t* hidden,
+                                                          int rows_h, const int32_t* hidden_row, int row_stride,
+                                                          const uint16_t* emb, int vocab, const int32_t* tokens,
+                                                          int tok_stride, float emb_scale, uint16_t* cat, float* x,
+                                                          int32_t* dev_status) {
+  __shared__ float s_red[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int dc = d_main + d_draft;
+  const int hr = hidden_row[(int64_t)b * row_stride];
+  const int tok = tokens[(int64_t)b * tok_stride];
+  const bool hok = hr >= 0 && hr < rows_h, tok_ok = tok >= 0 && tok < vocab;
+  if (tid == 0 && !(hok && tok_ok)) set_status(dev_status, SV_DEV_BAD_TOKEN);
+  const uint16_t* hrow = hidden + (int64_t)(hok ? hr : 0) * d_main;
+  const uint16_t* erow = emb + (int64_t)(tok_ok ? tok : 0) * d_draft;
+  float ss = 0.f;
+  for (int i = tid; i < d_main; i += 256) {
+    const float v = bf16_to_f32(hrow[i]);
+    ss = fmaf(v, v, ss);
+  }
+  const float hinv = hok ? 1.f / sqrtf(block_sum_256(ss, s_red) / (float)d_main + eps) : 0.f;
+  ss = 0.f;
+  for (int i = tid; i < d_draft; i += 256) {
+    const float v = emb_scale * bf16_to_f32(erow[i]);
+    ss = fmaf(v, v, ss);
+  }
+  const float einv = tok_ok ? 1.f / sqrtf(block_sum_256(ss, s_red) / (float)d_draft + eps) : 0.f;
+  uint16_t* crow = cat + (int64_t)b * dc;
+  for (int i = tid; i < d_main; i += 256) crow[i] = (uint16_t)f32_to_bf16_bits(bf16_to_f32(hrow[i]) * hinv);
+  for (int i = tid; i < d_draft; i += 256)
+    crow[d_main + i] = (uint16_t)f32_to_bf16_bits(emb_scale * bf16_to_f32(erow[i]) * einv);
+  for (int i = tid; i < d_draft; i += 256) x[(int64_t)b * d_draft + i] = 0.f;
+}
+
 __global__ __launch_bounds__(256) void geglu_kernel(int rows, int dff, int bf16, const void* gu, void* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)rows * dff) return;
@@ -227,6 +272,20 @@ extern "C" int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, co
   if (rc != SV_OK) return rc;
   hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(rows), dim3(kAddThreads), 0, (hipStream_t)stream, rows, dim, eps, x,
                      parts, splits, gain, y, out_dtype == SV_BF16 ? 1 : 0);
+  return launch_status();
+}
+
+extern "C" int sv_draft_input(int32_t batch, int32_t d_main, int32_t d_draft, float eps, const void* hidden,
+                              int32_t rows_h, const int32_t* hidden_row, int32_t row_stride, const void* emb,
+                              int32_t vocab, const int32_t* tokens, int32_t tok_stride, float emb_scale, void* cat,
+                              float* x, int32_t* dev_status, void* stream) {
+  if (batch <= 0 || d_main <= 0 || d_draft <= 0 || rows_h <= 0 || vocab <= 0 || !(eps >= 0.f)) return SV_ERR_ARG;
+  if (!hidden || !hidden_row || !emb || !tokens || !cat || !x || row_stride < 0 || tok_stride < 0) return SV_ERR_ARG;
+  int rc = check_device();
+  if (rc != SV_OK) return rc;
+  hipLaunchKernelGGL(draft_input_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, d_main, d_draft, eps,
+                     (const uint16_t*)hidden, rows_h, hidden_row, row_stride, (const uint16_t*)emb, vocab, tokens,
+                     tok_stride, emb_scale, (uint16_t*)cat, x, dev_status);
   return launch_status();
 }
 

@@ -144,6 +144,27 @@ def stack_weights(cfg, seed: int = 0, device="cpu") -> dict:
     return W
 
 
+def drafter_weights(target, dcfg, seed: int = 0, device="cpu") -> dict:
+    """Random-init drafter weights, N(0, 1/fan_in) entries: its embedder E [vocab,
+    d_draft]; w_down [d_draft, d_model + d_draft] over [target activation, token
+    embedding]; per block wq [Hq*D, d_draft], wo [d_draft, Hq*D] (the heads of the
+    target layer it reads), wgu [2*d_ff, d_draft] (gate rows, then up rows), wd
+    [d_draft, d_ff]; w_up [d_model, d_draft]."""
+    dt = target.dtype
+    d, dd, dff = target.d_model, dcfg.d_draft, dcfg.d_ff
+    W = {"E": normal((target.vocab, dd), dd ** -0.5, seed, "D.E", device, dt),
+         "w_down": normal((dd, d + dd), (d + dd) ** -0.5, seed, "D.w_down", device, dt),
+         "w_up": normal((d, dd), dd ** -0.5, seed, "D.w_up", device, dt), "blocks": []}
+    for j, ti in enumerate(dcfg.target_layers(target)):
+        ly = target.layers[ti]
+        nq = ly.n_heads_q * ly.head_dim
+        W["blocks"].append({"wq": normal((nq, dd), dd ** -0.5, seed, f"D{j}.wq", device, dt),
+                            "wo": normal((dd, nq), nq ** -0.5, seed, f"D{j}.wo", device, dt),
+                            "wgu": normal((2 * dff, dd), dd ** -0.5, seed, f"D{j}.wgu", device, dt),
+                            "wd": normal((dd, dff), dff ** -0.5, seed, f"D{j}.wd", device, dt)})
+    return W
+
+
 def stack_caches(cfg, seed: int = 0, device="cpu", capacity: int | None = None,
                  fill_from: int | None = None) -> list:
     """Per layer: k [B, Hkv, cap, D] (and v unless K = V), rows [fill_lo, ctx) ~ N(0,1),

@@ -120,6 +120,69 @@ class OracleModel:
         return res
 
 
+class OracleDrafter:
+    """One step of an MTP drafter that cross-attends the target's caches ("Gemma 4
+    拆解" (marsggbo), section 4.2, MTPDrafter.draft_one_step and draft):
+
+        cat = [norm(h_prev), norm(sqrt(d_draft) E_d[token])]   (the target's last
+              activation and the drafter's own token embedding)
+        x   = cat W_down^T
+        per block (reading the cache of the target's last local or global layer,
+              committed rows only, as a query at position L + i):
+            a = norm(x); q = a Wq^T; x += attn(q; cache) Wo^T
+            m = norm(x); x += (gelu_tanh(m Wg^T) * (m Wu^T)) Wd^T
+        h   = norm(x) W_up^T           (back to the target's width)
+        z   = h E^T with the target's tied unembedding; the draft is argmax z, and
+              h is the next step's h_prev.
+
+    The pages' listing leaves norms and RoPE out; here every norm is an RMSNorm of
+    unit gain and the queries get the RoPE of the target layer they read.  Values
+    the GPU path stores are rounded to bf16 at the same points as in OracleModel."""
+
+    def __init__(self, target_cfg, dcfg, target_E: np.ndarray, weights: dict):
+        self.t = target_cfg
+        self.d = dcfg
+        self.E = target_E
+        self.W = weights
+        last = {}
+        for i, ly in enumerate(target_cfg.layers):
+            last[ly.kind] = i
+        self.reads = [last[kind] for kind in dcfg.blocks]
+
+    def _r(self, x):
+        return bf16_round(x)
+
+    def step(self, state: dict, h_prev: np.ndarray, tokens, i: int) -> tuple[np.ndarray, np.ndarray]:
+        """h_prev [B, d_model] (values as stored), tokens [B]; the step's query sits at
+        position L_b + i.  Returns (h [B, d_model] as stored, logits [B, V] fp64)."""
+        t, dc = self.t, self.d
+        eps = dc.eps
+        tokens = np.asarray(tokens, dtype=np.int64)
+        B = tokens.shape[0]
+        e = np.sqrt(float(dc.d_draft)) * _to_f64(self.W["E"][tokens])
+        cat = np.concatenate([self._r(rmsnorm(np.asarray(h_prev, dtype=np.float64), eps)),
+                              self._r(rmsnorm(e, eps))], axis=1)
+        x = linear(cat, self.W["w_down"])
+        for blk, ti in zip(self.W["blocks"], self.reads):
+            ly = t.layers[ti]
+            cache = state["caches"][ti]
+            a = self._r(rmsnorm(x, eps))
+            q = self._r(linear(a, blk["wq"])).reshape(B, 1, ly.n_heads_q, ly.head_dim)
+            o = verify_attn(q=q.astype(np.float32), k_new=None, v_new=None, k_cache=cache["k"],
+                            v_cache=cache["v"], cache_len=state["L"], window=ly.window,
+                            rope_dims=ly.rope_dims, rope_base=ly.rope_base, scale=ly.scale,
+                            k_is_v=ly.k_is_v, append=False, q_pos_offset=i, round_bf16=True)
+            o = self._r(o.reshape(B, ly.n_heads_q * ly.head_dim))
+            x = x + linear(o, blk["wo"])
+            m = self._r(rmsnorm(x, eps))
+            g = self._r(linear(m, blk["wgu"][:dc.d_ff]))
+            u = self._r(linear(m, blk["wgu"][dc.d_ff:]))
+            f = self._r(geglu(g, u))
+            x = x + linear(f, blk["wd"])
+        h = self._r(linear(self._r(rmsnorm(x, eps)), self.W["w_up"]))
+        return h, lmhead(h, self.E)
+
+
 def new_state(caches: list, cache_len) -> dict:
     """caches: per layer {"k": [B, Hkv, cap, D] float32, "v": same or None}."""
     return {"caches": caches, "L": np.asarray(cache_len, dtype=np.int32).copy()}

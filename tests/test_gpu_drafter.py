@@ -1,0 +1,96 @@
+"""GPU parity of the drafter step (sv_draft_input, K-split projections, read-only
+verify attention into the target's caches, greedy unembedding) against the oracle.
+
+Each draft step is checked with matched inputs: the oracle takes the GPU's h_prev
+and token of that step, so a near-tie that sends the two sides to different tokens
+does not carry into later steps.  Per step the row statistics must agree within
+2e-2 (as in the stack test) and the drafted token must equal the oracle's argmax
+wherever its top-2 margin exceeds 1e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import model as om
+import mtp_draft_verification_amd._lib as L
+from mtp_draft_verification_amd import configs, inputs
+from mtp_draft_verification_amd.drafter import Drafter
+from gpu_util import gpu, host, need_gpu, say
+
+ATOL = 2e-2
+MARGIN = 1e-2
+
+
+def host_caches(caches):
+    return [{"k": inputs.host_f32(c["k"]), "v": None if c["v"] is None else inputs.host_f32(c["v"])} for c in caches]
+
+
+def drafter_case(tcfg, dcfg, lens, k, seed):
+    dev = need_gpu()
+    B = tcfg.batch
+    say(f"[drafter] d={tcfg.d_model} d_draft={dcfg.d_draft} B={B} k={k} lens={lens}")
+    cap = max(lens) + 16
+    tw = inputs.stack_weights(tcfg, seed, dev)
+    dw = inputs.drafter_weights(tcfg, dcfg, seed, dev)
+    caches = inputs.stack_caches(dataclass_replace(tcfg, ctx=max(lens)), seed, dev, capacity=cap)
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    R = B * (tcfg.k + 1)
+    h_verify = inputs.normal((R, tcfg.d_model), 1.0, seed, "h_verify", dev)
+    acc = torch.zeros(B, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+    hr = inputs.randint((B,), 0, tcfg.k, seed, "nacc", "cpu").numpy()
+    for b in range(B):
+        acc[b, 7] = b * (tcfg.k + 1) + int(hr[b])
+    acc[:, 1] = inputs.randint((B,), 0, tcfg.vocab - 1, seed, "next_tok", dev)
+    drafts = torch.full((B, k), -1, dtype=torch.int32, device=dev)
+    dr = Drafter(tcfg, dcfg, tw["E"], dw, caches, cl, dev)
+
+    o = om.OracleDrafter(tcfg, dcfg, inputs.bf16_bits(tw["E"]),
+                         {"E": inputs.bf16_bits(dw["E"]), "w_down": inputs.bf16_bits(dw["w_down"]),
+                          "w_up": inputs.bf16_bits(dw["w_up"]),
+                          "blocks": [{kk: inputs.bf16_bits(v) for kk, v in bw.items()} for bw in dw["blocks"]]})
+    st = om.new_state(host_caches(caches), lens)
+    h_prev = host(h_verify)[[b * (tcfg.k + 1) + int(hr[b]) for b in range(B)]]
+    tok = acc[:, 1].cpu().numpy()
+    checked = 0
+    for i in range(k):
+        if i == 0:
+            dr.step(0, k, h_verify, R, acc.data_ptr() + 28, L.ACCEPT_OUT_WORDS, acc.data_ptr() + 4,
+                    L.ACCEPT_OUT_WORDS, drafts)
+        else:
+            dr.step(i, k, dr.h, B, dr.rows, 1, drafts.data_ptr() + 4 * (i - 1), k, drafts)
+        torch.cuda.synchronize()
+        hq, z = o.step(st, h_prev, tok, i)
+        gs = L.decode_row_stats(dr.stats)
+        zmax = np.abs(z).max()
+        for b in range(B):
+            ref = oracle.row_stats(z[b])
+            assert abs(float(gs[b]["lse"]) - ref["lse"]) < ATOL * max(1.0, zmax), (i, b)
+            assert abs(float(gs[b]["top1"]) - ref["top1"]) < ATOL * max(1.0, zmax), (i, b)
+            if ref["top1"] - ref["top2"] > MARGIN:
+                assert int(drafts[b, i].item()) == ref["top1_id"], (i, b)
+                checked += 1
+        # the next step of both sides starts from the GPU's state
+        h_prev = host(dr.h)
+        tok = drafts[:, i].cpu().numpy()
+    assert int(dr.dev_status.item()) == 0
+    say(f"[drafter] ok: {checked} of {B * k} drafted tokens decided by a clear margin and equal")
+
+
+def dataclass_replace(cfg, **kw):
+    import dataclasses
+    return dataclasses.replace(cfg, **kw)
+
+
+@gpu
+def test_drafter_small():
+    tcfg = configs.scaled_stack(name="drafter_target", d_model=256, vocab=4096, d_ff=512, batch=3, k=3,
+                                window=64, local_heads=(4, 2, 128), global_heads=(4, 1, 256))
+    drafter_case(tcfg, configs.scaled_drafter(d_draft=128, d_ff=256), [200, 37, 500], 3, 1)
+
+
+@gpu
+def test_drafter_wide_window_and_ragged():
+    # window longer than some sequences, a 64-row batch of draft rows is not needed: B = 5
+    tcfg = configs.scaled_stack(name="drafter_target2", d_model=192, vocab=2048, d_ff=256, batch=5, k=2,
+                                window=300, local_heads=(4, 1, 128), global_heads=(8, 2, 256))
+    drafter_case(tcfg, configs.scaled_drafter(d_draft=256, d_ff=512), [5, 290, 301, 1000, 64], 2, 2)
