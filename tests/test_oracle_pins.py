@@ -473,3 +473,75 @@ def test_rmsnorm_unit_rms_and_gelu_identities():
     u = np.array([3.0, 2.0, 0.5])
     np.testing.assert_allclose(oracle.geglu(g, u), [0.0, 2 * oracle.gelu_tanh(1.0),
                                                     0.5 * oracle.gelu_tanh(-2.0)])
+
+
+# ---------------------------------------------------------------------------
+# drafter step
+# ---------------------------------------------------------------------------
+
+def test_drafter_step_closed_form():
+    """A drafter step where the attention has a closed form: the local blocks read a
+    cache of two committed rows with a window of 3, so the query at position L + 1
+    sees only row 1 (its output is v_1) and the query at L + 2 sees no row (zero
+    output); the global block's two rows are equal keys (output: that key, the value
+    on a K = V layer).  Everything else is written out with numpy in fp64; the oracle
+    rounds stored values to bf16, hence the tolerance.  A swapped concatenation, a
+    block reading the wrong layer's cache, a dropped residual or a wrong query
+    position changes the logits by far more."""
+    rng = np.random.default_rng(7)
+    loc = configs.AttnLayer("local", 4, 2, 8, 3, 8, 1e4, False)
+    glo = configs.AttnLayer("global", 4, 1, 16, 0, 4, 1e6, True)
+    tcfg = configs.StackConfig(name="pin", d_model=16, vocab=32, layers=(loc, loc, glo), d_ff=0, norm=True,
+                               eps=1e-6, dtype="bf16", batch=2, k=2, ctx=2)
+    dcfg = configs.DrafterConfig(name="pin_drafter", d_draft=8, d_ff=8, blocks=("local", "global"))
+    bf = lambda *s, sc=1.0: oracle.bf16_round(rng.standard_normal(s) * sc)
+    bits = lambda a: (np.asarray(a, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    d, dd, dff, V, B = 16, 8, 8, 32, 2
+    E = bf(V, d, sc=0.3)
+    W = {"E": bf(V, dd, sc=0.5), "w_down": bf(dd, d + dd, sc=0.2), "w_up": bf(d, dd, sc=0.3),
+         "blocks": [{"wq": bf(loc.n_heads_q * loc.head_dim, dd), "wo": bf(dd, 32, sc=0.2),
+                     "wgu": bf(2 * dff, dd, sc=0.3), "wd": bf(dd, dff, sc=0.3)},
+                    {"wq": bf(glo.n_heads_q * glo.head_dim, dd), "wo": bf(dd, 64, sc=0.2),
+                     "wgu": bf(2 * dff, dd, sc=0.3), "wd": bf(dd, dff, sc=0.3)}]}
+    cap = 4
+    caches = []
+    for ly in tcfg.layers:
+        kc = bf(B, ly.n_heads_kv, cap, ly.head_dim).astype(np.float32)
+        vc = None if ly.k_is_v else bf(B, ly.n_heads_kv, cap, ly.head_dim).astype(np.float32)
+        if ly.k_is_v:
+            kc[:, :, 1] = kc[:, :, 0]
+        caches.append({"k": kc, "v": vc})
+    o = om.OracleDrafter(tcfg, dcfg, bits(E), {"E": bits(W["E"]), "w_down": bits(W["w_down"]),
+                                               "w_up": bits(W["w_up"]),
+                                               "blocks": [{k: bits(v) for k, v in b.items()} for b in W["blocks"]]})
+    h_prev = bf(B, d)
+    tok = np.array([3, 30])
+
+    def rms(v):
+        return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + 1e-6)
+
+    def gelu(v):
+        return 0.5 * v * (1 + np.tanh(np.sqrt(2 / np.pi) * (v + 0.044715 * v ** 3)))
+
+    for i in (1, 2):
+        st = om.new_state([{k: (None if a is None else a.copy()) for k, a in c.items()} for c in caches], [2, 2])
+        h, z = o.step(st, h_prev, tok, i)
+        x = np.concatenate([rms(h_prev), rms(np.sqrt(dd) * W["E"][tok])], axis=1) @ W["w_down"].T
+        # blocks read the last local layer (index 1) and the global layer (index 2)
+        for blk, ly, c in ((W["blocks"][0], loc, caches[1]), (W["blocks"][1], glo, caches[2])):
+            G = ly.n_heads_q // ly.n_heads_kv
+            if ly.k_is_v:
+                src = c["k"][:, :, 0]                       # both rows equal
+            else:
+                src = c["v"][:, :, 1] if i == 1 else np.zeros_like(c["v"][:, :, 0])
+            att = np.repeat(src, G, axis=1).reshape(B, -1).astype(np.float64)
+            x = x + att @ blk["wo"].T
+            m = rms(x)
+            x = x + (gelu(m @ blk["wgu"][:dff].T) * (m @ blk["wgu"][dff:].T)) @ blk["wd"].T
+        href = rms(x) @ W["w_up"].T
+        zref = href @ E.T
+        assert np.abs(h - href).max() < 0.03 * np.abs(href).max(), i
+        assert np.abs(z - zref).max() < 0.03 * np.abs(zref).max(), i
+        # the same check fails if the step reads the other query position
+        _, z_wrong = o.step(st, h_prev, tok, 0)
+        assert np.abs(z_wrong - zref).max() > 0.1 * np.abs(zref).max()
