@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for profilers: no sweep, no oracle")
+    ap.add_argument("--no-drafter", action="store_true", help="skip the drafter measurement")
     ap.add_argument("--only", default=None,
                     help="time calls of the step in isolation at the workload's shapes; comma-separated "
                          f"from {', '.join(ONLY_CALLS)}")
@@ -318,6 +319,60 @@ def run_workload(cfg, W, steps, warmup, seed, dev, time_calls=None):
     return res
 
 
+def bench_drafter(cfg, W, caches, lens, dev, cycles: int = 10, warmup: int = 2) -> dict:
+    """Time k draft steps of the MTP drafter (3 local + 1 global cross-attention
+    blocks of width 1024) over the same caches, after the verify replay: reported
+    apart from the verify step.  Inputs: synthetic final hidden states and accept
+    records (row b(k+1), a random next token); random-init drafter weights."""
+    import numpy as np
+    import torch
+
+    from mtp_draft_verification_amd import _lib as L
+    from mtp_draft_verification_amd import configs, inputs
+    from mtp_draft_verification_amd.drafter import Drafter
+
+    dcfg = configs.DRAFTER
+    B, k = cfg.batch, cfg.k
+    log(f"drafter: d_draft={dcfg.d_draft}, blocks {','.join(dcfg.blocks)}, k={k}")
+    dw = inputs.drafter_weights(cfg, dcfg, 1, dev)
+    cl = torch.tensor(np.asarray(lens, dtype=np.int64).round().astype(np.int32), device=dev)
+    dr = Drafter(cfg, dcfg, W["E"], dw, caches, cl, dev)
+    R = B * (k + 1)
+    h = inputs.normal((R, cfg.d_model), 1.0, 1, "h_verify", dev)
+    acc = torch.zeros(B, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+    acc[:, 7] = torch.arange(B, dtype=torch.int32, device=dev) * (k + 1)
+    acc[:, 1] = inputs.randint((B,), 0, cfg.vocab - 1, 1, "next_tok", dev)
+    drafts = torch.zeros(B, k, dtype=torch.int32, device=dev)
+    for _ in range(warmup):
+        dr.draft(k, h, acc, drafts)
+    torch.cuda.synchronize()
+    names = ["draft_input", "unembed"] + [f"D{j}.{c}" for j in range(len(dcfg.blocks)) for c in ("attn", "mlp")]
+    dr.timers = {n: [] for n in names}
+    dr.draft(k, h, acc, drafts)
+    torch.cuda.synchronize()
+    call_us = {n: round(float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3, 2) for n, v in dr.timers.items()}
+    dr.timers = None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(cycles):
+        dr.draft(k, h, acc, drafts)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / cycles
+    assert int(dr.dev_status.item()) == 0
+    gi = dcfg.blocks.index("global")
+    ly = cfg.layers[dr.reads[gi]]
+    g_bytes = float(sum(int(x) for x in cl.tolist())) * ly.n_heads_kv * ly.head_dim * 2
+    g_us = call_us[f"D{gi}.attn"]
+    return {"k": k, "ms_per_k_steps": round(ms, 4), "ms_per_step": round(ms / k, 4),
+            "global_block_read_bytes_per_step": int(g_bytes),
+            "global_block_us": g_us, "global_block_GB/s": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
+            "calls_us": call_us,
+            "config": f"{dcfg.name}: d_draft {dcfg.d_draft}, d_ff {dcfg.d_ff}, blocks {'/'.join(dcfg.blocks)} "
+                      f"reading the target's last local and global caches, batch {B}"}
+
+
 def cpu_baseline(cfg, W, caches, tokens, lens, dev):
     """Time the oracle on a bounded sample: one verify step of sequence 0."""
     import numpy as np
@@ -464,6 +519,11 @@ def main():
             kern[n]["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
             kern[n]["frac"] = round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
 
+    drafter = None
+    if not args.no_drafter and not args.profile:
+        drafter = bench_drafter(cfg, W, main_res["caches"], main_res["first_len"], dev)
+        log(f"drafter: {drafter['ms_per_k_steps']:.3f} ms per {cfg.k} steps")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, W, main_res["caches"], main_res["first_tokens"], main_res["first_len"], dev)
@@ -485,6 +545,7 @@ def main():
         "sweep_tokens_per_s": sweep,
         "mean_accepted": round(main_res["mean_accepted"], 3),
         "kernels": kern,
+        "drafter": drafter,
         "source_digest": source_digest(),
     }
     print(json.dumps(out), flush=True)
