@@ -165,6 +165,32 @@ def drafter_weights(target, dcfg, seed: int = 0, device="cpu") -> dict:
     return W
 
 
+def clustered_unembedding(vocab: int, d: int, n_clusters: int, seed: int = 0, device="cpu",
+                           dtype: str = "bf16", center_std: float | None = None,
+                           spread: float = 0.5) -> dict:
+    """A vocabulary with cluster structure, for the clustered unembedding.
+
+    perm: a seeded random permutation of the token ids (int32 [V]); cluster c owns
+    the V / C consecutive rows [c V / C, (c + 1) V / C) of w_perm, row j holding
+    token perm[j].  Each cluster has a centre drawn N(0, center_std^2) (default
+    1/sqrt(d)); its rows are the centre plus N(0, (spread * center_std)^2) noise.
+    centroids are the centres.  E is the same unembedding in token order
+    (E[perm[j]] = w_perm[j]), for comparisons against the full vocabulary."""
+    assert vocab % n_clusters == 0
+    std = d ** -0.5 if center_std is None else float(center_std)
+    csize = vocab // n_clusters
+    g = generator(seed, "C.perm", device)
+    perm = torch.randperm(vocab, generator=g, device=device).to(torch.int32)
+    centers = normal((n_clusters, d), std, seed, "C.centers", device, "f32")
+    w = normal((vocab, d), std * spread, seed, "C.noise", device, "f32")
+    w.view(n_clusters, csize, d).add_(centers.view(n_clusters, 1, d))
+    w_perm = w.to(torch_dtype(dtype))
+    del w
+    E = torch.empty_like(w_perm)
+    E[perm.long()] = w_perm
+    return {"perm": perm, "w_perm": w_perm, "centroids": centers.to(torch_dtype(dtype)), "E": E}
+
+
 def stack_caches(cfg, seed: int = 0, device="cpu", capacity: int | None = None,
                  fill_from: int | None = None) -> list:
     """Per layer: k [B, Hkv, cap, D] (and v unless K = V), rows [fill_lo, ctx) ~ N(0,1),

@@ -186,6 +186,34 @@ def row_stats(z_row, draft_id: int = -1) -> dict:
                 lse=st.lse, draft_logit=st.draft_logit)
 
 
+def cluster_unembed(h, centroids, w_perm, perm, top: int) -> list:
+    """Clustered unembedding ("Gemma 4 拆解" (marsggbo), section 4.3, cheap_unembed),
+    fp64: cluster scores s = h . centroid, the `top` best clusters (ties: lowest
+    cluster index), the logits h . w of every token of those clusters (w_perm row j
+    is token perm[j]; cluster c owns rows [c V / C, (c + 1) V / C)), and per row the
+    statistics over those candidates only: top-1 / top-2 token ids and logits (ties:
+    lowest token id) and the log-sum-exp.  Returns one dict per row."""
+    h = _f64(h)
+    C = np.asarray(centroids).shape[0]
+    V = np.asarray(perm).shape[0]
+    csize = V // C
+    out = []
+    scores = lmhead(h, centroids)                          # [R, C] = h . centroid_c
+    for r in range(h.shape[0]):
+        order = sorted(range(C), key=lambda c: (-scores[r, c], c))
+        kept = order[:top]
+        rows = np.concatenate([np.arange(c * csize, (c + 1) * csize) for c in kept])
+        z = lmhead(h[r:r + 1], np.asarray(w_perm)[rows])[0]
+        ids = np.asarray(perm)[rows].astype(np.int64)
+        o = sorted(range(rows.size), key=lambda k: (-z[k], ids[k]))
+        m = z.max()
+        out.append(dict(clusters=kept, top1_id=int(ids[o[0]]), top2_id=int(ids[o[1]]) if rows.size > 1 else -1,
+                        top1=float(z[o[0]]), top2=float(z[o[1]]) if rows.size > 1 else float("-inf"),
+                        lse=float(m + np.log(np.exp(z - m).sum())),
+                        scores=scores[r].copy()))
+    return out
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------

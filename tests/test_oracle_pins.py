@@ -269,6 +269,48 @@ def test_lse_is_stable_for_large_logits():
     assert abs(st["lse"] - (1000.0 + math.log1p(math.exp(-1.0)))) < 1e-12
 
 
+def test_cluster_unembed_keeping_every_cluster_is_the_full_vocabulary():
+    # With every cluster kept, the candidates are the whole vocabulary: the result
+    # must be the plain argmax / logsumexp over E in token order, whatever perm is.
+    V, C, d = 96, 8, 32
+    cu = inputs.clustered_unembedding(V, d, C, seed=3, dtype="f32")
+    h = np.random.default_rng(13).standard_normal((4, d))
+    E = cu["E"].double().numpy()
+    res = oracle.cluster_unembed(h, cu["centroids"].numpy(), cu["w_perm"].numpy(), cu["perm"].numpy(), top=C)
+    for r in range(4):
+        z = h[r] @ E.T
+        order = np.argsort(-z, kind="stable")
+        assert (res[r]["top1_id"], res[r]["top2_id"]) == (order[0], order[1])
+        assert abs(res[r]["top1"] - z[order[0]]) < 1e-12 and abs(res[r]["lse"] - special.logsumexp(z)) < 1e-12
+        sc = h[r] @ cu["centroids"].double().numpy().T
+        assert list(res[r]["clusters"]) == list(np.argsort(-sc, kind="stable"))
+
+
+def test_cluster_unembed_restricts_to_kept_clusters_and_maps_ids():
+    # Three clusters of two tokens, centroids on the axes.  h scores cluster 1
+    # highest, but the largest logit overall belongs to a token of cluster 0: with
+    # one cluster kept the answer is cluster 1's best token, named by perm.
+    cent = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0]], dtype=np.float32)
+    w_perm = np.array([[8, 0, 0, 0], [0, 0, 0, 1],        # cluster 0: rows 0, 1
+                       [0, 2, 0, 0], [0, 3, 0, 0],        # cluster 1: rows 2, 3
+                       [0, 0, 1, 0], [0, 0, 0, 0]], dtype=np.float32)
+    perm = np.array([5, 0, 3, 1, 4, 2], dtype=np.int32)
+    h = np.array([[0.5, 1.0, 0.0, 0.0]])
+    r = oracle.cluster_unembed(h, cent, w_perm, perm, top=1)[0]
+    assert r["clusters"] == [1]
+    assert (r["top1_id"], r["top2_id"]) == (1, 3)          # rows 3 then 2
+    assert (r["top1"], r["top2"]) == (3.0, 2.0)
+    assert abs(r["lse"] - special.logsumexp([2.0, 3.0])) < 1e-12
+    r2 = oracle.cluster_unembed(h, cent, w_perm, perm, top=2)[0]
+    assert r2["clusters"] == [1, 0] and (r2["top1_id"], r2["top1"]) == (5, 4.0)
+    # equal cluster scores: the lower cluster index is kept; equal logits: lower token id
+    h = np.array([[1.0, 1.0, 0.0, 0.0]])
+    w_tie = w_perm.copy()
+    w_tie[0] = [0, 0, 0, 0]                                # cluster 0 logits 0, 0
+    r3 = oracle.cluster_unembed(h, cent, w_tie, perm, top=1)[0]
+    assert r3["clusters"] == [0] and (r3["top1_id"], r3["top2_id"]) == (0, 5)
+
+
 # ---------------------------------------------------------------------------
 # greedy acceptance
 # ---------------------------------------------------------------------------
