@@ -209,6 +209,50 @@ int sv_lmhead_select(const sv_lmhead_desc* desc, const void* hidden, const void*
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Clustered unembedding (a drafter's cheap unembed)                         */
+/* ------------------------------------------------------------------------ */
+
+/* "Gemma 4 拆解" (marsggbo), section 4.3 (cheap_unembed): score the rows against
+ * per-cluster centroids, keep the best clusters, and compute real logits only for
+ * the tokens of those clusters (about 4096 instead of the whole vocabulary).  The
+ * vocabulary is cut into n_clusters equal clusters; the unembedding rows are given
+ * grouped by cluster (w_perm row j holds token perm[j]; cluster c is rows
+ * [c * V / n_clusters, (c + 1) * V / n_clusters)). */
+typedef struct {
+  int32_t rows;          /* R hidden rows (<= 64) */
+  int32_t d_model;       /* d, a multiple of 8 */
+  int32_t vocab;         /* V, a multiple of n_clusters */
+  int32_t n_clusters;    /* C <= 4096 */
+  int32_t top_clusters;  /* clusters kept per row, 1 <= top_clusters <= min(C, 64) */
+  sv_dtype dtype;        /* bf16 only */
+} sv_cluster_desc;
+
+/* Workspace of sv_cluster_unembed (cluster scores, kept clusters, per-block select
+ * partials); 0 for an invalid descriptor.  Scratch: nothing survives the call. */
+size_t sv_cluster_unembed_workspace(const sv_cluster_desc* desc);
+
+/*   hidden     [R, d] bf16
+ *   centroids  [C, d] bf16
+ *   w_perm     [V, d] bf16   unembedding rows grouped by cluster
+ *   perm       [V] int32     token id of each w_perm row
+ *   stats      [R]           over the candidate tokens only: top1_id / top2_id (token
+ *                            ids), their logits, lse = log sum over the candidates;
+ *                            draft_logit NaN, sample_id -1
+ *   clusters   [R, top_clusters] int32 (optional): the kept clusters, best first
+ *   out_tokens optional: top1_id of row r at out_tokens[r * out_stride] (0 means 1)
+ * Cluster scores s_c = h . centroid_c are fp32; the kept clusters are the
+ * top_clusters largest (ties: lowest cluster index; a NaN score ranks as -inf);
+ * logits are fp32 dot products; ties between tokens go to the lowest token id.
+ * hidden, centroids and w_perm must be 16-byte aligned.  The caller owns every
+ * buffer; perm entries are copied to the result as they are (not range-checked).
+ * Errors: SV_ERR_ARG (bad descriptor, null or misaligned pointer, negative
+ * out_stride), SV_ERR_UNSUPPORTED (beyond the limits above), SV_ERR_WORKSPACE. */
+int sv_cluster_unembed(const sv_cluster_desc* desc, const void* hidden, const void* centroids,
+                       const void* w_perm, const int32_t* perm, sv_row_stats* stats, int32_t* clusters,
+                       int32_t* out_tokens, int32_t out_stride, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Accept                                                                    */
 /* ------------------------------------------------------------------------ */
 

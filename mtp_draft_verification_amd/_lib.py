@@ -24,7 +24,7 @@ SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
            "sv_add_rmsnorm", "sv_draft_input", "sv_linear_splits", "sv_linear_workspace", "sv_linear",
-           "sv_geglu")
+           "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed")
 
 
 class SvError(RuntimeError):
@@ -57,6 +57,11 @@ class AcceptDesc(ctypes.Structure):
 class LinearDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("in_features", ctypes.c_int32),
                 ("out_features", ctypes.c_int32), ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32)]
+
+
+class ClusterDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("d_model", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_clusters", ctypes.c_int32), ("top_clusters", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 # host views of the device result structs
@@ -111,6 +116,10 @@ def load():
     L.sv_linear.argtypes = [ctypes.POINTER(LinearDesc), P, P, P, P, sz, P]
     L.sv_geglu.restype = ctypes.c_int
     L.sv_geglu.argtypes = [i32, i32, ctypes.c_int, P, P, P]
+    L.sv_cluster_unembed_workspace.restype = sz
+    L.sv_cluster_unembed_workspace.argtypes = [ctypes.POINTER(ClusterDesc)]
+    L.sv_cluster_unembed.restype = ctypes.c_int
+    L.sv_cluster_unembed.argtypes = [ctypes.POINTER(ClusterDesc), P, P, P, P, P, P, P, i32, P, sz, P]
     _lib = L
     return L
 
@@ -233,6 +242,19 @@ def sv_linear(desc: LinearDesc, x, w, y, workspace=None, stream=None) -> None:
 def sv_geglu(rows: int, d_ff: int, dtype: int, gate_up, out, stream=None) -> None:
     rc = load().sv_geglu(rows, d_ff, dtype, _ptr(gate_up), _ptr(out), _stream(stream))
     _check("sv_geglu", rc)
+
+
+def sv_cluster_unembed_workspace(desc: ClusterDesc) -> int:
+    return int(load().sv_cluster_unembed_workspace(ctypes.byref(desc)))
+
+
+def sv_cluster_unembed(desc: ClusterDesc, hidden, centroids, w_perm, perm, stats, clusters, out_tokens,
+                       out_stride: int, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().sv_cluster_unembed(ctypes.byref(desc), _ptr(hidden), _ptr(centroids), _ptr(w_perm), _ptr(perm),
+                                   _ptr(stats), _ptr(clusters), _ptr(out_tokens), int(out_stride),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    _check("sv_cluster_unembed", rc)
 
 
 def decode_row_stats(t) -> np.ndarray:

@@ -555,6 +555,147 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Clustered unembedding: centroid scores, kept clusters, logits of their tokens
+// ---------------------------------------------------------------------------
+struct ClusterParams {
+  const uint16_t* h;     // [R, d]
+  const uint16_t* cent;  // [C, d]
+  const uint16_t* w;     // [V, d] grouped by cluster
+  const int32_t* perm;   // [V] token id of each w row
+  int R, d, V, C, top, csize, sub;
+  float* scores;         // [R, C]
+  int32_t* kept;         // [R, top]
+  SelPart* sel;          // [top * sub][R]
+};
+constexpr int kClusterBlock = 128;  // tokens per logits workgroup
+
+// dot product of a wave's 64 lanes over d (8 elements per lane per 512), all lanes
+// end with the sum
+__device__ __forceinline__ float wave_dot_bf16(const uint16_t* a, const uint16_t* b, int d, int lane) {
+  float acc = 0.f;
+  for (int i = lane * 8; i < d; i += 512) {
+    const uint4 av = *(const uint4*)(a + i), bv = *(const uint4*)(b + i);
+    const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(aw[e]), bf16_lo(bw[e]), acc);
+      acc = fmaf(bf16_hi(aw[e]), bf16_hi(bw[e]), acc);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) acc += shfl_xor_f(acc, m);
+  return acc;
+}
+
+// grid (ceil(C / 16), R): each wave scores four centroids of one row
+__global__ __launch_bounds__(256) void cluster_score_kernel(ClusterParams p) {
+  const int r = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* hr = p.h + (int64_t)r * p.d;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = blockIdx.x * 16 + wave * 4 + q;
+    if (c >= p.C) break;
+    const float s = wave_dot_bf16(hr, p.cent + (int64_t)c * p.d, p.d, lane);
+    if (lane == 0) p.scores[(int64_t)r * p.C + c] = s;
+  }
+}
+
+// grid R: the top largest cluster scores of row r, best first (ties: lowest index)
+__global__ __launch_bounds__(256) void cluster_topk_kernel(ClusterParams p) {
+  __shared__ float s_sc[4096];
+  __shared__ float s_bv[4];
+  __shared__ int s_bi[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // a NaN score ranks lowest (as -inf); NaN then marks a cluster already taken
+  for (int c = tid; c < p.C; c += 256) {
+    const float x = p.scores[(int64_t)r * p.C + c];
+    s_sc[c] = x == x ? x : kNegInf;
+  }
+  __syncthreads();
+  for (int i = 0; i < p.top; ++i) {
+    float bv = kNegInf;
+    int bi = -1;
+    for (int c = tid; c < p.C; c += 256) {
+      const float x = s_sc[c];
+      const int ci = x == x ? c : -1;   // a taken cluster never beats
+      if (beats(x, ci, bv, bi)) { bv = x; bi = ci; }
+    }
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+      const float ov = shfl_xor_f(bv, m);
+      const int oi = shfl_xor_i(bi, m);
+      if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) { s_bv[wave] = bv; s_bi[wave] = bi; }
+    __syncthreads();
+    if (tid == 0) {
+      float v = s_bv[0];
+      int id = s_bi[0];
+      for (int w = 1; w < 4; ++w)
+        if (beats(s_bv[w], s_bi[w], v, id)) { v = s_bv[w]; id = s_bi[w]; }
+      p.kept[(int64_t)r * p.top + i] = id;
+      s_sc[id] = __builtin_nanf("");  // taken: a NaN never beats anything
+    }
+    __syncthreads();
+  }
+}
+
+// grid (top * sub, R): logits of one row for up to kClusterBlock tokens of one kept
+// cluster, folded into a select partial (top-2 by token id, log-sum-exp)
+__global__ __launch_bounds__(256) void cluster_logits_kernel(ClusterParams p) {
+  __shared__ SelPart s_part[4];
+  const int r = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x / p.sub, sb = blockIdx.x - i * p.sub;
+  const int c = p.kept[(int64_t)r * p.top + i];
+  const bool ok = c >= 0 && c < p.C;   // always true: top <= C leaves a cluster to take
+  const int j0 = ok ? c * p.csize + sb * kClusterBlock : 0;
+  const int j1 = ok ? min(j0 + kClusterBlock, (c + 1) * p.csize) : 0;
+  const uint16_t* hr = p.h + (int64_t)r * p.d;
+  RowState st;
+  st.init();
+  for (int j = j0 + wave; j < j1; j += 4) {
+    const float z = wave_dot_bf16(hr, p.w + (int64_t)j * p.d, p.d, lane);
+    if (lane == 0) {
+      st.a.push(z, p.perm[j]);
+      st.l.merge(z, 1.f);
+    }
+  }
+  if (lane == 0) s_part[wave] = to_part(st);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RowState a = from_part(s_part[0]);
+    for (int w = 1; w < 4; ++w) state_merge(a, from_part(s_part[w]));
+    p.sel[(int64_t)blockIdx.x * p.R + r] = to_part(a);
+  }
+}
+
+// grid R, one wave: merge the top * sub partials of row r
+__global__ __launch_bounds__(64) void cluster_merge_kernel(ClusterParams p, sv_row_stats* stats, int32_t* clusters,
+                                                          int32_t* out_tokens, int out_stride) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  RowState a;
+  a.init();
+  for (int k = lane; k < p.top * p.sub; k += 64) state_merge(a, from_part(p.sel[(int64_t)k * p.R + r]));
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) state_merge_xor(a, m);
+  if (clusters)
+    for (int i = lane; i < p.top; i += 64) clusters[(int64_t)r * p.top + i] = p.kept[(int64_t)r * p.top + i];
+  if (lane != 0) return;
+  sv_row_stats o;
+  o.top1_id = a.a.i1;
+  o.top2_id = a.a.i2;
+  o.top1 = a.a.v1;
+  o.top2 = a.a.v2;
+  o.lse = a.l.m + logf(a.l.s);
+  o.draft_logit = __builtin_nanf("");
+  o.sample_id = -1;
+  o.sample_s1 = 0.f;
+  o.sample_s2 = 0.f;
+  stats[r] = o;
+  if (out_tokens) out_tokens[(int64_t)r * out_stride] = a.a.i1;
+}
+
+// ---------------------------------------------------------------------------
 // fp32 LM head (small vocabularies): one thread per vocabulary entry
 // ---------------------------------------------------------------------------
 template <int MODE>
@@ -790,6 +931,73 @@ static int validate_linear(const sv_linear_desc* d) {
 }  // namespace sv
 
 using namespace sv;
+
+static int validate_cluster(const sv_cluster_desc* d) {
+  if (!d) return SV_ERR_ARG;
+  if (d->rows <= 0 || d->d_model <= 0 || d->vocab <= 0 || d->n_clusters <= 0 || d->top_clusters <= 0)
+    return SV_ERR_ARG;
+  if (d->dtype != SV_BF16 || d->d_model % 8 || d->vocab % d->n_clusters) return SV_ERR_ARG;
+  if (d->top_clusters > d->n_clusters) return SV_ERR_ARG;
+  if (d->rows > 64 || d->n_clusters > 4096 || d->top_clusters > 64) return SV_ERR_UNSUPPORTED;
+  return SV_OK;
+}
+
+struct ClusterPlan {
+  int csize, sub;
+  size_t scores, kept, sel, total;
+};
+static ClusterPlan cluster_plan(const sv_cluster_desc& d) {
+  ClusterPlan pl{};
+  pl.csize = d.vocab / d.n_clusters;
+  pl.sub = (pl.csize + kClusterBlock - 1) / kClusterBlock;
+  pl.scores = align_up((size_t)d.rows * d.n_clusters * 4, 256);
+  pl.kept = align_up((size_t)d.rows * d.top_clusters * 4, 256);
+  pl.sel = align_up((size_t)d.top_clusters * pl.sub * d.rows * sizeof(SelPart), 256);
+  pl.total = pl.scores + pl.kept + pl.sel;
+  return pl;
+}
+
+extern "C" size_t sv_cluster_unembed_workspace(const sv_cluster_desc* d) {
+  if (validate_cluster(d) != SV_OK) return 0;
+  return cluster_plan(*d).total;
+}
+
+extern "C" int sv_cluster_unembed(const sv_cluster_desc* d, const void* hidden, const void* centroids,
+                                  const void* w_perm, const int32_t* perm, sv_row_stats* stats, int32_t* clusters,
+                                  int32_t* out_tokens, int32_t out_stride, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  int rc = validate_cluster(d);
+  if (rc != SV_OK) return rc;
+  if (!hidden || !centroids || !w_perm || !perm || !stats || out_stride < 0) return SV_ERR_ARG;
+  if (((uintptr_t)hidden | (uintptr_t)centroids | (uintptr_t)w_perm) & 15) return SV_ERR_ARG;
+  const ClusterPlan pl = cluster_plan(*d);
+  if (!workspace || workspace_bytes < pl.total) return SV_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc != SV_OK) return rc;
+  ClusterParams p{};
+  p.h = (const uint16_t*)hidden;
+  p.cent = (const uint16_t*)centroids;
+  p.w = (const uint16_t*)w_perm;
+  p.perm = perm;
+  p.R = d->rows;
+  p.d = d->d_model;
+  p.V = d->vocab;
+  p.C = d->n_clusters;
+  p.top = d->top_clusters;
+  p.csize = pl.csize;
+  p.sub = pl.sub;
+  char* ws = (char*)workspace;
+  p.scores = (float*)ws;
+  p.kept = (int32_t*)(ws + pl.scores);
+  p.sel = (SelPart*)(ws + pl.scores + pl.kept);
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(cluster_score_kernel, dim3((p.C + 15) / 16, p.R), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(cluster_topk_kernel, dim3(p.R), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(cluster_logits_kernel, dim3(p.top * p.sub, p.R), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(cluster_merge_kernel, dim3(p.R), dim3(64), 0, s, p, stats, clusters, out_tokens,
+                     out_stride > 0 ? out_stride : 1);
+  return launch_status();
+}
 
 extern "C" size_t sv_lmhead_workspace(const sv_lmhead_desc* d) {
   if (validate_lmhead(d) != SV_OK) return 0;

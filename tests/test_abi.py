@@ -100,6 +100,32 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.sv_geglu(4, 128, 5, fake, fake, None) == L.SV_ERR_ARG
 
 
+def test_cluster_unembed_rejects_bad_arguments():
+    lib = L.load()
+    fake = ctypes.c_void_p(4096)
+    base = dict(rows=8, d_model=2560, vocab=262144, n_clusters=2048, top_clusters=32, dtype=L.SV_BF16)
+    assert L.sv_cluster_unembed_workspace(L.ClusterDesc(**base)) > 0
+
+    def call(d, hidden=fake, ws_bytes=1 << 40, out_stride=1):
+        return lib.sv_cluster_unembed(ctypes.byref(d), hidden, fake, fake, fake, fake, None, None, out_stride,
+                                      fake, ws_bytes, None)
+
+    for kw, want in ((dict(rows=0), L.SV_ERR_ARG), (dict(d_model=100), L.SV_ERR_ARG),
+                     (dict(vocab=1000), L.SV_ERR_ARG), (dict(top_clusters=0), L.SV_ERR_ARG),
+                     (dict(n_clusters=16, top_clusters=17, vocab=4096), L.SV_ERR_ARG),
+                     (dict(dtype=L.SV_F32), L.SV_ERR_ARG), (dict(rows=65), L.SV_ERR_UNSUPPORTED),
+                     (dict(n_clusters=8192, vocab=8192 * 32), L.SV_ERR_UNSUPPORTED),
+                     (dict(top_clusters=65), L.SV_ERR_UNSUPPORTED)):
+        d = L.ClusterDesc(**{**base, **kw})
+        assert call(d) == want, kw
+        assert L.sv_cluster_unembed_workspace(d) == 0, kw
+    d = L.ClusterDesc(**base)
+    assert call(d, hidden=ctypes.c_void_p(4096 + 8)) == L.SV_ERR_ARG      # misaligned rows
+    assert call(d, hidden=None) == L.SV_ERR_ARG
+    assert call(d, out_stride=-1) == L.SV_ERR_ARG
+    assert call(d, ws_bytes=L.sv_cluster_unembed_workspace(d) - 1) == L.SV_ERR_WORKSPACE
+
+
 def test_valid_call_without_gpu_reports_device_error():
     import torch
     if torch.cuda.is_available():

@@ -1,0 +1,105 @@
+"""GPU parity of sv_cluster_unembed (the clustered unembedding of a drafter's
+cheap unembed) against the oracle.
+
+The kept clusters must be the oracle's wherever its cluster scores separate them
+by more than SCORE_GAP (order included); the candidate statistics (top-1 / top-2
+logits, log-sum-exp over the candidates) agree within ATOL, and the top-1 token id
+is bit-exact wherever the oracle's top-1 / top-2 margin exceeds MARGIN.  Products
+of bf16 operands are exact in fp32, so the GPU differs from the fp64 oracle by
+fp32 summation order only: about 1e-6 relative on logits of size ~10."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mtp_draft_verification_amd._lib as L
+from mtp_draft_verification_amd import inputs
+from gpu_util import gpu, host, need_gpu, say
+
+ATOL = 2e-3
+MARGIN = 1e-3
+SCORE_GAP = 1e-4
+
+
+def run_cluster(h, cu, top, dev, out_stride=1):
+    R, d = h.shape
+    V, C = cu["w_perm"].shape[0], cu["centroids"].shape[0]
+    desc = L.ClusterDesc(rows=R, d_model=d, vocab=V, n_clusters=C, top_clusters=top, dtype=L.SV_BF16)
+    ws = torch.zeros(L.sv_cluster_unembed_workspace(desc), dtype=torch.uint8, device=dev)
+    stats = torch.full((R, L.ROW_STATS_WORDS), -7, dtype=torch.int32, device=dev)
+    clusters = torch.full((R, top), -7, dtype=torch.int32, device=dev)
+    out_tokens = torch.full((R * out_stride,), -7, dtype=torch.int32, device=dev)
+    L.sv_cluster_unembed(desc, h, cu["centroids"], cu["w_perm"], cu["perm"], stats, clusters, out_tokens,
+                         out_stride, ws)
+    torch.cuda.synchronize()
+    return L.decode_row_stats(stats), clusters.cpu().numpy(), out_tokens.cpu().numpy()
+
+
+def check_rows(h, cu, top, st, kept, toks, out_stride, rows, tag):
+    hb = host(h)[rows]
+    ref = oracle.cluster_unembed(hb, inputs.bf16_bits(cu["centroids"]), inputs.bf16_bits(cu["w_perm"]),
+                                 cu["perm"].cpu().numpy(), top)
+    n_id = 0
+    for r, o in zip(rows, ref):
+        g = st[r]
+        sc = np.sort(o["scores"])[::-1]
+        gaps = -np.diff(sc)
+        boundary_clear = top == len(sc) or gaps[top - 1] > SCORE_GAP
+        if boundary_clear:
+            assert sorted(kept[r]) == sorted(o["clusters"]), (tag, r)
+            for i in range(top - 1):
+                if gaps[i] > SCORE_GAP:
+                    assert kept[r][i] == o["clusters"][i], (tag, r, i)
+        else:                                     # near-tie at the boundary: any valid choice
+            assert len(set(kept[r])) == top and all(o["scores"][c] >= sc[top - 1] - SCORE_GAP for c in kept[r])
+            continue
+        assert abs(float(g["top1"]) - o["top1"]) <= ATOL * max(1.0, abs(o["top1"])), (tag, r, g, o["top1"])
+        if o["top2_id"] >= 0:
+            assert abs(float(g["top2"]) - o["top2"]) <= ATOL * max(1.0, abs(o["top2"])), (tag, r)
+        assert abs(float(g["lse"]) - o["lse"]) <= ATOL * max(1.0, abs(o["lse"])), (tag, r, g["lse"], o["lse"])
+        assert np.isnan(float(g["draft_logit"])) and int(g["sample_id"]) == -1
+        if o["top1"] - o["top2"] > MARGIN:
+            assert int(g["top1_id"]) == o["top1_id"], (tag, r)
+            n_id += 1
+        assert toks[r * out_stride] == int(g["top1_id"])
+    return n_id
+
+
+CASES = [  # R, d, V, C, top
+    (8, 512, 8192, 64, 8),          # 128-token clusters: one logits block each
+    (3, 264, 12800, 64, 5),         # 200-token clusters: a ragged second block; d not a multiple of 512
+    (5, 128, 1600, 16, 16),         # every cluster kept: the whole vocabulary
+    (1, 64, 300, 1, 1),             # one cluster
+    (64, 256, 4096 * 3, 4096, 64),  # largest row count, cluster count and kept count; 3-token clusters
+]
+
+
+@gpu
+@pytest.mark.parametrize("R,d,V,C,top", CASES)
+def test_cluster_unembed_matches_oracle(R, d, V, C, top):
+    dev = need_gpu()
+    say(f"[cluster] R={R} d={d} V={V} C={C} top={top}")
+    cu = inputs.clustered_unembedding(V, d, C, seed=R + C, device=dev)
+    h = inputs.normal((R, d), 1.0, R + C, "h", dev)
+    st, kept, toks = run_cluster(h, cu, top, dev, out_stride=3)
+    n = check_rows(h, cu, top, st, kept, toks, 3, list(range(R)), f"R{R}C{C}")
+    assert n >= R // 2
+    if top == C:                                  # every cluster: the full-vocabulary statistics
+        z = oracle.lmhead(host(h), inputs.bf16_bits(cu["E"]))
+        for r in range(R):
+            full = oracle.row_stats(z[r])
+            assert abs(float(st[r]["lse"]) - full["lse"]) <= ATOL * max(1.0, abs(full["lse"]))
+
+
+@gpu
+def test_cluster_unembed_drafter_size_sampled_rows():
+    # the drafter's vocabulary: 262144 tokens, d 2560, 2048 clusters of 128, 32 kept
+    dev = need_gpu()
+    R, d, V, C, top = 8, 2560, 262144, 2048, 32
+    say(f"[cluster full] R={R} d={d} V={V} C={C} top={top}")
+    cu = inputs.clustered_unembedding(V, d, C, seed=5, device=dev)
+    h = inputs.normal((R, d), 1.0, 5, "h", dev)
+    st, kept, toks = run_cluster(h, cu, top, dev)
+    st2, kept2, _ = run_cluster(h, cu, top, dev)    # repeat: identical bits
+    assert (st.view(np.int32) == st2.view(np.int32)).all() and (kept == kept2).all()
+    assert check_rows(h, cu, top, st, kept, toks, 1, [0, 3, 7], "full") >= 2
