@@ -365,12 +365,43 @@ def bench_drafter(cfg, W, caches, lens, dev, cycles: int = 10, warmup: int = 2) 
     ly = cfg.layers[dr.reads[gi]]
     g_bytes = float(sum(int(x) for x in cl.tolist())) * ly.n_heads_kv * ly.head_dim * 2
     g_us = call_us[f"D{gi}.attn"]
-    return {"k": k, "ms_per_k_steps": round(ms, 4), "ms_per_step": round(ms / k, 4),
-            "global_block_read_bytes_per_step": int(g_bytes),
-            "global_block_us": g_us, "global_block_GB/s": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
-            "calls_us": call_us,
-            "config": f"{dcfg.name}: d_draft {dcfg.d_draft}, d_ff {dcfg.d_ff}, blocks {'/'.join(dcfg.blocks)} "
-                      f"reading the target's last local and global caches, batch {B}"}
+    out = {"k": k, "ms_per_k_steps": round(ms, 4), "ms_per_step": round(ms / k, 4),
+           "global_block_read_bytes_per_step": int(g_bytes),
+           "global_block_us": g_us, "global_block_GB/s": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
+           "calls_us": call_us,
+           "config": f"{dcfg.name}: d_draft {dcfg.d_draft}, d_ff {dcfg.d_ff}, blocks {'/'.join(dcfg.blocks)} "
+                     f"reading the target's last local and global caches, batch {B}"}
+    # the same drafter with the clustered unembedding: 2048 clusters of 128 tokens, the
+    # best 32 kept (4096 candidate rows per sequence)
+    C, top = 2048, 32
+    log(f"drafter: clustered unembedding, {C} clusters, {top} kept")
+    cu = inputs.clusters_of(W["E"], C, top, 1)
+    drc = Drafter(cfg, dcfg, W["E"], dw, caches, cl, dev, clusters=cu)
+    for _ in range(warmup):
+        drc.draft(k, h, acc, drafts)
+    torch.cuda.synchronize()
+    drc.timers = {"unembed": []}
+    drc.draft(k, h, acc, drafts)
+    torch.cuda.synchronize()
+    un_us = round(float(np.median([a.elapsed_time(b) for a, b in drc.timers["unembed"]])) * 1e3, 2)
+    drc.timers = None
+    e0.record()
+    for _ in range(cycles):
+        drc.draft(k, h, acc, drafts)
+    e1.record()
+    torch.cuda.synchronize()
+    msc = e0.elapsed_time(e1) / cycles
+    assert int(drc.dev_status.item()) == 0
+    d = cfg.d_model
+    cand = (cfg.vocab // C) * top
+    cl_bytes = C * d * 2 + B * (cand * d * 2 + cand * 4)
+    out["clustered_unembed"] = {
+        "n_clusters": C, "top_clusters": top, "candidates_per_row": cand,
+        "ms_per_k_steps": round(msc, 4), "ms_per_step": round(msc / k, 4),
+        "unembed_us": un_us, "unembed_read_bytes": int(cl_bytes),
+        "note": "unembed_us includes the final norm and W_up projection, as calls_us.unembed does"}
+    del drc, cu
+    return out
 
 
 def cpu_baseline(cfg, W, caches, tokens, lens, dev):

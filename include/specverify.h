@@ -220,15 +220,17 @@ int sv_lmhead_select(const sv_lmhead_desc* desc, const void* hidden, const void*
  * [c * V / n_clusters, (c + 1) * V / n_clusters)). */
 typedef struct {
   int32_t rows;          /* R hidden rows (<= 64) */
-  int32_t d_model;       /* d, a multiple of 8 */
+  int32_t d_model;       /* d, a multiple of 8, <= 8192 */
   int32_t vocab;         /* V, a multiple of n_clusters */
   int32_t n_clusters;    /* C <= 4096 */
   int32_t top_clusters;  /* clusters kept per row, 1 <= top_clusters <= min(C, 64) */
   sv_dtype dtype;        /* bf16 only */
 } sv_cluster_desc;
 
-/* Workspace of sv_cluster_unembed (cluster scores, kept clusters, per-block select
- * partials); 0 for an invalid descriptor.  Scratch: nothing survives the call. */
+/* Workspace of sv_cluster_unembed (cluster score slices, kept clusters, per-block
+ * select partials, arrival counters); 0 for an invalid descriptor.  Scratch: nothing
+ * needs to survive between calls and nothing needs zeroing; calls that share one
+ * workspace must be ordered (one stream). */
 size_t sv_cluster_unembed_workspace(const sv_cluster_desc* desc);
 
 /*   hidden     [R, d] bf16

@@ -562,15 +562,27 @@ struct ClusterParams {
   const uint16_t* cent;  // [C, d]
   const uint16_t* w;     // [V, d] grouped by cluster
   const int32_t* perm;   // [V] token id of each w row
-  int R, d, V, C, top, csize, sub;
-  float* scores;         // [R, C]
-  int32_t* kept;         // [R, top]
-  SelPart* sel;          // [top * sub][R]
+  int R, d, V, C, top, csize, sub, splits;
+  int cstride;           // scores row stride: C rounded up to a multiple of 4
+  int gs;                // top-k group size in lanes (power of two <= 64)
+  float* scores;         // [splits][R][cstride] fp32 slices, summed in slice order
+  int32_t* kept;         // [R, top] best first
+  float* part;           // [R][top * sub][kClPartWords] per-workgroup select partials
+  int32_t* cnt;          // [R] arrivals of a row's logits workgroups
+  uint32_t part_bytes;
+  sv_row_stats* stats;
+  int32_t* clusters;     // optional copy of kept
+  int32_t* out_tokens;
+  int out_stride;
 };
-constexpr int kClusterBlock = 128;  // tokens per logits workgroup
+constexpr int kClusterBlock = 64;    // tokens per logits workgroup (16 per wave)
+constexpr int kClusterMaxC = 4096;   // clusters per row held by the top-k workgroup
+constexpr int kClusterMaxD = 8192;   // hidden width staged in LDS by the logits kernel
+constexpr int kClPartWords = 8;      // top1 v/i, top2 v/i, lse m/s, 2 spare
+typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
 
-// dot product of a wave's 64 lanes over d (8 elements per lane per 512), all lanes
-// end with the sum
+// grid (ceil(C / 16), R): each wave scores four centroids of one row (used when the
+// centroid count or width does not fit the MFMA projection)
 __device__ __forceinline__ float wave_dot_bf16(const uint16_t* a, const uint16_t* b, int d, int lane) {
   float acc = 0.f;
   for (int i = lane * 8; i < d; i += 512) {
@@ -587,7 +599,6 @@ __device__ __forceinline__ float wave_dot_bf16(const uint16_t* a, const uint16_t
   return acc;
 }
 
-// grid (ceil(C / 16), R): each wave scores four centroids of one row
 __global__ __launch_bounds__(256) void cluster_score_kernel(ClusterParams p) {
   const int r = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint16_t* hr = p.h + (int64_t)r * p.d;
@@ -596,90 +607,250 @@ __global__ __launch_bounds__(256) void cluster_score_kernel(ClusterParams p) {
     const int c = blockIdx.x * 16 + wave * 4 + q;
     if (c >= p.C) break;
     const float s = wave_dot_bf16(hr, p.cent + (int64_t)c * p.d, p.d, lane);
-    if (lane == 0) p.scores[(int64_t)r * p.C + c] = s;
+    if (lane == 0) p.scores[(int64_t)r * p.cstride + c] = s;
   }
 }
 
-// grid R: the top largest cluster scores of row r, best first (ties: lowest index)
-__global__ __launch_bounds__(256) void cluster_topk_kernel(ClusterParams p) {
-  __shared__ float s_sc[4096];
-  __shared__ float s_bv[4];
-  __shared__ int s_bi[4];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // a NaN score ranks lowest (as -inf); NaN then marks a cluster already taken
-  for (int c = tid; c < p.C; c += 256) {
-    const float x = p.scores[(int64_t)r * p.C + c];
-    s_sc[c] = x == x ? x : kNegInf;
+// 64-bit ordering key of (score, cluster): larger key = larger score, then lower
+// index; -0 is folded into +0 first so equal scores compare equal.  0 means none.
+__device__ __forceinline__ uint64_t score_key(float x, int c) {
+  const uint32_t u = __float_as_uint(x + 0.f);
+  const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// grid R, 1024 threads: the top largest cluster scores of row r, best first (ties:
+// lowest index; a NaN score counts as -inf).  No sequential selection: thread t
+// holds scores 4t .. 4t+3, as 64-bit keys ordered like the result.  (1) The scores
+// with the same e = c % 4 in an aligned run of gs lanes form a group (gs a power
+// of two <= 64, the largest giving at least 4 top groups, else 1).  The top-th
+// largest group maximum is a lower bound of the top-th largest score: the group
+// maxima at or above it are that many distinct scores.  (2) Scores at or above the
+// bound are gathered in LDS (a little over `top` on typical inputs, all of them at
+// worst).  (3) Each candidate's rank is the number of candidates with a larger key
+// (eight lanes per candidate); ranks below top are written.  The block also zeroes
+// the row's arrival counter of the logits kernel.
+constexpr int kTopkThreads = 1024;
+__global__ __launch_bounds__(kTopkThreads) void cluster_topk_kernel(ClusterParams p) {
+  constexpr int SB = 16;
+  static_assert(kClusterMaxC == 4 * kTopkThreads, "one float4 per thread");
+  __shared__ uint64_t s_key[kClusterMaxC];   // group maxima, then candidates
+  __shared__ int s_n;
+  __shared__ uint64_t s_lo;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) {
+    s_n = 0;
+    s_lo = 0;
+    p.cnt[r] = 0;
   }
-  __syncthreads();
-  for (int i = 0; i < p.top; ++i) {
-    float bv = kNegInf;
-    int bi = -1;
-    for (int c = tid; c < p.C; c += 256) {
-      const float x = s_sc[c];
-      const int ci = x == x ? c : -1;   // a taken cluster never beats
-      if (beats(x, ci, bv, bi)) { bv = x; bi = ci; }
+  // the slices are added in slice order, SB slices' loads in flight at a time
+  const int c0 = 4 * tid;
+  const bool mine = c0 < p.C;   // scores rows are padded to a multiple of 4
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.splits; s0 += SB) {
+    f32x4_t x[SB];
+#pragma unroll
+    for (int q = 0; q < SB; ++q) {
+      x[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (mine && s0 + q < p.splits) x[q] = *(const f32x4_t*)(p.scores + ((int64_t)(s0 + q) * p.R + r) * p.cstride + c0);
     }
 #pragma unroll
-    for (int m = 32; m > 0; m >>= 1) {
-      const float ov = shfl_xor_f(bv, m);
-      const int oi = shfl_xor_i(bi, m);
-      if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    for (int q = 0; q < SB; ++q) v += x[q];
+  }
+  uint64_t key[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) key[e] = c0 + e >= p.C ? 0ull : score_key(v[e] == v[e] ? v[e] : kNegInf, c0 + e);
+  // (1) group maxima: the lane at the start of each group writes its four
+  uint64_t g[4] = {key[0], key[1], key[2], key[3]};
+  for (int k = p.gs >> 1; k > 0; k >>= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t o = shfl_xor_u64(g[e], k);
+      g[e] = o > g[e] ? o : g[e];
     }
-    if (lane == 0) { s_bv[wave] = bv; s_bi[wave] = bi; }
-    __syncthreads();
-    if (tid == 0) {
-      float v = s_bv[0];
-      int id = s_bi[0];
-      for (int w = 1; w < 4; ++w)
-        if (beats(s_bv[w], s_bi[w], v, id)) { v = s_bv[w]; id = s_bi[w]; }
-      p.kept[(int64_t)r * p.top + i] = id;
-      s_sc[id] = __builtin_nanf("");  // taken: a NaN never beats anything
+  const int ng = 4 * (((p.C + 3) / 4 + p.gs - 1) / p.gs);   // group slots of the threads holding scores
+  if ((lane & (p.gs - 1)) == 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_key[(tid / p.gs) * 4 + e] = g[e];
+  __syncthreads();
+  {
+    // rank of each group maximum, eight lanes per slot; the one ranked top - 1 is
+    // the bound (absent with fewer than top groups: the bound stays 0, take all)
+    const int q = tid & 7;
+    for (int i0 = 0; i0 < ng; i0 += kTopkThreads / 8) {
+      const int i = i0 + (tid >> 3);
+      const uint64_t me = i < ng ? s_key[i] : 0ull;
+      int rank = 0;
+      if (me != 0ull) {
+        int j = q;
+        for (; j + 24 < ng; j += 32) {
+          uint64_t o[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = s_key[j + 8 * u];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rank += o[u] > me ? 1 : 0;
+        }
+        for (; j < ng; j += 8) rank += s_key[j] > me ? 1 : 0;
+      }
+      rank += __shfl_xor(rank, 1, 64);
+      rank += __shfl_xor(rank, 2, 64);
+      rank += __shfl_xor(rank, 4, 64);
+      if (me != 0ull && q == 0 && rank == p.top - 1) s_lo = me;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  const uint64_t lo = s_lo;
+  __syncthreads();   // every lane has read the maxima before they are overwritten
+  // (2) candidates
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool take = key[e] != 0ull && key[e] >= lo;
+    const uint64_t mask = __ballot(take);
+    const int nw = __popcll(mask);
+    int base = 0;
+    if (lane == 0 && nw) base = atomicAdd(&s_n, nw);
+    base = __shfl(base, 0, 64);
+    if (take) s_key[base + __popcll(mask & ((1ull << lane) - 1ull))] = key[e];
+  }
+  __syncthreads();
+  // (3) ranks: eight lanes per candidate; lane q takes candidates q, q + 8, ...
+  const int n = s_n, q = tid & 7;
+  for (int i0 = 0; i0 < n; i0 += kTopkThreads / 8) {
+    const int i = i0 + (tid >> 3);
+    const bool act = i < n;
+    const uint64_t me = act ? s_key[i] : 0ull;
+    int rank = 0;
+    if (act) {
+      int j = q;
+      for (; j + 24 < n; j += 32) {
+        uint64_t o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = s_key[j + 8 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank += o[u] > me ? 1 : 0;
+      }
+      for (; j < n; j += 8) rank += s_key[j] > me ? 1 : 0;
+    }
+    rank += __shfl_xor(rank, 1, 64);
+    rank += __shfl_xor(rank, 2, 64);
+    rank += __shfl_xor(rank, 4, 64);
+    if (act && q == 0 && rank < p.top) {
+      const int ci = (int)(0xFFFFFFFFu - (uint32_t)me);
+      p.kept[(int64_t)r * p.top + rank] = ci;
+      if (p.clusters) p.clusters[(int64_t)r * p.top + rank] = ci;
+    }
   }
 }
 
-// grid (top * sub, R): logits of one row for up to kClusterBlock tokens of one kept
-// cluster, folded into a select partial (top-2 by token id, log-sum-exp)
+__device__ __forceinline__ void fma_bf16x8(float& acc, const uint4& a, const uint4& b) {
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc = fmaf(bf16_lo(aw[e]), bf16_lo(bw[e]), acc);
+    acc = fmaf(bf16_hi(aw[e]), bf16_hi(bw[e]), acc);
+  }
+}
+
+// grid (top * sub, R), 256 threads: logits of row r for up to kClusterBlock tokens of
+// one kept cluster.  The row sits in LDS; each wave takes 16 tokens, four at a time
+// with two 512-wide slices of each in flight (eight 16-byte loads per lane), then
+// folds them into a running top-2 (by token id) and log-sum-exp.  The workgroup's
+// partial goes to the device coherence point; the row's last workgroup to arrive
+// merges all of them in slot order and writes the statistics.
 __global__ __launch_bounds__(256) void cluster_logits_kernel(ClusterParams p) {
-  __shared__ SelPart s_part[4];
-  const int r = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = blockIdx.x / p.sub, sb = blockIdx.x - i * p.sub;
+  __shared__ __attribute__((aligned(16))) uint16_t s_h[kClusterMaxD];
+  __shared__ RowState s_st[4];
+  __shared__ int s_last;
+  const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = blockIdx.x, nslot = p.top * p.sub;
+  const int i = slot / p.sub, sb = slot - i * p.sub;
+  const uint16_t* hr = p.h + (int64_t)r * p.d;
+  for (int e = tid * 8; e < p.d; e += 2048) *(uint4*)(s_h + e) = *(const uint4*)(hr + e);
   const int c = p.kept[(int64_t)r * p.top + i];
   const bool ok = c >= 0 && c < p.C;   // always true: top <= C leaves a cluster to take
   const int j0 = ok ? c * p.csize + sb * kClusterBlock : 0;
   const int j1 = ok ? min(j0 + kClusterBlock, (c + 1) * p.csize) : 0;
-  const uint16_t* hr = p.h + (int64_t)r * p.d;
+  __syncthreads();
   RowState st;
   st.init();
-  for (int j = j0 + wave; j < j1; j += 4) {
-    const float z = wave_dot_bf16(hr, p.w + (int64_t)j * p.d, p.d, lane);
-    if (lane == 0) {
-      st.a.push(z, p.perm[j]);
-      st.l.merge(z, 1.f);
+  constexpr int TPW = kClusterBlock / 4, G = 4;
+  for (int g = 0; g < TPW; g += G) {
+    const int jb = j0 + wave * TPW + g;
+    if (jb >= j1) break;
+    const uint16_t* wr[G];
+    int id[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int j = min(jb + t, j1 - 1);   // a ragged group repeats its last token; only valid ones count
+      wr[t] = p.w + (int64_t)j * p.d;
+      id[t] = p.perm[j];
+    }
+    float acc[G] = {0.f, 0.f, 0.f, 0.f};
+    for (int e0 = lane * 8; e0 < p.d; e0 += 1024) {
+      const int e1 = e0 + 512;
+      uint4 a0[G], a1[G];
+#pragma unroll
+      for (int t = 0; t < G; ++t) a0[t] = *(const uint4*)(wr[t] + e0);
+      if (e1 < p.d) {
+#pragma unroll
+        for (int t = 0; t < G; ++t) a1[t] = *(const uint4*)(wr[t] + e1);
+      }
+      const uint4 h0 = *(const uint4*)(s_h + e0);
+#pragma unroll
+      for (int t = 0; t < G; ++t) fma_bf16x8(acc[t], h0, a0[t]);
+      if (e1 < p.d) {
+        const uint4 h1 = *(const uint4*)(s_h + e1);
+#pragma unroll
+        for (int t = 0; t < G; ++t) fma_bf16x8(acc[t], h1, a1[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+#pragma unroll
+      for (int k = 32; k > 0; k >>= 1) acc[t] += shfl_xor_f(acc[t], k);
+    }
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      if (jb + t < j1) {
+        st.a.push(acc[t], id[t]);
+        st.l.merge(acc[t], 1.f);
+      }
     }
   }
-  if (lane == 0) s_part[wave] = to_part(st);
+  if (lane == 0) s_st[wave] = st;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    RowState a = from_part(s_part[0]);
-    for (int w = 1; w < 4; ++w) state_merge(a, from_part(s_part[w]));
-    p.sel[(int64_t)blockIdx.x * p.R + r] = to_part(a);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(p.part, (short)0, p.part_bytes, kBufferWord3);
+  if (tid == 0) {
+    RowState a = s_st[0];
+    for (int w = 1; w < 4; ++w) state_merge(a, s_st[w]);
+    const uint32_t off = (uint32_t)(((int64_t)r * nslot + slot) * kClPartWords * 4);
+    const u32x4_t q0 = {__float_as_uint(a.a.v1), (uint32_t)a.a.i1, __float_as_uint(a.a.v2), (uint32_t)a.a.i2};
+    const u32x4_t q1 = {__float_as_uint(a.l.m), __float_as_uint(a.l.s), 0u, 0u};
+    __builtin_amdgcn_raw_buffer_store_b128(q0, rsrc, off, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b128(q1, rsrc, off + 16, 0, kCoherent);
+    wait_vm_n<0>();
+    s_last = __hip_atomic_fetch_add(p.cnt + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nslot - 1;
   }
-}
-
-// grid R, one wave: merge the top * sub partials of row r
-__global__ __launch_bounds__(64) void cluster_merge_kernel(ClusterParams p, sv_row_stats* stats, int32_t* clusters,
-                                                          int32_t* out_tokens, int out_stride) {
-  const int r = blockIdx.x, lane = threadIdx.x;
+  __syncthreads();
+  if (!s_last || wave != 0) return;
   RowState a;
   a.init();
-  for (int k = lane; k < p.top * p.sub; k += 64) state_merge(a, from_part(p.sel[(int64_t)k * p.R + r]));
+  for (int k = lane; k < nslot; k += 64) {
+    const uint32_t off = (uint32_t)(((int64_t)r * nslot + k) * kClPartWords * 4);
+    const u32x4_t q0 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kCoherent);
+    const u32x4_t q1 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, kCoherent);
+    RowState b;
+    b.init();
+    b.a.v1 = __uint_as_float(q0[0]); b.a.i1 = (int)q0[1]; b.a.v2 = __uint_as_float(q0[2]); b.a.i2 = (int)q0[3];
+    b.l.m = __uint_as_float(q1[0]); b.l.s = __uint_as_float(q1[1]);
+    state_merge(a, b);
+  }
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) state_merge_xor(a, m);
-  if (clusters)
-    for (int i = lane; i < p.top; i += 64) clusters[(int64_t)r * p.top + i] = p.kept[(int64_t)r * p.top + i];
   if (lane != 0) return;
   sv_row_stats o;
   o.top1_id = a.a.i1;
@@ -691,8 +862,8 @@ __global__ __launch_bounds__(64) void cluster_merge_kernel(ClusterParams p, sv_r
   o.sample_id = -1;
   o.sample_s1 = 0.f;
   o.sample_s2 = 0.f;
-  stats[r] = o;
-  if (out_tokens) out_tokens[(int64_t)r * out_stride] = a.a.i1;
+  p.stats[r] = o;
+  if (p.out_tokens) p.out_tokens[(int64_t)r * p.out_stride] = a.a.i1;
 }
 
 // ---------------------------------------------------------------------------
@@ -938,22 +1109,54 @@ static int validate_cluster(const sv_cluster_desc* d) {
     return SV_ERR_ARG;
   if (d->dtype != SV_BF16 || d->d_model % 8 || d->vocab % d->n_clusters) return SV_ERR_ARG;
   if (d->top_clusters > d->n_clusters) return SV_ERR_ARG;
-  if (d->rows > 64 || d->n_clusters > 4096 || d->top_clusters > 64) return SV_ERR_UNSUPPORTED;
+  if (d->rows > 64 || d->n_clusters > kClusterMaxC || d->top_clusters > 64 || d->d_model > kClusterMaxD)
+    return SV_ERR_UNSUPPORTED;
+  const int64_t sub = (d->vocab / d->n_clusters + kClusterBlock - 1) / kClusterBlock;
+  if ((int64_t)d->rows * d->top_clusters * sub * kClPartWords * 4 > ((int64_t)1 << 31)) return SV_ERR_UNSUPPORTED;
   return SV_OK;
 }
 
+// Cluster scores come from the MFMA projection with K-split fp32 slices when the
+// centroid count and width fit it, else from the plain per-centroid kernel.
+static bool cluster_scores_by_gemm(const sv_cluster_desc& d) {
+  return d.n_clusters % 64 == 0 && d.d_model % 32 == 0;
+}
+
+// Lanes per top-k group: the largest power of two <= 64 for which at least 4 top
+// groups hold a score, else 1 (every score its own group).  Thread t holds scores
+// 4t + e; the scores of residue e live on the first ceil((C - e) / 4) threads.
+static int topk_group_lanes(int C, int top) {
+  for (int gs = 64; gs > 1; gs >>= 1) {
+    int groups = 0;
+    for (int e = 0; e < 4 && e < C; ++e) {
+      const int ne = (C - e + 3) / 4;
+      groups += (ne + gs - 1) / gs;
+    }
+    if (groups >= 4 * top) return gs;
+  }
+  return 1;
+}
+
 struct ClusterPlan {
-  int csize, sub;
-  size_t scores, kept, sel, total;
+  int csize, sub, nslot;
+  size_t scores, kept, part, cnt, total;
 };
 static ClusterPlan cluster_plan(const sv_cluster_desc& d) {
   ClusterPlan pl{};
   pl.csize = d.vocab / d.n_clusters;
   pl.sub = (pl.csize + kClusterBlock - 1) / kClusterBlock;
-  pl.scores = align_up((size_t)d.rows * d.n_clusters * 4, 256);
+  pl.nslot = d.top_clusters * pl.sub;
+  int smax = 1;   // slices at most (the split count only shrinks with fewer compute units)
+  if (cluster_scores_by_gemm(d)) {
+    const RingPlan rp = ring_plan(2, d.rows, d.d_model, d.n_clusters, kMaxWG);
+    smax = split_count(rp, kMaxWG);
+    if (smax < 1) smax = 1;
+  }
+  pl.scores = align_up((size_t)smax * d.rows * ((d.n_clusters + 3) / 4 * 4) * 4, 256);
   pl.kept = align_up((size_t)d.rows * d.top_clusters * 4, 256);
-  pl.sel = align_up((size_t)d.top_clusters * pl.sub * d.rows * sizeof(SelPart), 256);
-  pl.total = pl.scores + pl.kept + pl.sel;
+  pl.part = align_up((size_t)d.rows * pl.nslot * kClPartWords * 4, 256);
+  pl.cnt = align_up((size_t)d.rows * 4, 256);
+  pl.total = pl.scores + pl.kept + pl.part + pl.cnt;
   return pl;
 }
 
@@ -986,16 +1189,45 @@ extern "C" int sv_cluster_unembed(const sv_cluster_desc* d, const void* hidden, 
   p.top = d->top_clusters;
   p.csize = pl.csize;
   p.sub = pl.sub;
+  p.cstride = (p.C + 3) / 4 * 4;
+  p.gs = topk_group_lanes(p.C, p.top);
   char* ws = (char*)workspace;
   p.scores = (float*)ws;
   p.kept = (int32_t*)(ws + pl.scores);
-  p.sel = (SelPart*)(ws + pl.scores + pl.kept);
+  p.part = (float*)(ws + pl.scores + pl.kept);
+  p.part_bytes = (uint32_t)pl.part;
+  p.cnt = (int32_t*)(ws + pl.scores + pl.kept + pl.part);
+  p.stats = stats;
+  p.clusters = clusters;
+  p.out_tokens = out_tokens;
+  p.out_stride = out_stride > 0 ? out_stride : 1;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(cluster_score_kernel, dim3((p.C + 15) / 16, p.R), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(cluster_topk_kernel, dim3(p.R), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(cluster_logits_kernel, dim3(p.top * p.sub, p.R), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(cluster_merge_kernel, dim3(p.R), dim3(64), 0, s, p, stats, clusters, out_tokens,
-                     out_stride > 0 ? out_stride : 1);
+  p.splits = 0;
+  if (cluster_scores_by_gemm(*d)) {
+    RingPlan rp = ring_plan(2, d->rows, d->d_model, d->n_clusters, live_wg());
+    const int S = split_count(rp, live_wg());
+    if (S >= 1) {
+      GemmParams g{};
+      g.x = p.h;
+      g.w = p.cent;
+      g.R = p.R;
+      g.K = p.d;
+      g.N = p.C;
+      g.nblk = rp.nblk;
+      g.kch = rp.kch;
+      g.y = p.scores;
+      g.splits = S;
+      rc = dispatch_ring<2, GM_SPLIT>(g, p.R, rp.nblk * S, s);
+      if (rc != SV_OK) return rc;
+      p.splits = S;
+    }
+  }
+  if (p.splits == 0) {
+    p.splits = 1;
+    hipLaunchKernelGGL(cluster_score_kernel, dim3((p.C + 15) / 16, p.R), dim3(256), 0, s, p);
+  }
+  hipLaunchKernelGGL(cluster_topk_kernel, dim3(p.R), dim3(kTopkThreads), 0, s, p);
+  hipLaunchKernelGGL(cluster_logits_kernel, dim3(pl.nslot, p.R), dim3(256), 0, s, p);
   return launch_status();
 }
 

@@ -16,6 +16,8 @@ draft) proposes k tokens one at a time.  Step i, for every sequence b:
     h  = norm(x) W_up^T                                     sv_add_rmsnorm, sv_linear (bf16)
     d_{b,i+1} = argmax h E^T                                sv_lmhead_select (greedy; the
                                                             token goes to drafts[b][i])
+    or, with a clustering of E given (section 4.3, cheap_unembed), the argmax over
+    the tokens of the clusters whose centroids score highest   sv_cluster_unembed
 
 h_prev and the token of step 0 are the verify step's final hidden state at the
 accepted row and its next token (both read through sv_accept_out); later steps use
@@ -35,7 +37,7 @@ class Drafter:
     """Device-resident drafter: weights, buffers and descriptors for batch B."""
 
     def __init__(self, target_cfg, dcfg, target_E: torch.Tensor, weights: dict, caches: list,
-                 cache_len: torch.Tensor, device="cuda"):
+                 cache_len: torch.Tensor, device="cuda", clusters: dict | None = None):
         if target_cfg.dtype != "bf16":
             raise ValueError("the drafter path is bf16")
         self.t = target_cfg
@@ -93,6 +95,15 @@ class Drafter:
         self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.lm_ws = None
         self.drafts = None
+        # clustered unembedding: {"perm", "w_perm", "centroids", "top"} (None: full vocabulary)
+        self.clusters = clusters
+        if clusters is not None:
+            C = clusters["centroids"].shape[0]
+            self.cl_desc = L.ClusterDesc(rows=B, d_model=d, vocab=target_cfg.vocab, n_clusters=C,
+                                         top_clusters=clusters["top"], dtype=L.SV_BF16)
+            self.cl_ws = torch.zeros(max(256, L.sv_cluster_unembed_workspace(self.cl_desc)), dtype=torch.uint8,
+                                     device=dev)
+            self.kept = torch.zeros(B, clusters["top"], dtype=torch.int32, device=dev)
 
     def _attn_desc(self, j: int, i: int) -> L.AttnDesc:
         key = (j, i)
@@ -161,6 +172,12 @@ class Drafter:
         tok = self._ev("unembed", stream)
         u = self._norm(pending, stream)
         L.sv_linear(self._lin(dd, d, L.SV_EPI_STORE), u, self.W["w_up"], self.h, self.lin_ws, stream)
+        if self.clusters is not None:
+            c = self.clusters
+            L.sv_cluster_unembed(self.cl_desc, self.h, c["centroids"], c["w_perm"], c["perm"], self.stats, self.kept,
+                                 drafts.data_ptr() + 4 * i, k, self.cl_ws, stream)
+            self._end(tok)
+            return
         desc = L.LMHeadDesc(batch=B, k=0, d_model=d, vocab=t.vocab, mode=L.SV_SELECT_GREEDY, dtype=L.SV_BF16,
                             out_stride=k)
         if self.lm_ws is None:

@@ -191,6 +191,19 @@ def clustered_unembedding(vocab: int, d: int, n_clusters: int, seed: int = 0, de
     return {"perm": perm, "w_perm": w_perm, "centroids": centers.to(torch_dtype(dtype)), "E": E}
 
 
+def clusters_of(E: torch.Tensor, n_clusters: int, top: int, seed: int = 0) -> dict:
+    """A clustering of an existing unembedding E [V, d] for the clustered unembed:
+    a seeded random permutation cut into n_clusters equal clusters, w_perm = E[perm]
+    and, standing in for trained centroids, the mean of each cluster's rows."""
+    V, d = E.shape
+    assert V % n_clusters == 0
+    g = generator(seed, "C.perm", E.device)
+    perm = torch.randperm(V, generator=g, device=E.device).to(torch.int32)
+    w_perm = E[perm.long()].contiguous()
+    cent = w_perm.view(n_clusters, V // n_clusters, d).float().mean(dim=1).to(E.dtype)
+    return {"perm": perm, "w_perm": w_perm, "centroids": cent, "top": int(top)}
+
+
 def stack_caches(cfg, seed: int = 0, device="cpu", capacity: int | None = None,
                  fill_from: int | None = None) -> list:
     """Per layer: k [B, Hkv, cap, D] (and v unless K = V), rows [fill_lo, ctx) ~ N(0,1),

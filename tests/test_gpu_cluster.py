@@ -103,3 +103,24 @@ def test_cluster_unembed_drafter_size_sampled_rows():
     st2, kept2, _ = run_cluster(h, cu, top, dev)    # repeat: identical bits
     assert (st.view(np.int32) == st2.view(np.int32)).all() and (kept == kept2).all()
     assert check_rows(h, cu, top, st, kept, toks, 1, [0, 3, 7], "full") >= 2
+
+
+@gpu
+@pytest.mark.parametrize("C", [128, 48])
+def test_cluster_unembed_tied_scores(C):
+    # a zero row ties every cluster score and every logit: the kept clusters are the
+    # lowest indices and the top token the lowest id among their tokens
+    dev = need_gpu()
+    R, d, top = 3, 256, 8
+    V = C * 40
+    say(f"[cluster ties] C={C}")
+    cu = inputs.clustered_unembedding(V, d, C, seed=C, device=dev)
+    h = inputs.normal((R, d), 1.0, C, "h", dev)
+    h[0].zero_()
+    st, kept, toks = run_cluster(h, cu, top, dev)
+    assert list(kept[0]) == list(range(top))
+    ids = cu["perm"].cpu().numpy()[: top * (V // C)]
+    srt = np.sort(ids)
+    assert (int(st[0]["top1_id"]), int(st[0]["top2_id"])) == (srt[0], srt[1])
+    assert float(st[0]["top1"]) == 0.0 and abs(float(st[0]["lse"]) - np.log(ids.size)) < 1e-5
+    check_rows(h, cu, top, st, kept, toks, 1, [1, 2], "ties")

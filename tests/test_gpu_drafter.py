@@ -1,5 +1,6 @@
 """GPU parity of the drafter step (sv_draft_input, K-split projections, read-only
-verify attention into the target's caches, greedy unembedding) against the oracle.
+verify attention into the target's caches, greedy unembedding over the whole vocabulary
+or over the kept clusters) against the oracle.
 
 Each draft step is checked with matched inputs: the oracle takes the GPU's h_prev
 and token of that step, so a near-tie that sends the two sides to different tokens
@@ -25,7 +26,7 @@ def host_caches(caches):
     return [{"k": inputs.host_f32(c["k"]), "v": None if c["v"] is None else inputs.host_f32(c["v"])} for c in caches]
 
 
-def drafter_case(tcfg, dcfg, lens, k, seed):
+def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0):
     dev = need_gpu()
     B = tcfg.batch
     say(f"[drafter] d={tcfg.d_model} d_draft={dcfg.d_draft} B={B} k={k} lens={lens}")
@@ -42,7 +43,10 @@ def drafter_case(tcfg, dcfg, lens, k, seed):
         acc[b, 7] = b * (tcfg.k + 1) + int(hr[b])
     acc[:, 1] = inputs.randint((B,), 0, tcfg.vocab - 1, seed, "next_tok", dev)
     drafts = torch.full((B, k), -1, dtype=torch.int32, device=dev)
-    dr = Drafter(tcfg, dcfg, tw["E"], dw, caches, cl, dev)
+    cu = inputs.clusters_of(tw["E"], n_clusters, top, seed) if n_clusters else None
+    dr = Drafter(tcfg, dcfg, tw["E"], dw, caches, cl, dev, clusters=cu)
+    if cu is not None:
+        cu_host = (inputs.bf16_bits(cu["centroids"]), inputs.bf16_bits(cu["w_perm"]), cu["perm"].cpu().numpy())
 
     o = om.OracleDrafter(tcfg, dcfg, inputs.bf16_bits(tw["E"]),
                          {"E": inputs.bf16_bits(dw["E"]), "w_down": inputs.bf16_bits(dw["w_down"]),
@@ -62,8 +66,16 @@ def drafter_case(tcfg, dcfg, lens, k, seed):
         hq, z = o.step(st, h_prev, tok, i)
         gs = L.decode_row_stats(dr.stats)
         zmax = np.abs(z).max()
+        cref = oracle.cluster_unembed(hq, *cu_host, top) if cu is not None else None
         for b in range(B):
-            ref = oracle.row_stats(z[b])
+            if cref is None:
+                ref = oracle.row_stats(z[b])
+            else:
+                ref = cref[b]
+                sc = np.sort(ref["scores"])[::-1]
+                if top < sc.size and sc[top - 1] - sc[top] <= ATOL * max(1.0, np.abs(sc).max()):
+                    continue                    # the kept set is a near-tie: either side may differ
+                assert sorted(dr.kept[b].tolist()) == sorted(ref["clusters"]), (i, b)
             assert abs(float(gs[b]["lse"]) - ref["lse"]) < ATOL * max(1.0, zmax), (i, b)
             assert abs(float(gs[b]["top1"]) - ref["top1"]) < ATOL * max(1.0, zmax), (i, b)
             if ref["top1"] - ref["top2"] > MARGIN:
@@ -94,3 +106,12 @@ def test_drafter_wide_window_and_ragged():
     tcfg = configs.scaled_stack(name="drafter_target2", d_model=192, vocab=2048, d_ff=256, batch=5, k=2,
                                 window=300, local_heads=(4, 1, 128), global_heads=(8, 2, 256))
     drafter_case(tcfg, configs.scaled_drafter(d_draft=256, d_ff=512), [5, 290, 301, 1000, 64], 2, 2)
+
+
+@gpu
+def test_drafter_clustered_unembed():
+    # the cheap unembed: 4096 tokens in 64 clusters of 64, the 8 best kept per row
+    tcfg = configs.scaled_stack(name="drafter_target3", d_model=256, vocab=4096, d_ff=512, batch=4, k=3,
+                                window=64, local_heads=(4, 2, 128), global_heads=(4, 1, 256))
+    drafter_case(tcfg, configs.scaled_drafter(d_draft=128, d_ff=256), [100, 7, 300, 64], 3, 3,
+                 n_clusters=64, top=8)
