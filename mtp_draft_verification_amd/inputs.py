@@ -87,6 +87,23 @@ def categorical(probs: torch.Tensor, seed: int, name: str) -> torch.Tensor:
     return torch.multinomial(probs, 1, replacement=True, generator=g)[:, 0].to(torch.int32)
 
 
+def channel_scales(shape, std: float, seed: int, name: str, device="cpu") -> torch.Tensor:
+    """Per-channel fp32 scales of an fp8 cache whose entries are about N(0, std^2):
+    a 4-sigma value lands near the largest E4M3 magnitude (448), times a seeded
+    per-channel factor in [0.75, 1.25)."""
+    return (std * 4.0 / 448.0) * (0.75 + 0.5 * uniform(shape, seed, name, device))
+
+
+def fp8_codes(shape, std: float, scales: torch.Tensor, seed: int, name: str, device="cpu") -> torch.Tensor:
+    """uint8 fp8 E4M3 codes of N(0, std^2) entries divided by per-channel `scales`
+    ([Hkv, D] for a [B, Hkv, cap, D] cache), clipped to +-448 and rounded to nearest
+    even by torch's fp8 cast."""
+    x = normal(shape, std, seed, name, device, "f32")
+    s = scales.view(1, scales.shape[0], 1, scales.shape[1]) if x.dim() == 4 else scales
+    x.div_(s).clamp_(-448.0, 448.0)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Host uint16 array holding the bit patterns of a bf16 tensor."""
     assert t.dtype == torch.bfloat16

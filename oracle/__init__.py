@@ -43,6 +43,7 @@ class AttnArgs(ctypes.Structure):
         ("cap", ctypes.c_int64), ("L", ctypes.c_int64),
         ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
         ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +68,10 @@ def lib():
         L.svo_bf16_round.argtypes = [f64]
         L.svo_bf16_round_array.argtypes = [P, i64]
         L.svo_rope.argtypes = [P, ctypes.c_int, f64, f64]
+        L.svo_e4m3_decode.restype = f64
+        L.svo_e4m3_decode.argtypes = [ctypes.c_int]
+        L.svo_e4m3_encode.restype = ctypes.c_int
+        L.svo_e4m3_encode.argtypes = [ctypes.c_float]
         L.svo_attn_group.argtypes = [ctypes.POINTER(AttnArgs)]
         L.svo_attn_group.restype = ctypes.c_int
         L.svo_linear.argtypes = [i64, i64, i64, P, P, ctypes.c_int, P]
@@ -133,6 +138,25 @@ def rope(x, rope_dims: int, base: float, pos: float) -> np.ndarray:
     y = _f64(x).copy()
     lib().svo_rope(_ptr(y), int(rope_dims), float(base), float(pos))
     return y
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of fp8 E4M3 codes (OCP E4M3FN: bias 7, subnormals m 2^-9, no
+    infinities, 0x7F / 0xFF NaN), fp64, same shape as `codes`."""
+    table = np.array([lib().svo_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each fp32 value (ties to even, saturating at +-448)."""
+    x = np.asarray(x, dtype=np.float32)
+    return np.array([lib().svo_e4m3_encode(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def dequant_cache(codes, scale) -> np.ndarray:
+    """An fp8 cache [..., cap, D] with per-channel scales [D] as the fp32 array the
+    attention oracle reads: scale * value, rounded once to fp32."""
+    return (e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)).astype(np.float32)
 
 
 def gelu_tanh(x: float) -> float:
@@ -220,9 +244,11 @@ def cluster_unembed(h, centroids, w_perm, perm, top: int) -> list:
 
 def attn_group(*, q, k_new, v_new, k_cache, v_cache, L: int, window: int, rope_dims: int,
                rope_base: float, scale: float, k_is_v: bool, append: bool,
-               q_pos_offset: int = 0, round_bf16: bool) -> np.ndarray:
+               q_pos_offset: int = 0, round_bf16: bool, k_scale=None, v_scale=None) -> np.ndarray:
     """One sequence, one KV head.  q [n_q, group, D]; k_new/v_new [n_q, D];
-    k_cache/v_cache [cap, D] float32 (modified in place when append).
+    k_cache/v_cache [cap, D] float32 (modified in place when append).  With k_scale /
+    v_scale [D] the cache is an fp8 one seen through its scales (dequant_cache): an
+    appended row is stored as scale * e4m3(row / scale).
     Returns out [n_q, group, D] fp64."""
     q = _f32(q)
     n_q, group, D = q.shape
@@ -232,12 +258,17 @@ def attn_group(*, q, k_new, v_new, k_cache, v_cache, L: int, window: int, rope_d
     kn = _f32(k_new) if append else None
     vn = _f32(v_new) if (append and not k_is_v) else None
     out = np.zeros((n_q, group, D), dtype=np.float64)
+    ks = None if k_scale is None else _f32(k_scale)
+    vs = None if (v_scale is None or k_is_v) else _f32(v_scale)
+    assert ks is None or ks.shape == (D,)
+    assert vs is None or vs.shape == (D,)
     a = AttnArgs(n_q=n_q, group=group, head_dim=D, window=int(window), rope_dims=int(rope_dims),
                  k_is_v=int(bool(k_is_v)), append=int(bool(append)),
                  q_pos_offset=int(q_pos_offset), round_bf16=int(bool(round_bf16)), pad_=0,
                  rope_base=float(rope_base), scale=float(scale), cap=k_cache.shape[0], L=int(L),
                  q=_ptr(q), k_new=_ptr(kn), v_new=_ptr(vn), k_cache=_ptr(k_cache),
-                 v_cache=_ptr(v_cache) if not k_is_v else None, out=_ptr(out))
+                 v_cache=_ptr(v_cache) if not k_is_v else None, out=_ptr(out),
+                 k_scale=_ptr(ks), v_scale=_ptr(vs))
     rc = lib().svo_attn_group(ctypes.byref(a))
     if rc != 0:
         raise ValueError("oracle attention: appended rows exceed the cache capacity")
@@ -246,9 +277,10 @@ def attn_group(*, q, k_new, v_new, k_cache, v_cache, L: int, window: int, rope_d
 
 def verify_attn(*, q, k_new, v_new, k_cache, v_cache, cache_len, window: int, rope_dims: int,
                 rope_base: float, scale: float, k_is_v: bool, append: bool = True,
-                q_pos_offset: int = 0, round_bf16: bool) -> np.ndarray:
+                q_pos_offset: int = 0, round_bf16: bool, k_scale=None, v_scale=None) -> np.ndarray:
     """Whole batch.  q [B, n_q, Hq, D]; k_new/v_new [B, n_q, Hkv, D];
-    k_cache/v_cache [B, Hkv, cap, D] float32 (modified in place).
+    k_cache/v_cache [B, Hkv, cap, D] float32 (modified in place); k_scale / v_scale
+    [Hkv, D] for fp8 caches (see attn_group).
     Returns out [B, n_q, Hq, D] fp64."""
     q = np.asarray(q)
     B, n_q, Hq, D = q.shape
@@ -265,7 +297,8 @@ def verify_attn(*, q, k_new, v_new, k_cache, v_cache, cache_len, window: int, ro
                            k_cache=kc, v_cache=vc, L=int(cache_len[b]), window=window,
                            rope_dims=rope_dims, rope_base=rope_base, scale=scale,
                            k_is_v=k_is_v, append=append, q_pos_offset=q_pos_offset,
-                           round_bf16=round_bf16)
+                           round_bf16=round_bf16, k_scale=None if k_scale is None else k_scale[g],
+                           v_scale=None if v_scale is None else v_scale[g])
             out[b, :, g * G:(g + 1) * G, :] = o
     return out
 

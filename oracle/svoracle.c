@@ -137,7 +137,48 @@ typedef struct {
   float* k_cache;       /* [cap][head_dim], rotated keys */
   float* v_cache;       /* [cap][head_dim] (unused if k_is_v) */
   double* out;          /* [n_q][group][head_dim] */
+  const float* k_scale; /* [head_dim] or NULL: appended keys are stored as fp8 E4M3 codes */
+  const float* v_scale; /* [head_dim] or NULL: the same for appended values */
 } svo_attn_args;
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 (the OCP 8-bit float "E4M3FN"): 1 sign bit, 4 exponent bits with */
+/* bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9;  */
+/* no infinities; S.1111.111 is NaN, so the largest finite value is 448.     */
+/* ------------------------------------------------------------------------ */
+double svo_e4m3_decode(int code) {
+  const int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest code to x (ties to the even code), values beyond +-448 saturating to
+ * +-448.  Brute force over the 127 finite magnitudes, which are increasing in the
+ * code, so an exact tie falls between two neighbours and "even" is the one whose
+ * lowest bit is 0. */
+int svo_e4m3_encode(float x) {
+  if (x != x) return 0x7F;
+  const int sign = signbit(x) ? 0x80 : 0;
+  const double a = fabs((double)x);
+  int best = 0;
+  double bd = a;
+  for (int c = 1; c <= 0x7E; ++c) {
+    const double d = fabs(svo_e4m3_decode(c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = c; }
+  }
+  if (a > 448.0) best = 0x7E;
+  return sign | best;
+}
+
+/* value stored by a quantized cache: s * decode(encode(x / s)), the quotient an
+ * IEEE fp32 division */
+static float svo_q8_store(double x, float s) {
+  const float q = (float)x / s;
+  return (float)((double)s * svo_e4m3_decode(svo_e4m3_encode(q)));
+}
 
 /* Multi-query verify attention, [G4] section 4.2 (one target forward scores
  * the k drafts plus the bonus position) and [AG4] section 3.  Steps:
@@ -163,13 +204,13 @@ int svo_attn_group(const svo_attn_args* a) {
     svo_rope(tmp, a->rope_dims, a->rope_base, (double)(L + j));
     for (int d = 0; d < D; ++d) {
       double kv = a->round_bf16 ? svo_bf16_round(tmp[d]) : tmp[d];
-      a->k_cache[(L + j) * D + d] = (float)kv;
+      a->k_cache[(L + j) * D + d] = a->k_scale ? svo_q8_store(kv, a->k_scale[d]) : (float)kv;
     }
     if (!a->k_is_v) {
       for (int d = 0; d < D; ++d) {
         double vv = (double)a->v_new[j * D + d];
         if (a->round_bf16) vv = svo_bf16_round(vv);
-        a->v_cache[(L + j) * D + d] = (float)vv;
+        a->v_cache[(L + j) * D + d] = a->v_scale ? svo_q8_store(vv, a->v_scale[d]) : (float)vv;
       }
     }
   }

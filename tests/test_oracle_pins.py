@@ -312,6 +312,68 @@ def test_cluster_unembed_restricts_to_kept_clusters_and_maps_ids():
 
 
 # ---------------------------------------------------------------------------
+# fp8 E4M3 cache codes
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_fixed_points_of_the_format():
+    # OCP E4M3FN: largest finite 448 (S.1111.110), smallest normal 2^-6, smallest
+    # subnormal 2^-9, 1.0 = 0.0111.000, NaN at S.1111.111 and no infinity
+    d = oracle.e4m3_decode(np.arange(256))
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0
+    assert d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9 and d[0x38] == 1.0 and d[0x39] == 1.125
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.isfinite(np.delete(d, [0x7F, 0xFF])).all()
+    assert (np.diff(d[:0x7F]) > 0).all()                        # magnitudes increase with the code
+    np.testing.assert_array_equal(d[0x80:0xFF], -d[:0x7F])
+    # the library's fp8 type agrees on every finite code
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    fin = np.isfinite(d)
+    np.testing.assert_array_equal(d[fin], lib[fin])
+
+
+def test_e4m3_encode_round_to_nearest_even_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)), codes)
+    # exact midpoints go to the even code, including across a binade and into zero
+    mids = np.array([1.0625, 1.1875, 1.9375, 2.0 ** -10, 3 * 2.0 ** -10, 432.0], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.e4m3_encode(mids), [0x38, 0x3A, 0x40, 0x00, 0x02, 0x7E])
+    # beyond the largest finite value: saturate, never NaN
+    np.testing.assert_array_equal(oracle.e4m3_encode([449.0, 1e30, -5000.0]), [0x7E, 0x7E, 0xFE])
+    # random in-range values: the library's round-to-nearest-even cast
+    x = (np.random.default_rng(21).standard_normal(4000) * 60).clip(-448, 448).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(x), lib)
+
+
+def test_attn_quantized_append_stores_scaled_codes():
+    # appended rows of an fp8 cache = scale * e4m3(bf16 row / scale); checked against
+    # the unquantized append of the same rows and the library's fp8 cast
+    rng = np.random.default_rng(22)
+    D, cap, L, nq = 64, 40, 30, 3
+    q = rng.standard_normal((nq, 2, D)).astype(np.float32)
+    kn = rng.standard_normal((nq, D)).astype(np.float32)
+    vn = rng.standard_normal((nq, D)).astype(np.float32)
+    ks = (0.01 + 0.02 * rng.random(D)).astype(np.float32)
+    vs = (0.01 + 0.02 * rng.random(D)).astype(np.float32)
+    kc = np.zeros((cap, D), np.float32); vc = np.zeros((cap, D), np.float32)
+    args = dict(L=L, window=0, rope_dims=D, rope_base=1e4, scale=0.125, k_is_v=False, append=True,
+                round_bf16=True)
+    oracle.attn_group(q=q, k_new=kn, v_new=vn, k_cache=kc, v_cache=vc, **args)
+    kq = np.zeros_like(kc); vq = np.zeros_like(vc)
+    o = oracle.attn_group(q=q, k_new=kn, v_new=vn, k_cache=kq, v_cache=vq, k_scale=ks, v_scale=vs, **args)
+
+    def lib_q(x, s):
+        c = torch.from_numpy((x / s).astype(np.float32)).to(torch.float8_e4m3fn)
+        return (c.double().numpy() * s.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(kq[L:L + nq], lib_q(kc[L:L + nq], ks))
+    np.testing.assert_array_equal(vq[L:L + nq], lib_q(vc[L:L + nq], vs))
+    # and the output is plain attention over the stored (dequantized) rows
+    kq2, vq2 = kq.copy(), vq.copy()
+    o2 = oracle.attn_group(q=q, k_new=None, v_new=None, k_cache=kq2, v_cache=vq2,
+                           **{**args, "append": False, "L": L + nq, "q_pos_offset": -nq})
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # greedy acceptance
 # ---------------------------------------------------------------------------
 
