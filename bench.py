@@ -65,8 +65,8 @@ def parse():
     return ap.parse_args()
 
 
-ONLY_CALLS = ("attn_global", "attn_local", "lmhead", "lmhead_sample", "qkv_local", "qkv_global", "o_local",
-              "o_global", "gu", "down", "hbm_copy")
+ONLY_CALLS = ("attn_global", "attn_local", "attn_global_fp8", "attn_local_fp8", "lmhead", "lmhead_sample",
+              "qkv_local", "qkv_global", "o_local", "o_global", "gu", "down", "hbm_copy")
 COPY_BYTES = 1 << 30  # hbm_copy: a plain 1 GiB device-to-device copy (counter calibration)
 
 
@@ -94,11 +94,17 @@ def bench_one(args, only):
     B, nq = cfg.batch, cfg.k + 1
     stream = torch.cuda.current_stream()
     if only.startswith("attn"):
-        ly = cfg.layers[-1] if only == "attn_global" else cfg.layers[0]
+        fp8 = only.endswith("_fp8")
+        ly = cfg.layers[-1] if only.startswith("attn_global") else cfg.layers[0]
         cap = cfg.ctx + nq + 8
         lo = 0 if ly.window == 0 else max(0, cfg.ctx - ly.window - 8)
-        kc = torch.zeros((B, ly.n_heads_kv, cap, ly.head_dim), dtype=torch.bfloat16, device=dev)
-        kc[:, :, lo:cfg.ctx] = inputs.normal((B, ly.n_heads_kv, cfg.ctx - lo, ly.head_dim), 1.0, 0, "kc", dev)
+        if fp8:
+            ks = inputs.channel_scales((ly.n_heads_kv, ly.head_dim), 1.0, 0, "ks", dev)
+            kc = torch.zeros((B, ly.n_heads_kv, cap, ly.head_dim), dtype=torch.uint8, device=dev)
+            kc[:, :, lo:cfg.ctx] = inputs.fp8_codes((B, ly.n_heads_kv, cfg.ctx - lo, ly.head_dim), 1.0, ks, 0, "kc8", dev)
+        else:
+            kc = torch.zeros((B, ly.n_heads_kv, cap, ly.head_dim), dtype=torch.bfloat16, device=dev)
+            kc[:, :, lo:cfg.ctx] = inputs.normal((B, ly.n_heads_kv, cfg.ctx - lo, ly.head_dim), 1.0, 0, "kc", dev)
         vc = None if ly.k_is_v else kc.clone()
         q = inputs.normal((B, nq, ly.n_heads_q, ly.head_dim), 1.0, 0, "q", dev)
         kn = inputs.normal((B, nq, ly.n_heads_kv, ly.head_dim), 1.0, 0, "kn", dev)
@@ -107,9 +113,13 @@ def bench_one(args, only):
         out = torch.empty_like(q)
         desc = attn_desc(ly, B, nq, cap, "bf16")
         ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
-        call = lambda: L.sv_verify_attn(desc, q, kn, vn, kc, vc, cl, out, ws, None, stream)
+        if fp8:
+            vs = None if ly.k_is_v else ks.clone()
+            call = lambda: L.sv_verify_attn_fp8(desc, q, kn, vn, kc, vc, ks, vs, cl, out, ws, None, stream)
+        else:
+            call = lambda: L.sv_verify_attn(desc, q, kn, vn, kc, vc, cl, out, ws, None, stream)
         lens = [cfg.ctx] * B
-        byts = call_bytes(cfg, lens)["L5.attn" if ly.window == 0 else "L0.attn"]
+        byts = call_bytes(cfg, lens, 1 if fp8 else 2)["L5.attn" if ly.window == 0 else "L0.attn"]
     elif only.startswith("lmhead"):
         mode = L.SV_SELECT_GREEDY if only == "lmhead" else L.SV_SELECT_SAMPLE
         R = B * nq
@@ -180,8 +190,9 @@ def source_digest() -> str:
 # ---------------------------------------------------------------------------
 # algorithmic bytes of the calls of one step (what the method must move)
 # ---------------------------------------------------------------------------
-def call_bytes(cfg, lens) -> dict:
-    """Bytes each named call must move once, for committed lengths `lens` (per sequence)."""
+def call_bytes(cfg, lens, kv_bytes: int = 2) -> dict:
+    """Bytes each named call must move once, for committed lengths `lens` (per
+    sequence); kv_bytes per cache element (2 bf16, 1 fp8)."""
     B, k, d, R = cfg.batch, cfg.k, cfg.d_model, cfg.batch * (cfg.k + 1)
     nq = k + 1
     e = 2  # bf16
@@ -193,7 +204,7 @@ def call_bytes(cfg, lens) -> dict:
         for L in lens:
             n = L + nq
             keys += min(n, ly.window + k) if ly.window else n
-        kv = keys * Hk * D * e * tensors
+        kv = keys * Hk * D * kv_bytes * tensors
         qio = B * nq * H * D * e * 2 + B * nq * Hk * D * e * tensors
         out[f"L{i}.attn"] = kv + qio
         nout = H * D + Hk * D * tensors

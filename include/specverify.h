@@ -128,6 +128,26 @@ int sv_verify_attn(const sv_attn_desc* desc, const void* q, const void* k_new,
                    const int32_t* cache_len, void* out, void* workspace,
                    size_t workspace_bytes, int32_t* dev_status, void* stream);
 
+/* The same verify attention over an fp8 KV cache: KV-cache quantization with
+ * static, per-channel scales, as in the mobile quantization set of "Gemma 4 与
+ * Gemini Nano：端侧智能的架构拆解" (kongchang), section "量化：为移动硬件定制的激进
+ * 路线" (the 8-bit format is this library's choice).  desc is as above with dtype SV_BF16 (q, k_new,
+ * v_new, out stay bf16); the caches hold one byte per element, an fp8 E4M3 code
+ * (OCP E4M3FN: bias 7, largest magnitude 448, no infinities), and represent
+ *   key[b, h, t, d] = k_scale[h, d] * e4m3(k_cache[b, h, t, d])
+ * (the same for values with v_scale).  An appended row is stored as the code of
+ * bf16(row) / scale (fp32 division, round to nearest even, saturating at +-448).
+ * The products use the codes exactly: the key scales are folded into the rotated
+ * queries (one bf16 rounding) and the value scales multiply the output.
+ *   k_scale [Hkv, D] fp32, 16-byte aligned (also the value scales when k_is_v)
+ *   v_scale [Hkv, D] fp32, 16-byte aligned; NULL when k_is_v
+ * Workspace: sv_verify_attn_workspace(desc).  Errors as sv_verify_attn, plus
+ * SV_ERR_ARG for a dtype other than bf16 or a missing or misaligned scale array. */
+int sv_verify_attn_fp8(const sv_attn_desc* desc, const void* q, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* cache_len, void* out, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_status, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* LM head + select                                                          */
 /* ------------------------------------------------------------------------ */

@@ -21,7 +21,7 @@ SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL = 0, 1, 2
 SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU, SV_EPI_SPLIT_F32 = 0, 1, 2, 3
 SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 
-EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn",
+EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn", "sv_verify_attn_fp8",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
            "sv_add_rmsnorm", "sv_draft_input", "sv_linear_splits", "sv_linear_workspace", "sv_linear",
            "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed")
@@ -94,6 +94,8 @@ def load():
     L.sv_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
     L.sv_verify_attn.restype = ctypes.c_int
     L.sv_verify_attn.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, sz, P, P]
+    L.sv_verify_attn_fp8.restype = ctypes.c_int
+    L.sv_verify_attn_fp8.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz, P, P]
     L.sv_lmhead_workspace.restype = sz
     L.sv_lmhead_workspace.argtypes = [ctypes.POINTER(LMHeadDesc)]
     L.sv_lmhead_select.restype = ctypes.c_int
@@ -174,6 +176,15 @@ def sv_verify_attn(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_len,
                                _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(workspace), ws_bytes,
                                _ptr(dev_status), _stream(stream))
     _check("sv_verify_attn", rc)
+
+
+def sv_verify_attn_fp8(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_len, out,
+                       workspace, dev_status=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().sv_verify_attn_fp8(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(cache_len), _ptr(out),
+                                   _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream))
+    _check("sv_verify_attn_fp8", rc)
 
 
 def sv_lmhead_workspace(desc: LMHeadDesc) -> int:

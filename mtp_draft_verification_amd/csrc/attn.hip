@@ -36,6 +36,9 @@ struct AttnParams {
   float* part_ml;         // workspace: [slots][M][2]  (m in log2 units, l)
   int32_t* seg_cnt;       // workspace: [B * Hkv] arrivals of a segment's pieces
   int in_splits;          // > 0: q, k_new, v_new are fp32 K-split partial products
+  int fp8;                // caches hold fp8 E4M3 codes seen through per-channel scales
+  const float* k_scale;   // fp8: [Hkv, D] scales of the key cache (also the values when K = V)
+  const float* v_scale;   // fp8: [Hkv, D] scales of the value cache
   int part_acc_bytes, part_ml_bytes;
   int32_t* dev_status;
   int64_t cap;
@@ -284,6 +287,35 @@ __device__ __forceinline__ double rope_elem(const InView& src, int64_t head_off,
   return x * cs + ld_in<T>(src, head_off + d - half) * sn;
 }
 
+// fp8 E4M3 code of a finite fp32 value: round to nearest with ties to even, values
+// beyond +-448 (the largest finite E4M3 magnitude) saturating; NaN gives 0x7F.
+// The quotient by the binade's quantum (2^(e-3), or 2^-9 below 2^-6) is exact, so
+// rintf does the rounding; a value that rounds up to the next binade gets its code.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a > 448.f) return sign | 0x7Eu;
+  int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+  if (e < -6) e = -6;
+  const float v = ldexpf(rintf(ldexpf(a, 3 - e)), e - 3);   // <= 448: 448 is on every grid above
+  if (v < 0.015625f) return sign | (uint32_t)ldexpf(v, 9);  // subnormal: m 2^-9
+  const uint32_t u = __float_as_uint(v);
+  return sign | ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);  // exponent bias 127 -> 7
+}
+
+// an appended cache element: bf16 rounding as in a bf16 cache, then (fp8) the code
+// of value / scale, the quotient correctly rounded in fp32
+__device__ __forceinline__ void st_cache(const AttnParams& p, void* base, const float* scale, int64_t i, int sidx,
+                                         double v) {
+  const uint32_t bits = f32_to_bf16_bits(__double2float_rn(v));
+  if (!p.fp8) {
+    ((uint16_t*)base)[i] = (uint16_t)bits;
+    return;
+  }
+  ((uint8_t*)base)[i] = (uint8_t)e4m3_code(__fdiv_rn(bf16_to_f32((uint16_t)bits), scale[sidx]));
+}
+
 // one workgroup per (sequence, row, head); one thread per element of the head
 template <typename T>
 __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
@@ -320,13 +352,16 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
     const InView kv{p.k_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits};
-    st_elem<T>(p.k_cache, dst + d, rope_elem<T>(kv, src, d, p.rope_dims, p.log2_base, pos));
+    const double kr = rope_elem<T>(kv, src, d, p.rope_dims, p.log2_base, pos);
+    if constexpr (sizeof(T) == 2) st_cache(p, p.k_cache, p.k_scale, dst + d, h * D + d, kr);
+    else st_elem<T>(p.k_cache, dst + d, kr);
   } else {
     const int h = hs - p.Hq - p.Hkv;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
     const InView vv{p.v_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits};
-    st_elem<T>(p.v_cache, dst + d, ld_in<T>(vv, src + d));
+    if constexpr (sizeof(T) == 2) st_cache(p, p.v_cache, p.v_scale, dst + d, h * D + d, ld_in<T>(vv, src + d));
+    else st_elem<T>(p.v_cache, dst + d, ld_in<T>(vv, src + d));
   }
 }
 
@@ -362,14 +397,14 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 
 // segment to finish; a large one by attn_merge, which spreads the work over the chip.
 constexpr bool attn_fuse_merge(int D, int MT) { return D * 16 * MT <= 4096; }
 
-template <int D, int MT, bool KV_SAME>
+template <int D, int MT, bool KV_SAME, bool FP8>
 struct AttnCfg {
   static constexpr int DS = D / 4;              // PV dims per wave
   static constexpr int KS = D / 32;             // 32-dim k-steps of QK (full head)
   static constexpr int DT = DS / 16;            // 16-dim output tiles of PV per wave
   static constexpr int TK = 64;                 // keys per tile (16 per wave)
-  static constexpr int ROWB = D * 2;            // bytes per key row
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int ROWB = FP8 ? D : D * 2;  // bytes per key row (fp8 codes or bf16)
+  static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;          // rows per DMA instruction
   static constexpr int NTEN = KV_SAME ? 1 : 2;  // staged tensors
   static constexpr int TILEB = TK * ROWB;
@@ -383,9 +418,23 @@ struct AttnCfg {
   static_assert((NS - 2) * NI <= 63, "vmcnt range");
 };
 
-template <int D, int MT, bool KV_SAME>
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+
+// eight fp8 E4M3 codes (byte e = element e) as eight bf16 values (exact: every
+// E4M3 value is a bf16 value)
+__device__ __forceinline__ V16 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  V16 r;
+  r.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false));
+  r.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true));
+  r.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false));
+  r.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true));
+  return r;
+}
+
+template <int D, int MT, bool KV_SAME, bool FP8>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
-  using C = AttnCfg<D, MT, KV_SAME>;
+  using C = AttnCfg<D, MT, KV_SAME, FP8>;
   constexpr int DS = C::DS, KS = C::KS, DT = C::DT, TK = C::TK, ROWB = C::ROWB, CPR = C::CPR,
                 RPI = C::RPI, TILEB = C::TILEB, STAGEB = C::STAGEB, NI = C::NI, NS = C::NS;
 
@@ -418,8 +467,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   piece_locate(p, bl, pc.chunk, slot, b, kvh, a0, a1, first, count);
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
-  const uint16_t* kcache = (const uint16_t*)p.k_cache;
-  const uint16_t* vcache = (const uint16_t*)p.v_cache;
+  const unsigned char* kcache = (const unsigned char*)p.k_cache;
+  const unsigned char* vcache = (const unsigned char*)p.v_cache;
   {
     {
       const int64_t L = p.cache_len[b];
@@ -451,7 +500,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           const int ii = wave * NI + jj;
           const int ten = ii / (TK / RPI);
           const int rb = ii % (TK / RPI);
-          const uint16_t* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
+          const unsigned char* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
           const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + ten * TILEB + rb * RPI * ROWB));
           int64_t brow = t0 + rb * RPI;  // first row of the block
           uint32_t off = off_pre[jj];
@@ -462,7 +511,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             if (key > a1 - 1) key = a1 - 1;
             off = (uint32_t)((key - brow) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
           }
-          dma16((const void*)(tbase + (head_row0 + brow) * D), off, lds);
+          dma16((const void*)(tbase + (head_row0 + brow) * ROWB), off, lds);
         }
       };
       auto issue = [&](int t, unsigned char* stage) __attribute__((always_inline)) {
@@ -491,6 +540,19 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           const uint16_t* src = qrot + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + lg * 8;
 #pragma unroll
           for (int s = 0; s < KS; ++s) qreg[lt][s].u = *(const uint4*)(src + s * 32);
+          if constexpr (FP8) {
+            // fp8 keys are scale * code: the per-channel key scales are folded into the
+            // queries (rounded to bf16), so the products take the codes as they are
+            const float* ksc = p.k_scale + kvh * D + lg * 8;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+              const f32x4_t a = *(const f32x4_t*)(ksc + s * 32), c = *(const f32x4_t*)(ksc + s * 32 + 4);
+              const float sc[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                qreg[lt][s].w[e] = pack_bf16x2(bf16_lo(qreg[lt][s].w[e]) * sc[2 * e], bf16_hi(qreg[lt][s].w[e]) * sc[2 * e + 1]);
+            }
+          }
         } else {
 #pragma unroll
           for (int s = 0; s < KS; ++s) qreg[lt][s].u = make_uint4(0, 0, 0, 0);
@@ -516,7 +578,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       }
 
       for (int tb = 0; tb < ntiles; tb += NS) {
-#pragma unroll
+#pragma unroll (FP8 ? 1 : NS)
       for (int u = 0; u < NS; ++u) {
         const int t = tb + u;  // tile t lives in stage u
         if (t >= ntiles) break;
@@ -543,7 +605,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         // chains over alternate k-steps keep the MFMA pipe busy.
         constexpr int NCH = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
         constexpr int PER = (NI + KS - 1) / KS;  // DMA instructions per k-step
-        constexpr int KPF = KS < 4 ? KS : 4;
+        constexpr int KPF = FP8 ? (KS < 2 ? KS : 2) : (KS < 4 ? KS : 4);
         int pkt[MT], pmt[MT];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
@@ -566,11 +628,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             krow[j] = kst + r * ROWB;
             sw[j] = swz(r);
           }
-          V16 kq[KPF][MT];
+          // key operands: 8 dims of a key row per lane (16 bytes of bf16, or 8 fp8 codes
+          // widened to bf16 when used)
+          auto kaddr = [&](int s, int j) -> const unsigned char* {
+            if constexpr (FP8) return krow[j] + (((2 * s + (lg >> 1)) ^ sw[j]) << 4) + ((lg & 1) << 3);
+            else return krow[j] + (((4 * s + lg) ^ sw[j]) << 4);
+          };
+          using KQ = typename std::conditional<FP8, uint2, uint4>::type;
+          KQ kq[KPF][MT];
 #pragma unroll
           for (int s = 0; s < KPF; ++s)
 #pragma unroll
-            for (int j = 0; j < MT; ++j) kq[s][j].u = *(const uint4*)(krow[j] + (((4 * s + lg) ^ sw[j]) << 4));
+            for (int j = 0; j < MT; ++j) kq[s][j] = *(const KQ*)kaddr(s, j);
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             if constexpr (DMA) {
@@ -581,8 +650,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
                   const int ii = wave * NI + jj;
                   const int ten = ii / (TK / RPI);
                   const int rb = ii % (TK / RPI);
-                  const uint16_t* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
-                  dma16<false>((const void*)(tbase + (head_row0 + tn0 + rb * RPI) * D), off_pre[jj],
+                  const unsigned char* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
+                  dma16<false>((const void*)(tbase + (head_row0 + tn0 + rb * RPI) * ROWB), off_pre[jj],
                                lds_addr(nstage + ten * TILEB + rb * RPI * ROWB));
                 }
               }
@@ -590,8 +659,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             V16 kreg[MT];
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
-              kreg[j] = kq[s % KPF][j];
-              if (s + KPF < KS) kq[s % KPF][j].u = *(const uint4*)(krow[j] + (((4 * (s + KPF) + lg) ^ sw[j]) << 4));
+              if constexpr (FP8) kreg[j] = fp8x8_to_bf16(kq[s % KPF][j].x, kq[s % KPF][j].y);
+              else kreg[j].u = kq[s % KPF][j];
+              if (s + KPF < KS) kq[s % KPF][j] = *(const KQ*)kaddr(s + KPF, j);
             }
 #pragma unroll
             for (int j = 0; j < MT; ++j) {
@@ -599,7 +669,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
               sch[s % NCH][j] = mfma16x16x32(kreg[j].b, qv, sch[s % NCH][j]);
             }
           }
-          {
+          if constexpr (FP8) {
+            // keep KPF k-steps of key reads ahead; each step's codes are widened right
+            // before its MFMAs, so only one step of widened operands is live
+            __builtin_amdgcn_sched_group_barrier(0x100, KPF * MT, 0);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+              __builtin_amdgcn_sched_group_barrier(0x002, 4 * MT, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+              if (s + KPF < KS) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+            }
+          } else {
             // keep KPF k-steps of key reads ahead of the MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, KPF * MT, 0);
 #pragma unroll
@@ -732,6 +812,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             }
             // value operands are read one dim tile ahead of their MFMAs
             auto read_v = [&](int dt) {
+              if constexpr (FP8) {
+                // 8-bit transpose read: lane 2k + h of the 16-lane group points at key
+                // slot k, dims 16 c16 + 8h; lane i gets dim 16 c16 + i of the 8 keys
+                const int c16 = wave * (DS / 16) + dt;
+                const int k = i >> 1;
+                const int r = 32 * ks + 16 * (k >> 2) + 4 * lg + (k & 3);
+                const unsigned char* ad = vst + r * ROWB + ((c16 ^ swz(r)) << 4) + ((i & 1) << 3);
+                const v2i_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)ad);
+                return fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1]);
+              }
               const int c = wave * (DS / 8) + 2 * dt + (a >> 1);
               V16 av;
 #pragma unroll
@@ -758,6 +848,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       }
       }
 
+      if constexpr (FP8) {
+        // values are scale * code: the per-channel value scales multiply the output
+        const float* vsc = (KV_SAME ? p.k_scale : p.v_scale) + kvh * D + wave * DS + lg * 4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4_t sc = *(const f32x4_t*)(vsc + dt * 16);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            O[dt][mt][0] *= sc[0]; O[dt][mt][1] *= sc[1]; O[dt][mt][2] *= sc[2]; O[dt][mt][3] *= sc[3];
+          }
+        }
+      }
       // ---- unnormalised partial of this piece: the row sums of the four waves
       // (each over its own keys, all on the same reference) add up
 #pragma unroll
@@ -1066,23 +1168,35 @@ static int validate_attn(const sv_attn_desc* d) {
   return SV_OK;
 }
 
-template <int D, int MT, bool KVS>
+template <int D, int MT, bool KVS, bool FP8>
 static void launch_mfma(const AttnParams& p, hipStream_t s) {
   // one workgroup per piece: at most nwg pieces, or one per segment when there are more segments
   const int grid = p.nwg > p.B * p.Hkv ? p.nwg : p.B * p.Hkv;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, MT, KVS>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, MT, KVS, FP8>), dim3(grid), dim3(256), 0, s, p);
 }
 
-template <int D, bool KVS>
+template <int D, bool KVS, bool FP8>
 static int dispatch_mfma(const AttnParams& p, int MT, hipStream_t s) {
   switch (MT) {
-    case 1: launch_mfma<D, 1, KVS>(p, s); break;
-    case 2: launch_mfma<D, 2, KVS>(p, s); break;
-    case 3: launch_mfma<D, 3, KVS>(p, s); break;
-    case 4: launch_mfma<D, 4, KVS>(p, s); break;
+    case 1: launch_mfma<D, 1, KVS, FP8>(p, s); break;
+    case 2: launch_mfma<D, 2, KVS, FP8>(p, s); break;
+    case 3: launch_mfma<D, 3, KVS, FP8>(p, s); break;
+    case 4: launch_mfma<D, 4, KVS, FP8>(p, s); break;
     default: return SV_ERR_UNSUPPORTED;
   }
   return SV_OK;
+}
+
+template <bool FP8>
+static int dispatch_attn(const sv_attn_desc* d, const AttnParams& p, int MT, hipStream_t s) {
+  switch (d->head_dim * 2 + (d->k_is_v ? 1 : 0)) {
+    case 256: return dispatch_mfma<128, false, FP8>(p, MT, s);
+    case 257: return dispatch_mfma<128, true, FP8>(p, MT, s);
+    case 512: return dispatch_mfma<256, false, FP8>(p, MT, s);
+    case 513: return dispatch_mfma<256, true, FP8>(p, MT, s);
+    case 1025: return dispatch_mfma<512, true, FP8>(p, MT, s);
+    default: return SV_ERR_UNSUPPORTED;
+  }
 }
 
 }  // namespace sv
@@ -1094,12 +1208,17 @@ extern "C" size_t sv_verify_attn_workspace(const sv_attn_desc* d) {
   return attn_plan(*d).total;
 }
 
-extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* k_new,
-                              const void* v_new, void* k_cache, void* v_cache,
-                              const int32_t* cache_len, void* out, void* workspace,
-                              size_t workspace_bytes, int32_t* dev_status, void* stream) {
+static int verify_attn(const sv_attn_desc* d, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, const float* k_scale, const float* v_scale, bool fp8,
+                       const int32_t* cache_len, void* out, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_status, void* stream) {
   int rc = validate_attn(d);
   if (rc != SV_OK) return rc;
+  if (fp8) {
+    if (d->dtype != SV_BF16) return SV_ERR_ARG;
+    if (!k_scale || ((uintptr_t)k_scale & 15)) return SV_ERR_ARG;
+    if (d->k_is_v ? v_scale != nullptr : (!v_scale || ((uintptr_t)v_scale & 15))) return SV_ERR_ARG;
+  }
   if (!q || !k_cache || !cache_len || !out) return SV_ERR_ARG;
   if (d->append && !k_new) return SV_ERR_ARG;
   if (!d->append && (k_new || v_new)) return SV_ERR_ARG;
@@ -1148,6 +1267,9 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
   p.nwg = device_cus();
   p.min_chunk = 64;
   p.in_splits = d->in_splits;
+  p.fp8 = fp8 ? 1 : 0;
+  p.k_scale = k_scale;
+  p.v_scale = d->k_is_v ? k_scale : v_scale;
 
   hipStream_t s = (hipStream_t)stream;
   const int heads = d->n_heads_q + (d->append ? d->n_heads_kv * (d->k_is_v ? 1 : 2) : 0);
@@ -1155,14 +1277,7 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
   if (d->dtype == SV_BF16) {
     hipLaunchKernelGGL(rope_append_kernel<uint16_t>, dim3(d->batch * d->n_q, heads), dim3(rope_threads), 0, s, p);
     const int MT = (pl.M + 15) / 16;
-    switch (d->head_dim * 2 + (d->k_is_v ? 1 : 0)) {
-      case 256: rc = dispatch_mfma<128, false>(p, MT, s); break;
-      case 257: rc = dispatch_mfma<128, true>(p, MT, s); break;
-      case 512: rc = dispatch_mfma<256, false>(p, MT, s); break;
-      case 513: rc = dispatch_mfma<256, true>(p, MT, s); break;
-      case 1025: rc = dispatch_mfma<512, true>(p, MT, s); break;
-      default: rc = SV_ERR_UNSUPPORTED;
-    }
+    rc = fp8 ? dispatch_attn<true>(d, p, MT, s) : dispatch_attn<false>(d, p, MT, s);
     if (rc != SV_OK) return rc;
     if (!attn_fuse_merge(d->head_dim, MT))
       // (at least one full wave: the piece plan works across 64 lanes)
@@ -1173,4 +1288,20 @@ extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* 
     hipLaunchKernelGGL(attn_f32_kernel, dim3(d->n_heads_q, d->n_q, d->batch), dim3(256), 0, s, p);
   }
   return launch_status();
+}
+
+extern "C" int sv_verify_attn(const sv_attn_desc* d, const void* q, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* cache_len, void* out, void* workspace,
+                              size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  return verify_attn(d, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr, false, cache_len, out, workspace,
+                     workspace_bytes, dev_status, stream);
+}
+
+extern "C" int sv_verify_attn_fp8(const sv_attn_desc* d, const void* q, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                                  const int32_t* cache_len, void* out, void* workspace, size_t workspace_bytes,
+                                  int32_t* dev_status, void* stream) {
+  return verify_attn(d, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, true, cache_len, out, workspace,
+                     workspace_bytes, dev_status, stream);
 }
