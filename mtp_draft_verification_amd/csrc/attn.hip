@@ -438,8 +438,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   constexpr int DS = C::DS, KS = C::KS, DT = C::DT, TK = C::TK, ROWB = C::ROWB, CPR = C::CPR,
                 RPI = C::RPI, TILEB = C::TILEB, STAGEB = C::STAGEB, NI = C::NI, NS = C::NS;
 
-  // one LDS object per ring stage: with the tile loop unrolled by NS every access
-  // names its stage statically
+  // one LDS object per ring stage (the stage loop is kept rolled: unrolling it by NS
+  // lets the scheduler stretch live ranges across stages and costs spills)
   __shared__ __attribute__((aligned(16))) unsigned char s_st0[STAGEB];
   __shared__ __attribute__((aligned(16))) unsigned char s_st1[STAGEB];
   __shared__ __attribute__((aligned(16))) unsigned char s_st2[NS > 2 ? STAGEB : 16];
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       }
 
       for (int tb = 0; tb < ntiles; tb += NS) {
-#pragma unroll (FP8 ? 1 : NS)
+#pragma unroll 1
       for (int u = 0; u < NS; ++u) {
         const int t = tb + u;  // tile t lives in stage u
         if (t >= ntiles) break;
