@@ -79,10 +79,15 @@ def bench_only(args):
 
 
 def bench_one(args, only):
+    print(json.dumps(time_one(args, only)), flush=True)
+
+
+def time_one(args, only) -> dict:
     """One call of the verify step, timed alone at the workload's shapes (batch,
     k, context): the global-layer attention (16q/4kv, D=512, K=V, p-RoPE), a local
-    layer's attention (16q/8kv, D=256, window 1024), the LM-head select, or one of
-    a layer's projections (fused q/k/v, output, gate/up, down)."""
+    layer's attention (16q/8kv, D=256, window 1024), either over an fp8 cache
+    (suffix _fp8), the LM-head select, or one of a layer's projections (fused
+    q/k/v, output, gate/up, down)."""
     import torch
 
     from mtp_draft_verification_amd import _lib as L
@@ -174,9 +179,23 @@ def bench_one(args, only):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.iters
     gbs = byts / (us * 1e-6) / 1e9
-    print(json.dumps({"call": only, "batch": B, "k": cfg.k, "ctx": cfg.ctx, "us_per_call": round(us, 2),
-                      "alg_bytes": int(byts), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-                      "source_digest": source_digest()}), flush=True)
+    return {"call": only, "batch": B, "k": cfg.k, "ctx": cfg.ctx, "us_per_call": round(us, 2),
+            "alg_bytes": int(byts), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "source_digest": source_digest()}
+
+
+def bench_fp8_kv(args) -> dict:
+    """The attention calls of the step over fp8 E4M3 caches (per-channel scales)
+    next to the same calls over bf16 caches, each timed alone (context, batch and
+    k of the workload)."""
+    res = {}
+    for layer in ("global", "local"):
+        a = time_one(args, f"attn_{layer}_fp8")
+        b = time_one(args, f"attn_{layer}")
+        res[layer] = {"us": a["us_per_call"], "alg_bytes": a["alg_bytes"], "GB/s": a["GB/s"],
+                      "frac": a["frac_of_peak"], "bf16_us": b["us_per_call"],
+                      "speedup_vs_bf16": round(b["us_per_call"] / a["us_per_call"], 3)}
+    return res
 
 
 def source_digest() -> str:
@@ -566,6 +585,11 @@ def main():
         drafter = bench_drafter(cfg, W, main_res["caches"], main_res["first_len"], dev)
         log(f"drafter: {drafter['ms_per_k_steps']:.3f} ms per {cfg.k} steps")
 
+    fp8_kv = None
+    if not args.profile:
+        fp8_kv = bench_fp8_kv(args)
+        log(f"fp8 KV: global attention {fp8_kv['global']['us']} us (bf16 {fp8_kv['global']['bf16_us']} us)")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, W, main_res["caches"], main_res["first_tokens"], main_res["first_len"], dev)
@@ -588,6 +612,7 @@ def main():
         "mean_accepted": round(main_res["mean_accepted"], 3),
         "kernels": kern,
         "drafter": drafter,
+        "fp8_kv_attention": fp8_kv,
         "source_digest": source_digest(),
     }
     print(json.dumps(out), flush=True)
