@@ -90,6 +90,15 @@ def lib():
         L.svo_sample_bonus.argtypes = [i64, P, P, ctypes.POINTER(f64)]
         L.svo_sample_bonus.restype = ctypes.c_int
         L.svo_toy_spec_trials.argtypes = [i64, ctypes.c_int, i64, P, P, P, P, P, P, P]
+        u64 = ctypes.c_uint64
+        L.svo_philox4x64.argtypes = [P, P, P]
+        L.svo_rs_uniform.restype = f64
+        L.svo_rs_uniform.argtypes = [u64, u64, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int]
+        L.svo_rs_candidates.argtypes = [i64, P, u64, u64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+        L.svo_rs_accept.restype = ctypes.c_int
+        L.svo_rs_accept.argtypes = [ctypes.c_int, P, P, f64, P, P, P]
+        L.svo_toy_spec_trials_rs.argtypes = [i64, ctypes.c_int, i64, P, P, P, P, P, u64, u64, ctypes.c_int, P, P, P,
+                                             P]
         _lib = L
     return _lib
 
@@ -339,6 +348,54 @@ def sample_bonus(z_row, u_row) -> tuple[int, float]:
     m = ctypes.c_double()
     y = lib().svo_sample_bonus(z.size, _ptr(z), _ptr(u), ctypes.byref(m))
     return int(y), float(m.value)
+
+
+def philox4x64(ctr, key) -> np.ndarray:
+    """One Philox4x64-10 block: counter [4] and key [2] uint64 -> 4 uint64."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    o = np.zeros(4, dtype=np.uint64)
+    lib().svo_philox4x64(_ptr(c), _ptr(k), _ptr(o))
+    return o
+
+
+def rs_uniform(key, b: int, i: int, v: int, r: int) -> float:
+    return float(lib().svo_rs_uniform(int(key[0]), int(key[1]), int(b), int(i), int(v), int(r)))
+
+
+def rs_candidates(z_row, key, b: int, i: int, R: int = 4) -> tuple[np.ndarray, np.ndarray]:
+    """R draws from softmax(z_row) for draft row (b, i) under `key` (2 uint64):
+    (token ids [R], Gumbel margins [R])."""
+    z = _f64(z_row)
+    cand = np.empty(R, dtype=np.int32)
+    margin = np.empty(R, dtype=np.float64)
+    lib().svo_rs_candidates(z.size, _ptr(z), int(key[0]), int(key[1]), int(b), int(i), int(R), _ptr(cand),
+                            _ptr(margin))
+    return cand, margin
+
+
+def rs_accept(cand, z_row, lse: float, q_row, u_rs) -> tuple[int, np.ndarray]:
+    """Residual by rejection over the candidates: (token or -1, margins [R])."""
+    c, z, q, u = _i32(cand), _f64(z_row), _f32(q_row), _f32(u_rs)
+    margin = np.full(c.size, np.nan, dtype=np.float64)
+    y = lib().svo_rs_accept(c.size, _ptr(c), _ptr(z), float(lse), _ptr(q), _ptr(u), _ptr(margin))
+    return int(y), margin
+
+
+def toy_spec_trials_rs(z, q, drafts, u_acc, u_tok, key, u_rs) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """toy_spec_trials with single-pass sampling (see svo_toy_spec_trials_rs).
+    Returns (n [T], y [T], fallback used [T])."""
+    z, q = _f64(z), _f32(q)
+    d, ua, ut, ur = _i32(drafts), _f32(u_acc), _f32(u_tok), _f32(u_rs)
+    T, k = d.shape
+    V = z.size
+    R = ur.shape[1]
+    n = np.empty(T, dtype=np.int32)
+    y = np.empty(T, dtype=np.int32)
+    fb = np.empty(T, dtype=np.int32)
+    lib().svo_toy_spec_trials_rs(T, k, V, _ptr(z), _ptr(q), _ptr(d), _ptr(ua), _ptr(ut), int(key[0]), int(key[1]),
+                                 R, _ptr(ur), _ptr(n), _ptr(y), _ptr(fb))
+    return n, y, fb
 
 
 def toy_spec_trials(z, q, drafts, u_acc, u_tok) -> tuple[np.ndarray, np.ndarray]:

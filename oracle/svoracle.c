@@ -429,6 +429,81 @@ int svo_sample_bonus(int64_t V, const double* z, const float* u, double* margin)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Single-pass sampling: candidates drawn from p in the first pass, the      */
+/* residual reached by rejection                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds of two
+ * 64 x 64 -> 128-bit products of the even counter words with the round
+ * multipliers, the high halves xored with the odd words and the key, the key
+ * bumped by the Weyl constants between rounds. */
+void svo_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += W0; k1 += W1; }
+    const unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
+    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Uniform r (0..3) of token v for draft row i of sequence b: the Philox block
+ * with counter (v / 2, i, b, 0) and key (key0, key1) serves tokens 2m and 2m+1;
+ * token v takes words 2 (v % 2) and 2 (v % 2) + 1, uniform r the low (r even) or
+ * high (r odd) 32 bits of word 2 (v % 2) + r / 2.  Bits x become the open-interval
+ * uniform ((x >> 9) + 1/2) 2^-23, exact in fp32. */
+double svo_rs_uniform(uint64_t key0, uint64_t key1, int b, int i, int64_t v, int r) {
+  const uint64_t ctr[4] = {(uint64_t)(v >> 1), (uint64_t)i, (uint64_t)b, 0};
+  const uint64_t key[2] = {key0, key1};
+  uint64_t o[4];
+  svo_philox4x64(ctr, key, o);
+  const uint64_t w = o[2 * (v & 1) + (r >> 1)];
+  const uint32_t x = (r & 1) ? (uint32_t)(w >> 32) : (uint32_t)w;
+  return ((double)(x >> 9) + 0.5) * ldexp(1.0, -23);
+}
+
+/* R independent draws from p = softmax(z) for draft row (b, i), each by
+ * Gumbel-max with its own uniforms: cand[r] = argmax_v z_v + G(u_r(v)) (ties:
+ * lowest id), margin[r] = best score - second best. */
+void svo_rs_candidates(int64_t V, const double* z, uint64_t key0, uint64_t key1, int b, int i, int R,
+                       int32_t* cand, double* margin) {
+  for (int r = 0; r < R; ++r) {
+    int64_t b1 = -1;
+    double s1 = -INFINITY, s2 = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
+      const double sc = z[v] + gumbel(svo_rs_uniform(key0, key1, b, i, v, r));
+      if (b1 < 0 || sc > s1) { s2 = s1; b1 = v; s1 = sc; }
+      else if (sc > s2) { s2 = sc; }
+    }
+    cand[r] = (int32_t)b1;
+    margin[r] = s1 - s2;
+  }
+}
+
+/* Residual draw by rejection from the candidates of the rejected row: candidate
+ * x = cand[r] (a draw from p) is accepted iff u_rs[r] p(x) < p(x) - q(x), i.e.
+ * with probability max(0, 1 - q(x) / p(x)); an accepted draw is distributed as
+ * max(p - q, 0) normalised.  The first accepted candidate is returned, -1 if
+ * none is (the caller then draws the residual directly).  p(x) = exp(z_x - lse);
+ * margin[r] = (p - q - u p) for each tested candidate (its sign is the decision). */
+int svo_rs_accept(int R, const int32_t* cand, const double* z, double lse, const float* q_row,
+                  const float* u_rs, double* margin) {
+  for (int r = 0; r < R; ++r) {
+    const int32_t x = cand[r];
+    const double p = exp(z[x] - lse), q = (double)q_row[x];
+    margin[r] = (p - q) - (double)u_rs[r] * p;
+    if ((double)u_rs[r] * p < p - q) return x;
+  }
+  return -1;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Trial driver for the statistical pins of the sampling rule               */
 /* ------------------------------------------------------------------------ */
 
@@ -466,4 +541,49 @@ void svo_toy_spec_trials(int64_t T, int k, int64_t V, const double* z, const flo
     y_out[t] = y;
   }
   free(lse_rows); free(dl); free(qd); free(mg);
+}
+
+/* The same toy with single-pass sampling: after a rejection at row n the
+ * residual comes from R candidates of row n (svo_rs_candidates with key
+ * (key0 + t, key1), sequence 0) by svo_rs_accept, and only if all are refused
+ * from svo_sample_residual.  u_rs [T][R]; fb_out[t] = 1 when the fallback ran. */
+void svo_toy_spec_trials_rs(int64_t T, int k, int64_t V, const double* z, const float* q,
+                            const int32_t* drafts, const float* u_acc, const float* u_tok, uint64_t key0,
+                            uint64_t key1, int R, const float* u_rs, int32_t* n_out, int32_t* y_out,
+                            int32_t* fb_out) {
+  double m = -INFINITY, acc = 0.0;
+  for (int64_t v = 0; v < V; ++v) if (z[v] > m) m = z[v];
+  for (int64_t v = 0; v < V; ++v) acc += exp(z[v] - m);
+  const double lse = m + log(acc);
+  double* lse_rows = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+  double* dl = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+  float* qd = (float*)malloc(sizeof(float) * (size_t)(k > 0 ? k : 1));
+  double* mg = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+  int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
+  double* cm = (double*)malloc(sizeof(double) * (size_t)R);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int i = 0; i < k; ++i) {
+      int32_t d = drafts[t * k + i];
+      lse_rows[i] = lse;
+      dl[i] = z[d];
+      qd[i] = q[d];
+    }
+    int n = svo_accept_sample(k, lse_rows, dl, qd, u_acc + t * k, mg);
+    double margin;
+    int y, fb = 0;
+    if (n < k) {
+      svo_rs_candidates(V, z, key0 + (uint64_t)t, key1, 0, n, R, cand, cm);
+      y = svo_rs_accept(R, cand, z, lse, q, u_rs + t * R, cm);
+      if (y < 0) {
+        fb = 1;
+        y = svo_sample_residual(V, z, lse, q, u_tok + t * V, &margin);
+      }
+    } else {
+      y = svo_sample_bonus(V, z, u_tok + t * V, &margin);
+    }
+    n_out[t] = n;
+    y_out[t] = y;
+    fb_out[t] = fb;
+  }
+  free(lse_rows); free(dl); free(qd); free(mg); free(cand); free(cm);
 }

@@ -506,6 +506,80 @@ def test_rejection_sampling_reproduces_target_distribution(k):
     assert abs(rate - expect) < 5 * math.sqrt(expect * (1 - expect) / T)
 
 
+def test_philox4x64_matches_the_library_generator():
+    # numpy's Philox bit generator is Philox4x64-10; it advances its counter before
+    # producing a block, so its first block belongs to counter + 1
+    rng = np.random.default_rng(31)
+    for _ in range(5):
+        ctr = rng.integers(1, 2 ** 63, size=4, dtype=np.uint64)
+        key = rng.integers(0, 2 ** 63, size=2, dtype=np.uint64)
+        start = ctr.copy()
+        start[0] -= np.uint64(1)
+        lib = np.random.Philox(counter=start, key=key).random_raw(4)
+        np.testing.assert_array_equal(oracle.philox4x64(ctr, key), lib)
+
+
+def test_rs_uniform_layout():
+    # token v of draft row (b, i): block (v // 2, i, b, 0); words 2 (v % 2) + r // 2,
+    # low half for even r; ((x >> 9) + 1/2) 2^-23
+    key = (0x1234, 0xABCD)
+    for (b, i, v, r) in ((0, 0, 2, 0), (3, 2, 7, 1), (1, 3, 262143, 2), (5, 0, 1000, 3), (2, 1, 3, 3)):
+        start = np.array([v // 2 - 1, i, b, 0], dtype=np.uint64)   # the generator steps first
+        blk = np.random.Philox(counter=start, key=np.array(key, dtype=np.uint64)).random_raw(4)
+        w = int(blk[2 * (v % 2) + r // 2])
+        x = (w >> 32) if r % 2 else (w & 0xFFFFFFFF)
+        assert oracle.rs_uniform(key, b, i, v, r) == ((x >> 9) + 0.5) * 2.0 ** -23
+
+
+def test_rs_candidates_are_draws_from_p():
+    """Each candidate is an exact draw from softmax(z): chi-square over many keys,
+    per candidate slot, and the four slots of one key are independent draws."""
+    V = 8
+    z = np.array([1.0, 0.2, -0.5, 2.0, 0.0, -1.5, 0.7, 1.2])
+    p = special.softmax(z)
+    T = 20000
+    cands = np.array([oracle.rs_candidates(z, (7 + t, 99), 0, 1, 4)[0] for t in range(T)])
+    for r in range(4):
+        cnt = np.bincount(cands[:, r], minlength=V)
+        chi2, pval = stats.chisquare(cnt, T * p)
+        assert pval > 0.001, (r, chi2, pval)
+    same = (cands[:, 0] == cands[:, 1]).mean()
+    assert abs(same - (p ** 2).sum()) < 5 * math.sqrt((p ** 2).sum() / T)
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_single_pass_sampling_reproduces_target_distribution(k):
+    """Residual by rejection over first-pass candidates, with the direct residual draw
+    as fallback, emits exactly p: chi-square on a vocab-16 toy; the fallback rate is
+    (1 - alpha)^R with alpha = sum_v max(0, p_v - q_v)."""
+    V, T, R = 16, 200_000, 4
+    z, q = _toy_pq(V)
+    p = special.softmax(z)
+    rng = np.random.default_rng(200 + k)
+    drafts = _draws(q, (T, k), rng).astype(np.int32)
+    u_acc = rng.random((T, k), dtype=np.float32)
+    u_tok = rng.random((T, V), dtype=np.float32)
+    u_rs = rng.random((T, R), dtype=np.float32)
+    n, y, fb = oracle.toy_spec_trials_rs(z, q, drafts, u_acc, u_tok, (1000 * k, 5), u_rs)
+    first = np.where(n >= 1, drafts[:, 0], y)
+    cnt = np.bincount(first, minlength=V)
+    chi2, pval = stats.chisquare(cnt, T * p)
+    assert pval > 0.01, (chi2, pval)
+    # the target's own token after a rejection follows the residual max(p - q, 0)
+    res = np.maximum(p - q.astype(np.float64), 0.0)
+    res /= res.sum()
+    rej = n < k
+    cnt = np.bincount(y[rej], minlength=V)
+    keep = res > 0
+    assert cnt[~keep].sum() == 0
+    chi2, pval = stats.chisquare(cnt[keep], rej.sum() * res[keep])
+    assert pval > 0.01, (chi2, pval)
+    alpha = np.maximum(p - q.astype(np.float64), 0.0).sum()
+    rate = fb[rej].mean()
+    expect = (1 - alpha) ** R
+    assert abs(rate - expect) < 5 * math.sqrt(expect * (1 - expect) / rej.sum())
+
+
 def test_sampling_special_cases():
     V, T = 16, 20000
     z, _ = _toy_pq(V, 1)
