@@ -66,6 +66,7 @@ def parse():
 
 
 ONLY_CALLS = ("attn_global", "attn_local", "attn_global_fp8", "attn_local_fp8", "lmhead", "lmhead_sample",
+              "lmhead_sample_rs",
               "qkv_local", "qkv_global", "o_local", "o_global", "gu", "down", "hbm_copy")
 COPY_BYTES = 1 << 30  # hbm_copy: a plain 1 GiB device-to-device copy (counter calibration)
 
@@ -126,16 +127,21 @@ def time_one(args, only) -> dict:
         lens = [cfg.ctx] * B
         byts = call_bytes(cfg, lens, 1 if fp8 else 2)["L5.attn" if ly.window == 0 else "L0.attn"]
     elif only.startswith("lmhead"):
-        mode = L.SV_SELECT_GREEDY if only == "lmhead" else L.SV_SELECT_SAMPLE
+        mode = {"lmhead": L.SV_SELECT_GREEDY, "lmhead_sample": L.SV_SELECT_SAMPLE,
+                "lmhead_sample_rs": L.SV_SELECT_SAMPLE_RS}[only]
         R = B * nq
         h = inputs.normal((R, cfg.d_model), 1.0, 0, "h", dev)
         W = inputs.normal((cfg.vocab, cfg.d_model), cfg.d_model ** -0.5, 0, "E", dev)
         drafts = torch.randint(0, cfg.vocab, (B, cfg.k), dtype=torch.int32, device=dev)
-        u_tok = torch.rand((B, cfg.vocab), device=dev) if mode == L.SV_SELECT_SAMPLE else None
+        u_tok = torch.rand((B, cfg.vocab), device=dev) if mode != L.SV_SELECT_GREEDY else None
         desc = L.LMHeadDesc(batch=B, k=cfg.k, d_model=cfg.d_model, vocab=cfg.vocab, mode=mode, dtype=L.SV_BF16)
         ws = torch.zeros(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
         stats = torch.empty((R, L.ROW_STATS_WORDS), dtype=torch.int32, device=dev)
-        call = lambda: L.sv_lmhead_select(desc, h, W, drafts, u_tok, None, stats, None, None, ws, stream)
+        if mode == L.SV_SELECT_SAMPLE_RS:
+            cands = torch.empty((B * cfg.k * L.RS_CANDIDATES, L.RS_CAND_WORDS), dtype=torch.int32, device=dev)
+            call = lambda: L.sv_lmhead_select_rs(desc, h, W, drafts, u_tok, 1, 2, stats, cands, None, ws, stream)
+        else:
+            call = lambda: L.sv_lmhead_select(desc, h, W, drafts, u_tok, None, stats, None, None, ws, stream)
         byts = call_bytes(cfg, [cfg.ctx] * B)["lmhead"]
     elif only == "hbm_copy":
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)

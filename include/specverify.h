@@ -155,7 +155,9 @@ int sv_verify_attn_fp8(const sv_attn_desc* desc, const void* q, const void* k_ne
 typedef enum {
   SV_SELECT_GREEDY = 0,    /* per-row argmax statistics */
   SV_SELECT_SAMPLE = 1,    /* GREEDY + a Gumbel-max draw from softmax(z) on bonus rows */
-  SV_SELECT_RESIDUAL = 2   /* draw from max(p - q, 0) for sequences that rejected */
+  SV_SELECT_RESIDUAL = 2,  /* draw from max(p - q, 0) for sequences that rejected */
+  SV_SELECT_SAMPLE_RS = 3  /* SAMPLE + first-pass candidates for single-pass sampling
+                              (sv_lmhead_select_rs, sv_accept_rs) */
 } sv_select_mode;
 
 /* Per-row result of the LM head (logits themselves are never written). */
@@ -167,6 +169,16 @@ typedef struct {
   int32_t sample_id;         /* SAMPLE, bonus rows: argmax_v z_v + G(u_v); else -1 */
   float sample_s1, sample_s2;/* winning and runner-up perturbed scores */
 } sv_row_stats;
+
+/* One first-pass candidate of single-pass sampling: a draw from p = softmax(z) of a
+ * draft row by Gumbel-max over counter-based uniforms. */
+typedef struct {
+  int32_t id;            /* the drawn token */
+  float z;               /* its logit (p(id) = exp(z - lse of the row)) */
+  float s1, s2;          /* winning and runner-up perturbed scores */
+  int32_t pad;
+} sv_rs_cand;
+#define SV_RS_CANDIDATES 4
 
 /* Per-sequence result of the accept step. */
 typedef struct {
@@ -227,6 +239,22 @@ int sv_lmhead_select(const sv_lmhead_desc* desc, const void* hidden, const void*
                      const int32_t* drafts, const float* u_tok, const float* q_rows,
                      sv_row_stats* stats, sv_accept_out* acc, int32_t* out_tokens,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Single-pass sampling, first pass (the rejection of speculative sampling reached
+ * without a second pass over w in most steps).  desc->mode must be
+ * SV_SELECT_SAMPLE_RS; hidden, w, drafts, u_tok, stats and out_tokens are as in
+ * SAMPLE mode (the bonus rows' Gumbel-max draw included).  In the same pass every
+ * draft row b(k+1)+i, i < k, draws SV_RS_CANDIDATES independent tokens from its p:
+ *   cands[(b k + i) * SV_RS_CANDIDATES + c].id = argmax_v z_v + G(u_c(v))
+ * (ties: lowest id), u_c(v) from Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3"): word c of the block with key (key0, key1) and
+ * counter (v, i, b, 0), as the uniform ((x >> 9) + 1/2) 2^-23; G(u) = -ln(-ln u)
+ * in fp32 (hardware base-2 logarithms).  The caller changes the key every step.  cands [B*k, SV_RS_CANDIDATES];
+ * bf16 only; workspace
+ * sv_lmhead_workspace(desc). */
+int sv_lmhead_select_rs(const sv_lmhead_desc* desc, const void* hidden, const void* w, const int32_t* drafts,
+                        const float* u_tok, uint32_t key0, uint32_t key1, sv_row_stats* stats, sv_rs_cand* cands,
+                        int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Clustered unembedding (a drafter's cheap unembed)                         */
@@ -310,6 +338,21 @@ typedef struct {
 int sv_accept(const sv_accept_desc* desc, const int32_t* drafts, const sv_row_stats* stats,
               const float* q_rows, const float* u_accept, int32_t* cache_len,
               int32_t* out_tokens, sv_accept_out* acc, int32_t* dev_status, void* stream);
+
+/* Accept step of single-pass sampling (desc->mode SV_SELECT_SAMPLE_RS).  Drafts
+ * are accepted as in SAMPLE.  After a rejection at row n = n_b, the candidates
+ * x_c of row b k + n are tested in order: x_c is taken iff
+ *   u_rs[b][c] * p(x_c) < p(x_c) - q_rows[b][n][x_c],   p(x) = exp(z_x - lse_n),
+ * i.e. with probability max(0, 1 - q/p), which makes the taken token a draw from
+ * max(p - q, 0) normalised (rejection sampling with p as the proposal).  A taken
+ * candidate becomes next_token (draw_margin = its Gumbel margin s1 - s2); if every
+ * candidate is refused, next_token stays -1 and residual_row is set, exactly as in
+ * SAMPLE, for the sv_lmhead_select(RESIDUAL) fallback.
+ *   cands [B*k, SV_RS_CANDIDATES] from sv_lmhead_select_rs; u_rs [B, SV_RS_CANDIDATES]
+ *   fp32 uniforms; the other arguments as sv_accept (q_rows and u_accept required). */
+int sv_accept_rs(const sv_accept_desc* desc, const int32_t* drafts, const sv_row_stats* stats,
+                 const sv_rs_cand* cands, const float* q_rows, const float* u_accept, const float* u_rs,
+                 int32_t* cache_len, int32_t* out_tokens, sv_accept_out* acc, int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Decoder-stack support (embedding, RMSNorm, projections, GeGLU)            */

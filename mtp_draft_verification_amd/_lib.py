@@ -17,14 +17,14 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE = 0, -1, -2, -3, -4, -5
 SV_F32, SV_BF16 = 0, 1
-SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL = 0, 1, 2
+SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL, SV_SELECT_SAMPLE_RS = 0, 1, 2, 3
 SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU, SV_EPI_SPLIT_F32 = 0, 1, 2, 3
 SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn", "sv_verify_attn_fp8",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
            "sv_add_rmsnorm", "sv_draft_input", "sv_linear_splits", "sv_linear_workspace", "sv_linear",
-           "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed")
+           "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed", "sv_lmhead_select_rs", "sv_accept_rs")
 
 
 class SvError(RuntimeError):
@@ -73,6 +73,9 @@ ACCEPT_OUT_DTYPE = np.dtype([("n_accepted", "<i4"), ("next_token", "<i4"), ("new
                              ("drop_end", "<i4"), ("hidden_row", "<i4"), ("residual_row", "<i4"),
                              ("draw_margin", "<f4")])
 ROW_STATS_WORDS = ROW_STATS_DTYPE.itemsize // 4   # 9
+RS_CAND_DTYPE = np.dtype([("id", "<i4"), ("z", "<f4"), ("s1", "<f4"), ("s2", "<f4"), ("pad", "<i4")])
+RS_CAND_WORDS = RS_CAND_DTYPE.itemsize // 4       # 5
+RS_CANDIDATES = 4
 ACCEPT_OUT_WORDS = ACCEPT_OUT_DTYPE.itemsize // 4  # 10
 
 _lib = None
@@ -118,6 +121,11 @@ def load():
     L.sv_linear.argtypes = [ctypes.POINTER(LinearDesc), P, P, P, P, sz, P]
     L.sv_geglu.restype = ctypes.c_int
     L.sv_geglu.argtypes = [i32, i32, ctypes.c_int, P, P, P]
+    u32 = ctypes.c_uint32
+    L.sv_lmhead_select_rs.restype = ctypes.c_int
+    L.sv_lmhead_select_rs.argtypes = [ctypes.POINTER(LMHeadDesc), P, P, P, P, u32, u32, P, P, P, P, sz, P]
+    L.sv_accept_rs.restype = ctypes.c_int
+    L.sv_accept_rs.argtypes = [ctypes.POINTER(AcceptDesc), P, P, P, P, P, P, P, P, P, P, P]
     L.sv_cluster_unembed_workspace.restype = sz
     L.sv_cluster_unembed_workspace.argtypes = [ctypes.POINTER(ClusterDesc)]
     L.sv_cluster_unembed.restype = ctypes.c_int
@@ -198,6 +206,29 @@ def sv_lmhead_select(desc: LMHeadDesc, hidden, w, drafts, u_tok, q_rows, stats, 
                                  _ptr(q_rows), _ptr(stats), _ptr(acc), _ptr(out_tokens), _ptr(workspace),
                                  ws_bytes, _stream(stream))
     _check("sv_lmhead_select", rc)
+
+
+def sv_lmhead_select_rs(desc: LMHeadDesc, hidden, w, drafts, u_tok, key0: int, key1: int, stats, cands, out_tokens,
+                        workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().sv_lmhead_select_rs(ctypes.byref(desc), _ptr(hidden), _ptr(w), _ptr(drafts), _ptr(u_tok),
+                                    int(key0) & 0xFFFFFFFF, int(key1) & 0xFFFFFFFF, _ptr(stats), _ptr(cands),
+                                    _ptr(out_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("sv_lmhead_select_rs", rc)
+
+
+def sv_accept_rs(desc: AcceptDesc, drafts, stats, cands, q_rows, u_accept, u_rs, cache_len, out_tokens, acc,
+                 dev_status=None, stream=None) -> None:
+    rc = load().sv_accept_rs(ctypes.byref(desc), _ptr(drafts), _ptr(stats), _ptr(cands), _ptr(q_rows),
+                             _ptr(u_accept), _ptr(u_rs), _ptr(cache_len), _ptr(out_tokens), _ptr(acc),
+                             _ptr(dev_status), _stream(stream))
+    _check("sv_accept_rs", rc)
+
+
+def decode_rs_cands(t) -> np.ndarray:
+    """int32 tensor [..., 5] holding sv_rs_cand -> structured numpy array."""
+    a = np.ascontiguousarray(t.detach().cpu().numpy().astype(np.int32, copy=False))
+    return a.view(RS_CAND_DTYPE).reshape(a.shape[:-1])
 
 
 def sv_accept(desc: AcceptDesc, drafts, stats, q_rows, u_accept, cache_len, out_tokens, acc,

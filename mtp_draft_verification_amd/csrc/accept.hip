@@ -8,6 +8,9 @@
 // property the pages state is that the output distribution is unchanged
 // ("Gemma 4 与 Gemini Nano" (kongchang), section "草稿模型").
 //
+// Single-pass sampling takes the residual token after a rejection from the first
+// pass's candidates of the rejected row by rejection (see sv_accept_rs).
+//
 // One thread per sequence; the committed length moves from L_b to L_b + n_b + 1,
 // rows [L_b + n_b + 1, L_b + k + 1) are rolled back by not being committed (the
 // next verify step appends over them), so no cache data moves.
@@ -16,12 +19,13 @@
 
 namespace sv {
 
-template <bool SAMPLE>
+template <bool SAMPLE, bool RS>
 __global__ __launch_bounds__(64) void accept_kernel(sv_accept_desc d, const int32_t* drafts,
                                                     const sv_row_stats* stats, const float* q_rows,
                                                     const float* u_acc, int32_t* cache_len,
                                                     int32_t* out_tokens, sv_accept_out* acc,
-                                                    int32_t* dev_status) {
+                                                    int32_t* dev_status, const sv_rs_cand* cands,
+                                                    const float* u_rs) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= d.batch) return;
   const int k = d.k, base = b * (k + 1);
@@ -54,6 +58,23 @@ __global__ __launch_bounds__(64) void accept_kernel(sv_accept_desc d, const int3
       y = -1;
       res = base + n;
       margin = 0.f;
+      if constexpr (RS) {
+        // the residual by rejection: candidate x (a draw from p of this row) is taken
+        // iff u p(x) < p(x) - q(x)
+        const float* qrow = q_rows + ((int64_t)b * k + n) * d.vocab;
+        for (int c = 0; c < SV_RS_CANDIDATES; ++c) {
+          const sv_rs_cand x = cands[((int64_t)b * k + n) * SV_RS_CANDIDATES + c];
+          if (x.id < 0 || x.id >= d.vocab) continue;
+          const float p = expf(x.z - last.lse);
+          const float u = u_rs[b * SV_RS_CANDIDATES + c];
+          if (u * p < p - qrow[x.id]) {
+            y = x.id;
+            res = -1;
+            margin = x.s1 - x.s2;
+            break;
+          }
+        }
+      }
     }
   } else {
     y = last.top1_id;
@@ -85,7 +106,7 @@ extern "C" int sv_accept(const sv_accept_desc* d, const int32_t* drafts, const s
                          int32_t* out_tokens, sv_accept_out* acc, int32_t* dev_status, void* stream) {
   if (!d) return SV_ERR_ARG;
   if (d->batch <= 0 || d->k < 0 || d->vocab <= 0) return SV_ERR_ARG;
-  if (d->mode != SV_SELECT_GREEDY && d->mode != SV_SELECT_SAMPLE) return SV_ERR_ARG;
+  if (d->mode != SV_SELECT_GREEDY && d->mode != SV_SELECT_SAMPLE) return SV_ERR_ARG;  // SAMPLE_RS: sv_accept_rs
   if (!stats || !cache_len || !out_tokens || !acc) return SV_ERR_ARG;
   if (d->k > 0 && !drafts) return SV_ERR_ARG;
   if (d->mode == SV_SELECT_SAMPLE && d->k > 0 && (!q_rows || !u_accept)) return SV_ERR_ARG;
@@ -94,10 +115,27 @@ extern "C" int sv_accept(const sv_accept_desc* d, const int32_t* drafts, const s
   hipStream_t s = (hipStream_t)stream;
   const unsigned g = (unsigned)((d->batch + 63) / 64);
   if (d->mode == SV_SELECT_SAMPLE)
-    hipLaunchKernelGGL(accept_kernel<true>, dim3(g), dim3(64), 0, s, *d, drafts, stats, q_rows, u_accept,
-                       cache_len, out_tokens, acc, dev_status);
+    hipLaunchKernelGGL((accept_kernel<true, false>), dim3(g), dim3(64), 0, s, *d, drafts, stats, q_rows, u_accept,
+                       cache_len, out_tokens, acc, dev_status, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(accept_kernel<false>, dim3(g), dim3(64), 0, s, *d, drafts, stats, q_rows, u_accept,
-                       cache_len, out_tokens, acc, dev_status);
+    hipLaunchKernelGGL((accept_kernel<false, false>), dim3(g), dim3(64), 0, s, *d, drafts, stats, q_rows, u_accept,
+                       cache_len, out_tokens, acc, dev_status, nullptr, nullptr);
+  return launch_status();
+}
+
+extern "C" int sv_accept_rs(const sv_accept_desc* d, const int32_t* drafts, const sv_row_stats* stats,
+                            const sv_rs_cand* cands, const float* q_rows, const float* u_accept, const float* u_rs,
+                            int32_t* cache_len, int32_t* out_tokens, sv_accept_out* acc, int32_t* dev_status,
+                            void* stream) {
+  if (!d) return SV_ERR_ARG;
+  if (d->batch <= 0 || d->k < 0 || d->vocab <= 0 || d->mode != SV_SELECT_SAMPLE_RS) return SV_ERR_ARG;
+  if (!stats || !cache_len || !out_tokens || !acc) return SV_ERR_ARG;
+  if (d->k > 0 && (!drafts || !q_rows || !u_accept || !cands || !u_rs)) return SV_ERR_ARG;
+  int rc = check_device();
+  if (rc != SV_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned g = (unsigned)((d->batch + 63) / 64);
+  hipLaunchKernelGGL((accept_kernel<true, true>), dim3(g), dim3(64), 0, s, *d, drafts, stats, q_rows, u_accept,
+                     cache_len, out_tokens, acc, dev_status, cands, u_rs);
   return launch_status();
 }

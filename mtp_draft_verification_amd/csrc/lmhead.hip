@@ -18,7 +18,7 @@
 namespace sv {
 
 enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_GEGLU = 5,
-                      GM_SPLIT = 6 };
+                      GM_SPLIT = 6, GM_SAMPLE_RS = 7 };
 
 struct SelPart {   // per (workgroup, row) partial of the select epilogue
   float t1v, t2v;  // top-2 logits (RESIDUAL: residual-draw scores)
@@ -29,6 +29,10 @@ struct SelPart {   // per (workgroup, row) partial of the select epilogue
   int s1i, s2i;
   int pad;
 };
+
+constexpr bool sample_mode(int m) { return m == GM_SAMPLE || m == GM_SAMPLE_RS; }
+constexpr bool select_mode(int m) { return m <= GM_RESIDUAL || m == GM_SAMPLE_RS; }
+constexpr int kRsCand = 4;  // first-pass candidates per draft row (single-pass sampling)
 
 struct GemmParams {
   const uint16_t* x;     // [R, K] rows (RESIDUAL: the hidden states, gathered per slot)
@@ -49,6 +53,9 @@ struct GemmParams {
   float* part;           // [grid][2][rows][NB] partial sums
   int splits;            // GM_SPLIT: K slices per block (grid = nblk * splits)
   int out_stride;        // GREEDY / SAMPLE: top-1 ids to out_tokens[r * out_stride]
+  uint32_t rs_key0, rs_key1;  // SAMPLE_RS: Philox key of the candidate draws
+  float* rs_part;        // SAMPLE_RS: [grid][rows][kRsCand][4] candidate partials
+  sv_rs_cand* rs_out;    // SAMPLE_RS: [B*k][kRsCand] candidates of the draft rows
   int32_t* cnt;          // [nblk][4] arrival counters, zero between calls
 };
 
@@ -63,6 +70,8 @@ struct RowCtx {
   const float* u;        // uniforms of the token draw
   const float* qrow;     // RESIDUAL: q distribution of the rejected draft
   float lse;             // RESIDUAL: log-partition of the row
+  bool rs;               // SAMPLE_RS: a draft row, which draws candidates
+  int rb, ri;            // SAMPLE_RS: its sequence and draft index
 };
 
 struct RowState {
@@ -88,6 +97,9 @@ __device__ __forceinline__ RowCtx make_ctx(const GemmParams& p, int r) {
   c.u = nullptr;
   c.qrow = nullptr;
   c.lse = 0.f;
+  c.rs = false;
+  c.rb = 0;
+  c.ri = 0;
   if constexpr (MODE == GM_RESIDUAL) {
     if (r < p.batch) {
       const sv_accept_out a = p.acc[r];
@@ -105,9 +117,14 @@ __device__ __forceinline__ RowCtx make_ctx(const GemmParams& p, int r) {
       c.valid = true;
       const int b = r / (p.kdr + 1), i = r % (p.kdr + 1);
       if (i < p.kdr) c.draft = p.drafts[b * p.kdr + i];
-      if (MODE == GM_SAMPLE && i == p.kdr) {
+      if (sample_mode(MODE) && i == p.kdr) {
         c.bonus = true;
         c.u = p.u_tok + (int64_t)b * p.N;
+      }
+      if (MODE == GM_SAMPLE_RS && i < p.kdr) {
+        c.rs = true;
+        c.rb = b;
+        c.ri = i;
       }
     }
   }
@@ -138,7 +155,7 @@ __device__ __forceinline__ void select_push4(RowState& st, const RowCtx& c, cons
       if (v0 + i == c.draft) st.dl = z[i];
     }
     st.l.merge(mx, e);
-    if (MODE == GM_SAMPLE && c.bonus) {
+    if (sample_mode(MODE) && c.bonus) {
       const f32x4_t u = *(const f32x4_t*)(c.u + v0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.s.push(z[i] + gumbel(u[i]), v0 + i);
@@ -189,7 +206,7 @@ __device__ __forceinline__ void select_fold(RowState& st, const RowCtx& c, const
       j2 = nj2;
     }
   st.a.merge(b1, j1, b2, j2);
-  if (MODE == GM_SAMPLE && c.bonus) {
+  if (sample_mode(MODE) && c.bonus) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const f32x4_t u = *(const f32x4_t*)(c.u + vbase + t * 16);
@@ -197,6 +214,87 @@ __device__ __forceinline__ void select_fold(RowState& st, const RowCtx& c, const
       for (int i = 0; i < 4; ++i) st.s.push(z[t][i] + gumbel(u[i]), vbase + t * 16 + i);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// single-pass sampling: kRsCand independent Gumbel-max draws from p per draft row
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC 2011): ten rounds of 32 x 32 -> 64-bit products of counter words 0
+// and 2 with the round multipliers; the key advances by the Weyl constants.
+__device__ __forceinline__ void philox4x32(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll 1  // rolled: the callers' unrolled loops stay within the unroller's budget
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+// open-interval uniform from 32 random bits: ((x >> 9) + 1/2) 2^-23, exact in fp32
+__device__ __forceinline__ float rs_uniform(uint32_t x) { return ((float)(x >> 9) + 0.5f) * 0x1p-23f; }
+// Gumbel noise -ln(-ln u) from the hardware base-2 logarithm (u in [2^-24, 1): no
+// denormal or zero argument reaches either logarithm)
+__device__ __forceinline__ float rs_gumbel(float u) {
+  constexpr float kLn2 = 0.69314718056f;
+  return -kLn2 * __builtin_amdgcn_logf(-kLn2 * __builtin_amdgcn_logf(u));
+}
+
+// per candidate: best and second-best perturbed score, the best's token id and logit
+struct RsState {
+  float s1[kRsCand], s2[kRsCand], z[kRsCand];
+  int id[kRsCand];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int c = 0; c < kRsCand; ++c) {
+      s1[c] = s2[c] = kNegInf;
+      z[c] = 0.f;
+      id[c] = -1;
+    }
+  }
+  __device__ __forceinline__ void push(int c, float sc, int v, float zv) {
+    const bool w = beats(sc, v, s1[c], id[c]);
+    s2[c] = w ? s1[c] : fmaxf(s2[c], sc);
+    s1[c] = w ? sc : s1[c];
+    z[c] = w ? zv : z[c];
+    id[c] = w ? v : id[c];
+  }
+  __device__ __forceinline__ void merge(int c, float os1, float os2, int oid, float oz) {
+    const bool w = beats(os1, oid, s1[c], id[c]);
+    s2[c] = w ? fmaxf(s1[c], os2) : fmaxf(s2[c], os1);
+    s1[c] = w ? os1 : s1[c];
+    z[c] = w ? oz : z[c];
+    id[c] = w ? oid : id[c];
+  }
+  __device__ __forceinline__ void merge_xor(int m) {
+#pragma unroll
+    for (int c = 0; c < kRsCand; ++c)
+      merge(c, shfl_xor_f(s1[c], m), shfl_xor_f(s2[c], m), shfl_xor_i(id[c], m), shfl_xor_f(z[c], m));
+  }
+};
+
+// candidate draws over a wave tile's logits of one draft row: token v takes the
+// Philox block with counter (v, i, b, 0), word c for candidate c
+template <int T>
+__device__ __forceinline__ void rs_fold(RsState& rs, const RowCtx& c, const GemmParams& p, const f32x4_t (&z)[T],
+                                        int vbase) {
+  if (!c.valid || !c.rs) return;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = vbase + t * 16 + e;
+      uint32_t w[4] = {(uint32_t)v, (uint32_t)c.ri, (uint32_t)c.rb, 0u};
+      philox4x32(w, p.rs_key0, p.rs_key1);
+      const float zv = z[t][e];
+#pragma unroll
+      for (int k = 0; k < kRsCand; ++k) rs.push(k, zv + rs_gumbel(rs_uniform(w[k])), v, zv);
+    }
 }
 
 __device__ __forceinline__ void state_merge(RowState& a, const RowState& b) {
@@ -275,7 +373,7 @@ __device__ __forceinline__ int logical_wg(int b, int P) {
 template <int MT, int T, int MODE>
 __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
   using C = RingCfg<MT, T>;
-  constexpr bool SELECT = MODE <= GM_RESIDUAL;
+  constexpr bool SELECT = select_mode(MODE);
   constexpr int NB = C::NB, NS = C::NS, WROWS = 16 * T;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGEB];
 
@@ -321,11 +419,13 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
   // ---- select state ----
   RowCtx ctx[MT];
   RowState st[MT];
+  RsState rs[MT];  // SAMPLE_RS only
   if constexpr (SELECT) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       ctx[mt] = make_ctx<MODE>(p, mt * 16 + lr);
       st[mt].init();
+      if constexpr (MODE == GM_SAMPLE_RS) rs[mt].init();
     }
   }
 
@@ -443,6 +543,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < T; ++t) zt[t] = acc[t][mt];
         select_fold<MODE, T>(st[mt], ctx[mt], zt, row0 + lg * 4);
+        if constexpr (MODE == GM_SAMPLE_RS) rs_fold<T>(rs[mt], ctx[mt], p, zt, row0 + lg * 4);
       }
       return;
     }
@@ -549,6 +650,48 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
         RowState a = from_part(s_sel[mt * 16 + lr]);
         for (int w = 1; w < 4; ++w) state_merge(a, from_part(s_sel[(w * MT + mt) * 16 + lr]));
         if (r < nx) p.sel[(int64_t)me * nx + r] = to_part(a);
+      }
+    }
+    if constexpr (MODE == GM_SAMPLE_RS) {
+      // candidate states: the same lane / wave combination, then one partial per row
+      float* s_rs = (float*)(ring + 4 * MT * 16 * sizeof(SelPart));  // [4][MT][16][kRsCand][4]
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        rs[mt].merge_xor(16);
+        rs[mt].merge_xor(32);
+        if (lg == 0) {
+          float* d = s_rs + (((wave * MT + mt) * 16 + lr) * kRsCand) * 4;
+#pragma unroll
+          for (int c = 0; c < kRsCand; ++c) {
+            d[4 * c] = rs[mt].s1[c];
+            d[4 * c + 1] = rs[mt].s2[c];
+            d[4 * c + 2] = __int_as_float(rs[mt].id[c]);
+            d[4 * c + 3] = rs[mt].z[c];
+          }
+        }
+      }
+      __syncthreads();
+      if (wave == 0 && lg == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int r = mt * 16 + lr;
+          RsState a = rs[mt];   // wave 0's own combined state
+          for (int w = 1; w < 4; ++w) {
+            const float* o = s_rs + (((w * MT + mt) * 16 + lr) * kRsCand) * 4;
+#pragma unroll
+            for (int c = 0; c < kRsCand; ++c) a.merge(c, o[4 * c], o[4 * c + 1], __float_as_int(o[4 * c + 2]), o[4 * c + 3]);
+          }
+          if (r < nx) {
+            float* d = p.rs_part + (((int64_t)me * nx + r) * kRsCand) * 4;
+#pragma unroll
+            for (int c = 0; c < kRsCand; ++c) {
+              d[4 * c] = a.s1[c];
+              d[4 * c + 1] = a.s2[c];
+              d[4 * c + 2] = __int_as_float(a.id[c]);
+              d[4 * c + 3] = a.z[c];
+            }
+          }
+        }
       }
     }
   }
@@ -922,6 +1065,30 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(GemmParams p, int npa
   __shared__ SelPart s_red[256];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int nrows = MODE == GM_RESIDUAL ? p.batch : p.R;
+  if constexpr (MODE == GM_SAMPLE_RS) {
+    // wave c merges candidate c of a draft row over the workgroups' partials
+    const int b = r / (p.kdr + 1), i = r % (p.kdr + 1), c = tid >> 6, lane = tid & 63;
+    if (i < p.kdr && c < kRsCand) {
+      RsState a;
+      a.init();
+      for (int w = lane; w < nparts; w += 64) {
+        const float* o = p.rs_part + (((int64_t)w * nrows + r) * kRsCand + c) * 4;
+        a.merge(c, o[0], o[1], __float_as_int(o[2]), o[3]);
+      }
+#pragma unroll
+      for (int m = 32; m > 0; m >>= 1)
+        a.merge(c, shfl_xor_f(a.s1[c], m), shfl_xor_f(a.s2[c], m), shfl_xor_i(a.id[c], m), shfl_xor_f(a.z[c], m));
+      if (lane == 0) {
+        sv_rs_cand o;
+        o.id = a.id[c];
+        o.z = a.z[c];
+        o.s1 = a.s1[c];
+        o.s2 = a.s2[c];
+        o.pad = 0;
+        p.rs_out[((int64_t)b * p.kdr + i) * kRsCand + c] = o;
+      }
+    }
+  }
   RowState a;
   a.init();
   for (int i = tid; i < nparts; i += 256) state_merge(a, from_part(p.sel[(int64_t)i * nrows + r]));
@@ -956,9 +1123,9 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(GemmParams p, int npa
     o.top2 = f.a.v2;
     o.lse = f.l.m + logf(f.l.s);
     o.draft_logit = f.dl;
-    o.sample_id = MODE == GM_SAMPLE ? f.s.i1 : -1;
-    o.sample_s1 = MODE == GM_SAMPLE ? f.s.v1 : 0.f;
-    o.sample_s2 = MODE == GM_SAMPLE ? f.s.v2 : 0.f;
+    o.sample_id = sample_mode(MODE) ? f.s.i1 : -1;
+    o.sample_s1 = sample_mode(MODE) ? f.s.v1 : 0.f;
+    o.sample_s2 = sample_mode(MODE) ? f.s.v2 : 0.f;
     stats[r] = o;
     if (out_tokens) out_tokens[(int64_t)r * p.out_stride] = f.a.i1;
   }
@@ -1045,8 +1212,11 @@ static int f32_grid(const sv_lmhead_desc& d) { return (d.vocab + 255) / 256; }
 static int validate_lmhead(const sv_lmhead_desc* d) {
   if (!d) return SV_ERR_ARG;
   if (d->batch <= 0 || d->k < 0 || d->d_model <= 0 || d->vocab <= 0) return SV_ERR_ARG;
-  if (d->mode != SV_SELECT_GREEDY && d->mode != SV_SELECT_SAMPLE && d->mode != SV_SELECT_RESIDUAL) return SV_ERR_ARG;
+  if (d->mode != SV_SELECT_GREEDY && d->mode != SV_SELECT_SAMPLE && d->mode != SV_SELECT_RESIDUAL &&
+      d->mode != SV_SELECT_SAMPLE_RS)
+    return SV_ERR_ARG;
   if (d->mode == SV_SELECT_RESIDUAL && d->k == 0) return SV_ERR_ARG;
+  if (d->mode == SV_SELECT_SAMPLE_RS && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->out_stride < 0) return SV_ERR_ARG;
   if (d->vocab % 64) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
@@ -1236,15 +1406,17 @@ extern "C" size_t sv_lmhead_workspace(const sv_lmhead_desc* d) {
   const int nrows = sel_rows(*d);
   if (d->dtype == SV_F32) return align_up((size_t)f32_grid(*d) * nrows * sizeof(SelPart), 256);
   const RingPlan pl = ring_plan(kSelT, nrows, d->d_model, d->vocab, kMaxWG);
-  return pl.cnt_bytes + pl.part_bytes + align_up((size_t)kMaxWG * nrows * sizeof(SelPart), 256);
+  return pl.cnt_bytes + pl.part_bytes + align_up((size_t)kMaxWG * nrows * sizeof(SelPart), 256) +
+         (d->mode == SV_SELECT_SAMPLE_RS ? align_up((size_t)kMaxWG * nrows * kRsCand * 16, 256) : 0);
 }
 
-extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, const void* w,
-                                const int32_t* drafts, const float* u_tok, const float* q_rows,
-                                sv_row_stats* stats, sv_accept_out* acc, int32_t* out_tokens,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+static int lmhead_select(const sv_lmhead_desc* d, const void* hidden, const void* w, const int32_t* drafts,
+                         const float* u_tok, const float* q_rows, sv_row_stats* stats, sv_accept_out* acc,
+                         int32_t* out_tokens, uint32_t key0, uint32_t key1, sv_rs_cand* cands, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   int rc = validate_lmhead(d);
   if (rc != SV_OK) return rc;
+  if (d->mode == SV_SELECT_SAMPLE_RS && d->k > 0 && !cands) return SV_ERR_ARG;
   if (!hidden || !w || !stats) return SV_ERR_ARG;
   if (d->k > 0 && !drafts && d->mode != SV_SELECT_RESIDUAL) return SV_ERR_ARG;
   if (d->mode != SV_SELECT_GREEDY && !u_tok) return SV_ERR_ARG;
@@ -1267,6 +1439,9 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
   p.stats_in = stats;
   p.acc = acc;
   p.out_stride = d->out_stride > 0 ? d->out_stride : 1;
+  p.rs_key0 = key0;
+  p.rs_key1 = key1;
+  p.rs_out = cands;
   const int nrows = sel_rows(*d);
   hipStream_t s = (hipStream_t)stream;
   int grid;
@@ -1278,10 +1453,13 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
     p.cnt = (int32_t*)workspace;
     p.part = (float*)((char*)workspace + pl.cnt_bytes);
     p.sel = (SelPart*)((char*)workspace + pl.cnt_bytes + pl.part_bytes);
+    p.rs_part = (float*)((char*)workspace + pl.cnt_bytes + pl.part_bytes +
+                         align_up((size_t)kMaxWG * nrows * sizeof(SelPart), 256));
     grid = pl.grid;
     switch (d->mode) {
       case SV_SELECT_GREEDY: rc = dispatch_ring<kSelT, GM_GREEDY>(p, nrows, grid, s); break;
       case SV_SELECT_SAMPLE: rc = dispatch_ring<kSelT, GM_SAMPLE>(p, nrows, grid, s); break;
+      case SV_SELECT_SAMPLE_RS: rc = dispatch_ring<kSelT, GM_SAMPLE_RS>(p, nrows, grid, s); break;
       default: rc = dispatch_ring<kSelT, GM_RESIDUAL>(p, nrows, grid, s); break;
     }
     if (rc != SV_OK) return rc;
@@ -1303,11 +1481,32 @@ extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, con
     case SV_SELECT_SAMPLE:
       hipLaunchKernelGGL(lmhead_merge_kernel<GM_SAMPLE>, dim3(nrows), dim3(256), 0, s, p, grid, stats, out_tokens);
       break;
+    case SV_SELECT_SAMPLE_RS:
+      hipLaunchKernelGGL(lmhead_merge_kernel<GM_SAMPLE_RS>, dim3(nrows), dim3(256), 0, s, p, grid, stats, out_tokens);
+      break;
     default:
       hipLaunchKernelGGL(lmhead_merge_kernel<GM_RESIDUAL>, dim3(nrows), dim3(256), 0, s, p, grid, stats, out_tokens);
       break;
   }
   return launch_status();
+}
+
+extern "C" int sv_lmhead_select(const sv_lmhead_desc* d, const void* hidden, const void* w,
+                                const int32_t* drafts, const float* u_tok, const float* q_rows,
+                                sv_row_stats* stats, sv_accept_out* acc, int32_t* out_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (d && d->mode == SV_SELECT_SAMPLE_RS) return SV_ERR_ARG;  // sv_lmhead_select_rs
+  return lmhead_select(d, hidden, w, drafts, u_tok, q_rows, stats, acc, out_tokens, 0, 0, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" int sv_lmhead_select_rs(const sv_lmhead_desc* d, const void* hidden, const void* w, const int32_t* drafts,
+                                   const float* u_tok, uint32_t key0, uint32_t key1, sv_row_stats* stats,
+                                   sv_rs_cand* cands, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!d || d->mode != SV_SELECT_SAMPLE_RS) return SV_ERR_ARG;
+  return lmhead_select(d, hidden, w, drafts, u_tok, nullptr, stats, nullptr, out_tokens, key0, key1, cands,
+                       workspace, workspace_bytes, stream);
 }
 
 extern "C" int32_t sv_linear_splits(const sv_linear_desc* d) {

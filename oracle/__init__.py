@@ -90,14 +90,14 @@ def lib():
         L.svo_sample_bonus.argtypes = [i64, P, P, ctypes.POINTER(f64)]
         L.svo_sample_bonus.restype = ctypes.c_int
         L.svo_toy_spec_trials.argtypes = [i64, ctypes.c_int, i64, P, P, P, P, P, P, P]
-        u64 = ctypes.c_uint64
-        L.svo_philox4x64.argtypes = [P, P, P]
+        u32 = ctypes.c_uint32
+        L.svo_philox4x32.argtypes = [P, P, P]
         L.svo_rs_uniform.restype = f64
-        L.svo_rs_uniform.argtypes = [u64, u64, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int]
-        L.svo_rs_candidates.argtypes = [i64, P, u64, u64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+        L.svo_rs_uniform.argtypes = [u32, u32, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int]
+        L.svo_rs_candidates.argtypes = [i64, P, u32, u32, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
         L.svo_rs_accept.restype = ctypes.c_int
         L.svo_rs_accept.argtypes = [ctypes.c_int, P, P, f64, P, P, P]
-        L.svo_toy_spec_trials_rs.argtypes = [i64, ctypes.c_int, i64, P, P, P, P, P, u64, u64, ctypes.c_int, P, P, P,
+        L.svo_toy_spec_trials_rs.argtypes = [i64, ctypes.c_int, i64, P, P, P, P, P, u32, u32, ctypes.c_int, P, P, P,
                                              P]
         _lib = L
     return _lib
@@ -350,12 +350,12 @@ def sample_bonus(z_row, u_row) -> tuple[int, float]:
     return int(y), float(m.value)
 
 
-def philox4x64(ctr, key) -> np.ndarray:
-    """One Philox4x64-10 block: counter [4] and key [2] uint64 -> 4 uint64."""
-    c = np.ascontiguousarray(ctr, dtype=np.uint64)
-    k = np.ascontiguousarray(key, dtype=np.uint64)
-    o = np.zeros(4, dtype=np.uint64)
-    lib().svo_philox4x64(_ptr(c), _ptr(k), _ptr(o))
+def philox4x32(ctr, key) -> np.ndarray:
+    """One Philox4x32-10 block: counter [4] and key [2] uint32 -> 4 uint32."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    o = np.zeros(4, dtype=np.uint32)
+    lib().svo_philox4x32(_ptr(c), _ptr(k), _ptr(o))
     return o
 
 
@@ -364,7 +364,7 @@ def rs_uniform(key, b: int, i: int, v: int, r: int) -> float:
 
 
 def rs_candidates(z_row, key, b: int, i: int, R: int = 4) -> tuple[np.ndarray, np.ndarray]:
-    """R draws from softmax(z_row) for draft row (b, i) under `key` (2 uint64):
+    """R draws from softmax(z_row) for draft row (b, i) under `key` (2 uint32):
     (token ids [R], Gumbel margins [R])."""
     z = _f64(z_row)
     cand = np.empty(R, dtype=np.int32)

@@ -433,45 +433,38 @@ int svo_sample_bonus(int64_t V, const double* z, const float* u, double* margin)
 /* residual reached by rejection                                             */
 /* ------------------------------------------------------------------------ */
 
-/* Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
  * "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds of two
- * 64 x 64 -> 128-bit products of the even counter words with the round
+ * 32 x 32 -> 64-bit products of the even counter words with the round
  * multipliers, the high halves xored with the odd words and the key, the key
  * bumped by the Weyl constants between rounds. */
-void svo_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-  uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+void svo_philox4x32(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
   for (int r = 0; r < 10; ++r) {
     if (r > 0) { k0 += W0; k1 += W1; }
-    const unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
-    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
-    const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
   }
   out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-/* Uniform r (0..3) of token v for draft row i of sequence b: the Philox block
- * with counter (v / 2, i, b, 0) and key (key0, key1) serves tokens 2m and 2m+1;
- * token v takes words 2 (v % 2) and 2 (v % 2) + 1, uniform r the low (r even) or
- * high (r odd) 32 bits of word 2 (v % 2) + r / 2.  Bits x become the open-interval
- * uniform ((x >> 9) + 1/2) 2^-23, exact in fp32. */
-double svo_rs_uniform(uint64_t key0, uint64_t key1, int b, int i, int64_t v, int r) {
-  const uint64_t ctr[4] = {(uint64_t)(v >> 1), (uint64_t)i, (uint64_t)b, 0};
-  const uint64_t key[2] = {key0, key1};
-  uint64_t o[4];
-  svo_philox4x64(ctr, key, o);
-  const uint64_t w = o[2 * (v & 1) + (r >> 1)];
-  const uint32_t x = (r & 1) ? (uint32_t)(w >> 32) : (uint32_t)w;
-  return ((double)(x >> 9) + 0.5) * ldexp(1.0, -23);
+/* Uniform r (0..3) of token v for draft row i of sequence b: word r of the
+ * Philox4x32-10 block with counter (v, i, b, 0) and key (key0, key1).  Bits x
+ * become the open-interval uniform ((x >> 9) + 1/2) 2^-23, exact in fp32. */
+double svo_rs_uniform(uint32_t key0, uint32_t key1, int b, int i, int64_t v, int r) {
+  const uint32_t ctr[4] = {(uint32_t)v, (uint32_t)i, (uint32_t)b, 0};
+  const uint32_t key[2] = {key0, key1};
+  uint32_t o[4];
+  svo_philox4x32(ctr, key, o);
+  return ((double)(o[r] >> 9) + 0.5) * ldexp(1.0, -23);
 }
 
 /* R independent draws from p = softmax(z) for draft row (b, i), each by
  * Gumbel-max with its own uniforms: cand[r] = argmax_v z_v + G(u_r(v)) (ties:
  * lowest id), margin[r] = best score - second best. */
-void svo_rs_candidates(int64_t V, const double* z, uint64_t key0, uint64_t key1, int b, int i, int R,
+void svo_rs_candidates(int64_t V, const double* z, uint32_t key0, uint32_t key1, int b, int i, int R,
                        int32_t* cand, double* margin) {
   for (int r = 0; r < R; ++r) {
     int64_t b1 = -1;
@@ -548,8 +541,8 @@ void svo_toy_spec_trials(int64_t T, int k, int64_t V, const double* z, const flo
  * (key0 + t, key1), sequence 0) by svo_rs_accept, and only if all are refused
  * from svo_sample_residual.  u_rs [T][R]; fb_out[t] = 1 when the fallback ran. */
 void svo_toy_spec_trials_rs(int64_t T, int k, int64_t V, const double* z, const float* q,
-                            const int32_t* drafts, const float* u_acc, const float* u_tok, uint64_t key0,
-                            uint64_t key1, int R, const float* u_rs, int32_t* n_out, int32_t* y_out,
+                            const int32_t* drafts, const float* u_acc, const float* u_tok, uint32_t key0,
+                            uint32_t key1, int R, const float* u_rs, int32_t* n_out, int32_t* y_out,
                             int32_t* fb_out) {
   double m = -INFINITY, acc = 0.0;
   for (int64_t v = 0; v < V; ++v) if (z[v] > m) m = z[v];
@@ -572,7 +565,7 @@ void svo_toy_spec_trials_rs(int64_t T, int k, int64_t V, const double* z, const 
     double margin;
     int y, fb = 0;
     if (n < k) {
-      svo_rs_candidates(V, z, key0 + (uint64_t)t, key1, 0, n, R, cand, cm);
+      svo_rs_candidates(V, z, key0 + (uint32_t)t, key1, 0, n, R, cand, cm);
       y = svo_rs_accept(R, cand, z, lse, q, u_rs + t * R, cm);
       if (y < 0) {
         fb = 1;

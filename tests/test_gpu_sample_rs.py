@@ -1,0 +1,144 @@
+"""GPU parity of single-pass sampling (sv_lmhead_select_rs, sv_accept_rs) against
+the oracle.
+
+The first pass must leave the SAMPLE statistics as they are (to rounding) and add,
+per draft row, four draws from p: each candidate id must equal the oracle's
+(same Philox4x32-10 uniforms; Gumbel noise in fp32 against fp64) wherever the
+oracle's winner leads the runner-up by more than MARGIN, and carry its logit to
+ATOL.  The accept step must take the oracle's decisions wherever the deciding
+margins are clear: the number of accepted drafts, then after a rejection the first
+candidate with u p(x) < p(x) - q(x), or the direct residual draw when none is."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mtp_draft_verification_amd._lib as L
+from mtp_draft_verification_amd import configs, inputs
+from gpu_util import gpu, host, need_gpu, say
+from test_gpu_lmhead import ATOL, MARGIN, check_stats, lm_inputs, run_select, w_host
+
+RC = L.RS_CANDIDATES
+
+
+def rs_case(B, k, d, V, seed, key, q_from_p=None, rows_check=None):
+    dev = need_gpu()
+    say(f"[sample-rs] B={B} k={k} d={d} V={V} seed={seed} key={key} q_from_p={q_from_p}")
+    h, W = lm_inputs(B, k, d, V, seed, dev)
+    Wh, hh = w_host(W), host(h)
+    seqs = rows_check if rows_check is not None else list(range(B))
+    if q_from_p is not None:
+        zz = oracle.lmhead(hh, Wh).reshape(B, k + 1, V)
+        p = np.exp(zz - zz.max(axis=2, keepdims=True))
+        p /= p.sum(axis=2, keepdims=True)
+        noise = inputs.dirichlet_rows(B * k, V, 1.0, seed, "qnoise", "cpu").numpy().reshape(B, k, V)
+        q_rows = torch.from_numpy(((1 - q_from_p) * p[:, :k] + q_from_p * noise).astype(np.float32)).to(dev)
+    else:
+        q_rows = inputs.dirichlet_rows(B * k, V, 0.3, seed, "q", dev).view(B, k, V)
+    drafts = inputs.categorical(q_rows.view(B * k, V), seed, "drafts").view(B, k)
+    u_acc = inputs.uniform((B, k), seed, "u_acc", dev)
+    u_tok = inputs.uniform((B, V), seed, "u_tok", dev)
+    u_rs = inputs.uniform((B, RC), seed, "u_rs", dev)
+    desc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=L.SV_SELECT_SAMPLE_RS, dtype=L.SV_BF16)
+    ws = torch.zeros(L.sv_lmhead_workspace(desc), dtype=torch.uint8, device=dev)
+    stats = torch.full((B * (k + 1), L.ROW_STATS_WORDS), -7, dtype=torch.int32, device=dev)
+    cands = torch.full((B * k * RC, L.RS_CAND_WORDS), -7, dtype=torch.int32, device=dev)
+    L.sv_lmhead_select_rs(desc, h, W, drafts, u_tok, key[0], key[1], stats, cands, None, ws)
+    ref_stats = run_select(h, W, drafts, B, k, L.SV_SELECT_SAMPLE, dev, u_tok=u_tok)
+    torch.cuda.synchronize()
+    # the candidate draws leave the SAMPLE statistics as they are (ids exactly; values to
+    # rounding, as fused multiply-adds may be contracted differently in the two builds)
+    sa, sb = L.decode_row_stats(stats), L.decode_row_stats(ref_stats)
+    for f in ("top1_id", "top2_id", "sample_id"):
+        np.testing.assert_array_equal(sa[f], sb[f])
+    for f in ("top1", "top2", "lse", "draft_logit", "sample_s1", "sample_s2"):
+        np.testing.assert_allclose(sa[f], sb[f], rtol=1e-6, atol=1e-6)
+    cl = torch.full((B,), 100, dtype=torch.int32, device=dev)
+    out = torch.full((B, k + 1), -9, dtype=torch.int32, device=dev)
+    acc = torch.zeros(B, L.ACCEPT_OUT_WORDS, dtype=torch.int32, device=dev)
+    L.sv_accept_rs(L.AcceptDesc(batch=B, k=k, vocab=V, mode=L.SV_SELECT_SAMPLE_RS), drafts, stats, cands, q_rows,
+                   u_acc, u_rs, cl, out, acc)
+    # sequences whose candidates were all refused: the direct residual draw
+    run_select(h, W, drafts, B, k, L.SV_SELECT_RESIDUAL, dev, u_tok=u_tok, q_rows=q_rows, stats=stats, acc=acc,
+               out_tokens=out)
+    torch.cuda.synchronize()
+    gs = L.decode_row_stats(stats)
+    gc = L.decode_rs_cands(cands).reshape(B, k, RC)
+    ga = L.decode_accept_out(acc)
+    qh, dh, uah, uth, urh = host(q_rows), drafts.cpu().numpy(), host(u_acc), host(u_tok), host(u_rs)
+    n_cand = n_seq = excused = n_taken = n_fallback = 0
+    for b in seqs:
+        z = oracle.lmhead(hh[b * (k + 1):(b + 1) * (k + 1)], Wh)
+        st = [oracle.row_stats(z[i], int(dh[b, i]) if i < k else -1) for i in range(k + 1)]
+        for i in range(k + 1):
+            check_stats(gs[b * (k + 1) + i], st[i], f"b{b} row{i}")
+        oc = []
+        for i in range(k):
+            cand, marg = oracle.rs_candidates(z[i], key, b, i, RC)
+            oc.append((cand, marg))
+            for c in range(RC):
+                g = gc[b, i, c]
+                assert 0 <= int(g["id"]) < V
+                assert abs(float(g["z"]) - z[i][int(g["id"])]) <= ATOL, (b, i, c)
+                if marg[c] > MARGIN:
+                    assert int(g["id"]) == cand[c], (b, i, c, g, cand[c], marg[c])
+                    n_cand += 1
+        lse = np.array([s["lse"] for s in st[:k]])
+        dl = np.array([s["draft_logit"] for s in st[:k]])
+        qd = np.array([qh[b, i, dh[b, i]] for i in range(k)], dtype=np.float32)
+        n, margins = oracle.accept_sample(lse, dl, qd, uah[b])
+        if np.any(np.abs(margins[:min(n + 1, k)]) <= MARGIN):
+            excused += 1
+            continue
+        assert int(ga[b]["n_accepted"]) == n, (b, n, ga[b])
+        if n == k:
+            y, m = oracle.sample_bonus(z[k], uth[b])
+            clear = m > MARGIN
+        else:
+            cand, marg = oc[n]
+            y, am = oracle.rs_accept(cand, z[n], st[n]["lse"], qh[b, n], urh[b])
+            # each test u p < p - q, relative to p: (1 - q/p) - u, against fp32 on the GPU
+            nt = int((~np.isnan(am)).sum())
+            rel = am[:nt] / np.exp(z[n][cand[:nt]] - st[n]["lse"])
+            clear = np.all(np.abs(rel) > 1e-3) and np.all(marg[:nt] > MARGIN)
+            if y < 0:
+                y, m = oracle.sample_residual(z[n], st[n]["lse"], qh[b, n], uth[b])
+                clear = clear and m > MARGIN
+                if clear:
+                    assert int(ga[b]["residual_row"]) == b * (k + 1) + n
+                    n_fallback += 1
+            elif clear:
+                assert int(ga[b]["residual_row"]) == -1
+                n_taken += 1
+        if clear:
+            assert int(ga[b]["next_token"]) == y, (b, n, y, ga[b])
+            assert out.cpu().numpy()[b, n] == y
+            n_seq += 1
+        else:
+            excused += 1
+    say(f"[sample-rs] {n_cand} candidates equal; {n_seq} sequences checked ({n_taken} residual by a "
+        f"candidate, {n_fallback} by the fallback), {excused} excused; n = {ga['n_accepted'].tolist()}")
+    return ga
+
+
+@gpu
+def test_single_pass_small_rejects():
+    rs_case(4, 4, 128, 2048, 1, (11, 22))
+
+
+@gpu
+def test_single_pass_small_close_drafter():
+    ga = rs_case(8, 4, 128, 2048, 2, (33, 44), q_from_p=0.3)
+    assert ga["n_accepted"].max() >= 1
+
+
+@gpu
+def test_single_pass_many_rows():
+    # 12 sequences x 5 rows = 60 rows: four row tiles per wave
+    rs_case(12, 4, 256, 4096, 3, (55, 66), q_from_p=0.5)
+
+
+@gpu
+def test_single_pass_full_size_sampled():
+    cfg = configs.LMHEAD_B8
+    rs_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0, (2 ** 31 + 5, 77), q_from_p=0.3, rows_check=[0, 5])

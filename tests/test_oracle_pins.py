@@ -506,29 +506,27 @@ def test_rejection_sampling_reproduces_target_distribution(k):
     assert abs(rate - expect) < 5 * math.sqrt(expect * (1 - expect) / T)
 
 
-def test_philox4x64_matches_the_library_generator():
-    # numpy's Philox bit generator is Philox4x64-10; it advances its counter before
-    # producing a block, so its first block belongs to counter + 1
-    rng = np.random.default_rng(31)
-    for _ in range(5):
-        ctr = rng.integers(1, 2 ** 63, size=4, dtype=np.uint64)
-        key = rng.integers(0, 2 ** 63, size=2, dtype=np.uint64)
-        start = ctr.copy()
-        start[0] -= np.uint64(1)
-        lib = np.random.Philox(counter=start, key=key).random_raw(4)
-        np.testing.assert_array_equal(oracle.philox4x64(ctr, key), lib)
+def test_philox4x32_known_answers():
+    # the known-answer vectors published with the generator's reference
+    # implementation (Random123, Salmon et al. SC 2011) for Philox4x32-10
+    kat = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+           ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+           ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+            (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in kat:
+        np.testing.assert_array_equal(oracle.philox4x32(ctr, key), np.array(want, dtype=np.uint32))
 
 
 def test_rs_uniform_layout():
-    # token v of draft row (b, i): block (v // 2, i, b, 0); words 2 (v % 2) + r // 2,
-    # low half for even r; ((x >> 9) + 1/2) 2^-23
+    # token v of draft row (b, i): word r of block (v, i, b, 0); ((x >> 9) + 1/2) 2^-23
     key = (0x1234, 0xABCD)
-    for (b, i, v, r) in ((0, 0, 2, 0), (3, 2, 7, 1), (1, 3, 262143, 2), (5, 0, 1000, 3), (2, 1, 3, 3)):
-        start = np.array([v // 2 - 1, i, b, 0], dtype=np.uint64)   # the generator steps first
-        blk = np.random.Philox(counter=start, key=np.array(key, dtype=np.uint64)).random_raw(4)
-        w = int(blk[2 * (v % 2) + r // 2])
-        x = (w >> 32) if r % 2 else (w & 0xFFFFFFFF)
+    for (b, i, v, r) in ((0, 0, 0, 0), (3, 2, 7, 1), (1, 3, 262143, 2), (5, 0, 1000, 3)):
+        x = int(oracle.philox4x32((v, i, b, 0), key)[r])
         assert oracle.rs_uniform(key, b, i, v, r) == ((x >> 9) + 0.5) * 2.0 ** -23
+    # uniforms are open-interval and fill [0, 1) evenly
+    u = np.array([oracle.rs_uniform(key, 0, 0, v, r) for v in range(2000) for r in range(4)])
+    assert u.min() > 0 and u.max() < 1
+    assert stats.kstest(u, "uniform").pvalue > 0.001
 
 
 def test_rs_candidates_are_draws_from_p():
