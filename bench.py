@@ -66,7 +66,7 @@ def parse():
 
 
 ONLY_CALLS = ("attn_global", "attn_local", "attn_global_fp8", "attn_local_fp8", "lmhead", "lmhead_sample",
-              "lmhead_sample_rs",
+              "lmhead_sample_rs", "cluster_unembed",
               "qkv_local", "qkv_global", "o_local", "o_global", "gu", "down", "hbm_copy")
 COPY_BYTES = 1 << 30  # hbm_copy: a plain 1 GiB device-to-device copy (counter calibration)
 
@@ -143,6 +143,22 @@ def time_one(args, only) -> dict:
         else:
             call = lambda: L.sv_lmhead_select(desc, h, W, drafts, u_tok, None, stats, None, None, ws, stream)
         byts = call_bytes(cfg, [cfg.ctx] * B)["lmhead"]
+    elif only == "cluster_unembed":
+        # the drafter's clustered unembedding at its shape: one row per sequence over
+        # 2048 clusters of 128 tokens, the best 32 kept (4096 candidates per row)
+        C, top = 2048, 32
+        E = inputs.normal((cfg.vocab, cfg.d_model), cfg.d_model ** -0.5, 0, "E", dev)
+        cu = inputs.clusters_of(E, C, top, 0)
+        del E
+        h = inputs.normal((B, cfg.d_model), 1.0, 0, "h", dev)
+        cdesc = L.ClusterDesc(rows=B, d_model=cfg.d_model, vocab=cfg.vocab, n_clusters=C, top_clusters=top,
+                              dtype=L.SV_BF16)
+        ws = torch.zeros(L.sv_cluster_unembed_workspace(cdesc), dtype=torch.uint8, device=dev)
+        stats = torch.empty((B, L.ROW_STATS_WORDS), dtype=torch.int32, device=dev)
+        call = lambda: L.sv_cluster_unembed(cdesc, h, cu["centroids"], cu["w_perm"], cu["perm"], stats, None, None,
+                                            1, ws, stream)
+        cand = (cfg.vocab // C) * top
+        byts = C * cfg.d_model * 2 + B * (cand * cfg.d_model * 2 + cand * 4)
     elif only == "hbm_copy":
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
