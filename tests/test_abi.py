@@ -126,6 +126,47 @@ def test_cluster_unembed_rejects_bad_arguments():
     assert call(d, ws_bytes=L.sv_cluster_unembed_workspace(d) - 1) == L.SV_ERR_WORKSPACE
 
 
+def test_fp8_attention_and_single_pass_sampling_reject_bad_arguments():
+    lib = L.load()
+    fake = ctypes.c_void_p(4096)
+    big = 1 << 40
+
+    def fp8(d, ks=fake, vs=fake, **ptrs):
+        p = dict(q=fake, kn=fake, vn=fake, kc=fake, vc=fake, cl=fake, out=fake, ws=fake)
+        p.update(ptrs)
+        return lib.sv_verify_attn_fp8(ctypes.byref(d), p["q"], p["kn"], p["vn"], p["kc"], p["vc"], ks, vs, p["cl"],
+                                      p["out"], p["ws"], big, None, None)
+
+    assert fp8(_desc(dtype=L.SV_F32, cache_capacity=1000)) == L.SV_ERR_ARG      # fp8 caches need bf16 rows
+    assert fp8(_desc(), ks=None) == L.SV_ERR_ARG                                  # key scales missing
+    assert fp8(_desc(), ks=ctypes.c_void_p(4096 + 4)) == L.SV_ERR_ARG             # misaligned scales
+    assert fp8(_desc(), vs=None) == L.SV_ERR_ARG                                  # value scales missing (K != V)
+    gl = _desc(k_is_v=1, head_dim=512, rope_dims=128)
+    assert fp8(gl, vn=None, vc=None) == L.SV_ERR_ARG                              # K = V takes no value scales
+    assert fp8(_desc(batch=0)) == L.SV_ERR_ARG
+
+    rs = L.LMHeadDesc(batch=8, k=4, d_model=3840, vocab=262144, mode=L.SV_SELECT_SAMPLE_RS, dtype=L.SV_BF16)
+    assert L.sv_lmhead_workspace(rs) > L.sv_lmhead_workspace(
+        L.LMHeadDesc(batch=8, k=4, d_model=3840, vocab=262144, mode=L.SV_SELECT_SAMPLE, dtype=L.SV_BF16))
+    # the RS mode only through its own entry point, and the entry point only in RS mode
+    assert lib.sv_lmhead_select(ctypes.byref(rs), fake, fake, fake, fake, None, fake, None, None, fake, big,
+                                None) == L.SV_ERR_ARG
+    smp = L.LMHeadDesc(batch=8, k=4, d_model=3840, vocab=262144, mode=L.SV_SELECT_SAMPLE, dtype=L.SV_BF16)
+    assert lib.sv_lmhead_select_rs(ctypes.byref(smp), fake, fake, fake, fake, 1, 2, fake, fake, None, fake, big,
+                                   None) == L.SV_ERR_ARG
+    assert lib.sv_lmhead_select_rs(ctypes.byref(rs), fake, fake, fake, fake, 1, 2, fake, None, None, fake, big,
+                                   None) == L.SV_ERR_ARG                             # candidates missing
+    f32 = L.LMHeadDesc(batch=2, k=4, d_model=64, vocab=1024, mode=L.SV_SELECT_SAMPLE_RS, dtype=L.SV_F32)
+    assert L.sv_lmhead_workspace(f32) == 0                                          # bf16 only
+    ad = L.AcceptDesc(batch=4, k=4, vocab=1000, mode=L.SV_SELECT_SAMPLE_RS)
+    assert lib.sv_accept(ctypes.byref(ad), fake, fake, fake, fake, fake, fake, fake, None, None) == L.SV_ERR_ARG
+    assert lib.sv_accept_rs(ctypes.byref(ad), fake, fake, None, fake, fake, fake, fake, fake, fake, None,
+                            None) == L.SV_ERR_ARG                                   # candidates missing
+    ad2 = L.AcceptDesc(batch=4, k=4, vocab=1000, mode=L.SV_SELECT_SAMPLE)
+    assert lib.sv_accept_rs(ctypes.byref(ad2), fake, fake, fake, fake, fake, fake, fake, fake, fake, None,
+                            None) == L.SV_ERR_ARG                                   # wrong mode
+
+
 def test_valid_call_without_gpu_reports_device_error():
     import torch
     if torch.cuda.is_available():
