@@ -35,6 +35,7 @@ struct AttnParams {
   float* part_acc;        // workspace: [slots][M][D]
   float* part_ml;         // workspace: [slots][M][2]  (m in log2 units, l)
   int32_t* seg_cnt;       // workspace: [B * Hkv] arrivals of a segment's pieces
+  int32_t* plan;          // workspace: the work split {chunk, pieces}, set by rope_append
   int in_splits;          // > 0: q, k_new, v_new are fp32 K-split partial products
   int fp8;                // caches hold fp8 E4M3 codes seen through per-channel scales
   const float* k_scale;   // fp8: [Hkv, D] scales of the key cache (also the values when K = V)
@@ -85,10 +86,11 @@ __device__ __forceinline__ void seq_range(const AttnParams& p, int b, int64_t& l
 // pieces number at most nwg (or one piece per segment when there are at least nwg
 // segments), so no workgroup's keys cross a segment boundary.  Every workgroup and
 // the merge derive the same plan from the cache lengths.
-// The plan is computed by each wave on its own, in parallel over the batch: lane l
-// holds the key counts of sequences l, l + 64, ... (up to kPlanGroups * 64 of them,
-// key counts below 2^31) and sums or scans them with cross-lane shuffles, so a
-// workgroup spends well under a microsecond on it.  All 64 lanes must be active.
+// The plan (chunk, piece count) is computed once per call by the first wave of
+// rope_append_kernel and left in the workspace; a workgroup then only locates its
+// piece.  Both run wave-parallel over the batch: lane l holds the key counts of
+// sequences l, l + 64, ... (up to kPlanGroups * 64 of them, key counts below 2^31)
+// and sums or scans them with cross-lane shuffles.  All 64 lanes must be active.
 constexpr int kPlanGroups = 4;  // batch up to 256
 struct Pieces {
   int chunk;
@@ -323,9 +325,20 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
   const int hs = blockIdx.y;  // [0, Hq): query head, then key heads, then value heads
   const int d = threadIdx.x;
   if constexpr (sizeof(T) == 2) {
-    // the attention kernel counts each segment's finished pieces from zero
-    if (blockIdx.x == 0 && blockIdx.y == 0)
+    // the attention kernel counts each segment's finished pieces from zero and reads
+    // the work split computed here once (the first wave of block (0, 0); all 64
+    // lanes take part in the plan's cross-lane sums)
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
       for (int i = d; i < p.B * p.Hkv; i += blockDim.x) p.seg_cnt[i] = 0;
+      if (d < 64) {
+        const BatchLens bl = batch_lens(p);
+        const Pieces pc = piece_plan(p, bl);
+        if (d == 0) {
+          p.plan[0] = pc.chunk;
+          p.plan[1] = pc.n;
+        }
+      }
+    }
     // a sequence without visible keys has no pieces: its output rows are zero (a
     // skipped sequence's rows are left untouched)
     if (hs < p.Hq && d < p.D && seq_ok(p, p.cache_len[b])) {
@@ -459,7 +472,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int M = p.M, G = p.G;
 
   const BatchLens bl = batch_lens(p);
-  const Pieces pc = piece_plan(p, bl);
+  const Pieces pc = {p.plan[0], p.plan[1]};   // computed once by rope_append_kernel
   const int slot = blockIdx.x;  // this workgroup's piece
   if (slot >= pc.n) return;
   int b, kvh, first, count;
@@ -1082,7 +1095,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
   const int64_t L = p.cache_len[b];
   if (!seq_ok(p, L)) return;
   const BatchLens bl = batch_lens(p);
-  const Pieces pc = piece_plan(p, bl);
+  const Pieces pc = {p.plan[0], p.plan[1]};
   int first, nb;
   segment_pieces(p, bl, pc.chunk, b, kvh, first, nb);
   int64_t lo, len;
@@ -1121,7 +1134,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
 static constexpr int kAttnNwgMax = 2048;
 
 struct AttnPlan {
-  size_t q_rot_bytes, acc_bytes, ml_bytes, cnt_bytes, total;
+  size_t q_rot_bytes, acc_bytes, ml_bytes, cnt_bytes, plan_bytes, total;
   int M, slots;
 };
 
@@ -1135,8 +1148,9 @@ static AttnPlan attn_plan(const sv_attn_desc& d) {
     pl.acc_bytes = align_up((size_t)pl.slots * pl.M * d.head_dim * 4, 256);
     pl.ml_bytes = align_up((size_t)pl.slots * pl.M * 2 * 4, 256);
     pl.cnt_bytes = align_up((size_t)d.batch * d.n_heads_kv * 4, 256);
+    pl.plan_bytes = 256;
   }
-  pl.total = pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes + pl.cnt_bytes;
+  pl.total = pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes + pl.cnt_bytes + pl.plan_bytes;
   return pl;
 }
 
@@ -1249,6 +1263,7 @@ static int verify_attn(const sv_attn_desc* d, const void* q, const void* k_new, 
   p.part_acc = (float*)(ws + pl.q_rot_bytes);
   p.part_ml = (float*)(ws + pl.q_rot_bytes + pl.acc_bytes);
   p.seg_cnt = (int32_t*)(ws + pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes);
+  p.plan = (int32_t*)(ws + pl.q_rot_bytes + pl.acc_bytes + pl.ml_bytes + pl.cnt_bytes);
   p.part_acc_bytes = (int)pl.acc_bytes;
   p.part_ml_bytes = (int)pl.ml_bytes;
   p.dev_status = dev_status;
