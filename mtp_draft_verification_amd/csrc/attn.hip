@@ -141,27 +141,34 @@ __device__ __forceinline__ int pieces_at(const AttnParams& p, const BatchLens& b
 }
 
 __device__ __forceinline__ Pieces piece_plan(const AttnParams& p, const BatchLens& bl) {
-  int64_t total = 0;
+  // per-lane partial sums stay far below 2^31 before the cross-lane sums; the four
+  // reductions share their shuffle steps so their latencies overlap
+  int64_t tl = 0;
   int nseg = 0, maxlen = 0;
 #pragma unroll
   for (int g = 0; g < kPlanGroups; ++g) {
-    // per-lane partial sums stay far below 2^31 before the cross-lane sum
-    total += bl.len[g];
+    tl += bl.len[g];
     nseg += bl.len[g] > 0 ? 1 : 0;
     maxlen = max(maxlen, bl.len[g]);
   }
-  {
-    const int lo32 = wave_sum_i((int)(total & 0xffff)), hi32 = wave_sum_i((int)(total >> 16));
-    total = ((int64_t)hi32 << 16) + lo32;
+  int lo32 = (int)(tl & 0xffff), hi32 = (int)(tl >> 16);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    const int a = __shfl_xor(lo32, m, 64), b = __shfl_xor(hi32, m, 64);
+    const int c = __shfl_xor(nseg, m, 64), d = __shfl_xor(maxlen, m, 64);
+    lo32 += a;
+    hi32 += b;
+    nseg += c;
+    maxlen = max(maxlen, d);
   }
-  total *= p.Hkv;
-  nseg = wave_sum_i(nseg) * p.Hkv;
-  maxlen = wave_max_i(maxlen);
+  const int64_t total = (((int64_t)hi32 << 16) + lo32) * p.Hkv;
+  nseg *= p.Hkv;
   if (total == 0) return {64, 0};
   auto up64 = [](int64_t x) { return (int)((x + 63) & ~int64_t(63)); };
   int c = up64((total + p.nwg - 1) / p.nwg);
   if (c < p.min_chunk) c = p.min_chunk;
-  if (pieces_at(p, bl, c) > p.nwg) {
+  int n = pieces_at(p, bl, c);
+  if (n > p.nwg) {
     if (nseg >= p.nwg) {
       c = up64(maxlen);
     } else {
@@ -175,8 +182,9 @@ __device__ __forceinline__ Pieces piece_plan(const AttnParams& p, const BatchLen
       }
       c = hi;
     }
+    n = pieces_at(p, bl, c);
   }
-  return {c, pieces_at(p, bl, c)};
+  return {c, n};
 }
 
 // piece q -> sequence b, kv head kvh, its keys [a0, a1), and the pieces of its
