@@ -453,6 +453,39 @@ def bench_drafter(cfg, W, caches, lens, dev, cycles: int = 10, warmup: int = 2) 
         "unembed_us": un_us, "unembed_read_bytes": int(cl_bytes),
         "note": "unembed_us includes the final norm and W_up projection, as calls_us.unembed does"}
     del drc, cu
+    torch.cuda.empty_cache()
+    # the same drafter reading fp8 E4M3 copies (per-channel scales) of the caches of
+    # the two target layers it reads
+    log("drafter: fp8 caches of the layers it reads")
+    caches8 = list(caches)
+    scales = {}
+    for ti in sorted(set(dr.reads)):
+        ly = cfg.layers[ti]
+        ks = inputs.channel_scales((ly.n_heads_kv, ly.head_dim), 1.0, 1, f"ks{ti}", dev)
+        vs = None if ly.k_is_v else inputs.channel_scales((ly.n_heads_kv, ly.head_dim), 1.0, 1, f"vs{ti}", dev)
+        caches8[ti] = {"k": inputs.fp8_codes(caches[ti]["k"].shape, 1.0, ks, 1, f"k8{ti}", dev),
+                       "v": None if vs is None else inputs.fp8_codes(caches[ti]["v"].shape, 1.0, vs, 1, f"v8{ti}", dev)}
+        scales[ti] = (ks, vs)
+    dr8 = Drafter(cfg, dcfg, W["E"], dw, caches8, cl, dev, kv_scales=scales)
+    for _ in range(warmup):
+        dr8.draft(k, h, acc, drafts)
+    torch.cuda.synchronize()
+    dr8.timers = {f"D{gi}.attn": []}
+    dr8.draft(k, h, acc, drafts)
+    torch.cuda.synchronize()
+    g8_us = round(float(np.median([a.elapsed_time(b) for a, b in dr8.timers[f"D{gi}.attn"]])) * 1e3, 2)
+    dr8.timers = None
+    e0.record()
+    for _ in range(cycles):
+        dr8.draft(k, h, acc, drafts)
+    e1.record()
+    torch.cuda.synchronize()
+    ms8 = e0.elapsed_time(e1) / cycles
+    assert int(dr8.dev_status.item()) == 0
+    out["fp8_kv"] = {"ms_per_k_steps": round(ms8, 4), "ms_per_step": round(ms8 / k, 4), "global_block_us": g8_us,
+                     "global_block_read_bytes_per_step": int(g_bytes // 2),
+                     "global_block_GB/s": round(g_bytes / 2 / (g8_us * 1e-6) / 1e9, 1)}
+    del dr8, caches8
     return out
 
 

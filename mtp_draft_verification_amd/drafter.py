@@ -19,6 +19,10 @@ draft) proposes k tokens one at a time.  Step i, for every sequence b:
     or, with a clustering of E given (section 4.3, cheap_unembed), the argmax over
     the tokens of the clusters whose centroids score highest   sv_cluster_unembed
 
+The target's caches may be fp8 E4M3 codes with per-channel scales (kv_scales given
+for the layers the drafter reads): the blocks then read them with
+sv_verify_attn_fp8.
+
 h_prev and the token of step 0 are the verify step's final hidden state at the
 accepted row and its next token (both read through sv_accept_out); later steps use
 the previous step's h and draft.  Everything runs on one stream, nothing is
@@ -37,7 +41,8 @@ class Drafter:
     """Device-resident drafter: weights, buffers and descriptors for batch B."""
 
     def __init__(self, target_cfg, dcfg, target_E: torch.Tensor, weights: dict, caches: list,
-                 cache_len: torch.Tensor, device="cuda", clusters: dict | None = None):
+                 cache_len: torch.Tensor, device="cuda", clusters: dict | None = None,
+                 kv_scales: dict | None = None):
         if target_cfg.dtype != "bf16":
             raise ValueError("the drafter path is bf16")
         self.t = target_cfg
@@ -46,6 +51,8 @@ class Drafter:
         self.W = weights
         self.caches = caches
         self.cache_len = cache_len
+        # fp8 caches: {target layer: (k_scale [Hkv, D], v_scale or None)}
+        self.kv_scales = kv_scales or {}
         self.dev = torch.device(device)
         B, d, dd = target_cfg.batch, target_cfg.d_model, dcfg.d_draft
         self.B = B
@@ -160,8 +167,13 @@ class Drafter:
             L.sv_linear(self._lin(dd, nq, L.SV_EPI_SPLIT_F32), a, bw["wq"], qp, None, stream)
             o = self.o.view(-1)[:B * nq].view(B, nq)
             kc = self.caches[ti]
-            L.sv_verify_attn(self._attn_desc(j, i), qp, None, None, kc["k"], kc["v"], self.cache_len, o,
-                             self.attn_ws, self.dev_status, stream)
+            if ti in self.kv_scales:
+                ks, vs = self.kv_scales[ti]
+                L.sv_verify_attn_fp8(self._attn_desc(j, i), qp, None, None, kc["k"], kc["v"], ks, vs, self.cache_len,
+                                     o, self.attn_ws, self.dev_status, stream)
+            else:
+                L.sv_verify_attn(self._attn_desc(j, i), qp, None, None, kc["k"], kc["v"], self.cache_len, o,
+                                 self.attn_ws, self.dev_status, stream)
             pending = self._residual(o, bw["wo"], stream)
             self._end(tok)
             tok = self._ev(f"D{j}.mlp", stream)

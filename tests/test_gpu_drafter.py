@@ -26,7 +26,7 @@ def host_caches(caches):
     return [{"k": inputs.host_f32(c["k"]), "v": None if c["v"] is None else inputs.host_f32(c["v"])} for c in caches]
 
 
-def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0):
+def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
     dev = need_gpu()
     B = tcfg.batch
     say(f"[drafter] d={tcfg.d_model} d_draft={dcfg.d_draft} B={B} k={k} lens={lens}")
@@ -34,6 +34,18 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0):
     tw = inputs.stack_weights(tcfg, seed, dev)
     dw = inputs.drafter_weights(tcfg, dcfg, seed, dev)
     caches = inputs.stack_caches(dataclass_replace(tcfg, ctx=max(lens)), seed, dev, capacity=cap)
+    kv_scales = None
+    if fp8:
+        # the layers the drafter reads hold fp8 codes with per-channel scales
+        kv_scales = {}
+        for ti in set(dcfg.target_layers(tcfg)):
+            ly = tcfg.layers[ti]
+            ks = inputs.channel_scales((ly.n_heads_kv, ly.head_dim), 1.0, seed, f"ks{ti}", dev)
+            vs = None if ly.k_is_v else inputs.channel_scales((ly.n_heads_kv, ly.head_dim), 1.0, seed, f"vs{ti}", dev)
+            caches[ti] = {"k": inputs.fp8_codes(caches[ti]["k"].shape, 1.0, ks, seed, f"k8{ti}", dev),
+                          "v": None if vs is None else inputs.fp8_codes(caches[ti]["v"].shape, 1.0, vs, seed,
+                                                                       f"v8{ti}", dev)}
+            kv_scales[ti] = (ks, vs)
     cl = torch.tensor(lens, dtype=torch.int32, device=dev)
     R = B * (tcfg.k + 1)
     h_verify = inputs.normal((R, tcfg.d_model), 1.0, seed, "h_verify", dev)
@@ -44,7 +56,7 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0):
     acc[:, 1] = inputs.randint((B,), 0, tcfg.vocab - 1, seed, "next_tok", dev)
     drafts = torch.full((B, k), -1, dtype=torch.int32, device=dev)
     cu = inputs.clusters_of(tw["E"], n_clusters, top, seed) if n_clusters else None
-    dr = Drafter(tcfg, dcfg, tw["E"], dw, caches, cl, dev, clusters=cu)
+    dr = Drafter(tcfg, dcfg, tw["E"], dw, caches, cl, dev, clusters=cu, kv_scales=kv_scales)
     if cu is not None:
         cu_host = (inputs.bf16_bits(cu["centroids"]), inputs.bf16_bits(cu["w_perm"]), cu["perm"].cpu().numpy())
 
@@ -52,7 +64,12 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0):
                          {"E": inputs.bf16_bits(dw["E"]), "w_down": inputs.bf16_bits(dw["w_down"]),
                           "w_up": inputs.bf16_bits(dw["w_up"]),
                           "blocks": [{kk: inputs.bf16_bits(v) for kk, v in bw.items()} for bw in dw["blocks"]]})
-    st = om.new_state(host_caches(caches), lens)
+    hc = host_caches(caches) if not fp8 else [
+        {"k": oracle.dequant_cache(c["k"].cpu().numpy(), kv_scales[ti][0].cpu().numpy()[None, :, None, :]),
+         "v": None if c["v"] is None else oracle.dequant_cache(c["v"].cpu().numpy(),
+                                                                kv_scales[ti][1].cpu().numpy()[None, :, None, :])}
+        if ti in kv_scales else host_caches([c])[0] for ti, c in enumerate(caches)]
+    st = om.new_state(hc, lens)
     h_prev = host(h_verify)[[b * (tcfg.k + 1) + int(hr[b]) for b in range(B)]]
     tok = acc[:, 1].cpu().numpy()
     checked = 0
@@ -115,3 +132,11 @@ def test_drafter_clustered_unembed():
                                 window=64, local_heads=(4, 2, 128), global_heads=(4, 1, 256))
     drafter_case(tcfg, configs.scaled_drafter(d_draft=128, d_ff=256), [100, 7, 300, 64], 3, 3,
                  n_clusters=64, top=8)
+
+
+@gpu
+def test_drafter_fp8_caches():
+    # the drafter reading fp8 E4M3 caches (per-channel scales) of the target's layers
+    tcfg = configs.scaled_stack(name="drafter_target4", d_model=256, vocab=4096, d_ff=512, batch=3, k=3,
+                                window=64, local_heads=(4, 2, 128), global_heads=(4, 1, 256))
+    drafter_case(tcfg, configs.scaled_drafter(d_draft=128, d_ff=256), [200, 37, 500], 3, 4, fp8=True)
