@@ -941,73 +941,67 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       __syncthreads();
       if (s_flag[0] != count - 1) return;
 
-      // ---- merge of the segment's pieces [first, first + count): per row the
-      // largest reference, then out = sum_w 2^(m_w - Mx) O_w / sum_w 2^(m_w - Mx) l_w
-      float* s_mx = &s_max[0][0][0];  // [M] (4 * MT * 16 >= M floats)
-      float* s_inv = &s_sum[0][0][0];
+      // ---- merge of the segment's pieces [first, first + count) in one pass: each
+      // thread keeps, for its output quads, the running reference mx, the sum l and
+      // the output rescaled to it, so that out = sum_w 2^(m_w - mx) O_w /
+      // sum_w 2^(m_w - mx) l_w needs one round of loads per batch of PB pieces (with
+      // all of a batch's loads in flight; slots past the segment re-read its last
+      // piece, so that every loaded value is finite, and are masked out).  Up to PB
+      // pieces, mx is the largest reference of the row and no rescaling happens.
       auto ld_ml = [&](int w, int r, int e) {
         return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             ml_rsrc, (uint32_t)((((int64_t)w * M + r) * 2 + e) * 4), 0, kCoherent));
       };
-      // pieces are read in batches of PB with all of a batch's loads in flight (a
-      // buffer load past the end of the partials returns 0 and is masked out)
-      constexpr int PB = 8;
       const int wend = first + count;
-      for (int r = tid; r < M; r += 256) {
-        // one pass: running maximum and the sum rescaled to it
-        float mx = kNegInf, l = 0.f;
-        for (int w0 = first; w0 < wend; w0 += PB) {
-          float mv[PB], lv[PB];
-#pragma unroll
-          for (int k = 0; k < PB; ++k) {
-            mv[k] = ld_ml(w0 + k, r, 0);
-            lv[k] = ld_ml(w0 + k, r, 1);
-          }
-          float nmx = mx;
-#pragma unroll
-          for (int k = 0; k < PB; ++k) nmx = (w0 + k < wend) ? fmaxf(nmx, mv[k]) : nmx;
-          if (nmx == kNegInf) continue;
-          l *= mx == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx - nmx);
-#pragma unroll
-          for (int k = 0; k < PB; ++k)
-            if (w0 + k < wend && mv[k] != kNegInf) l += __builtin_amdgcn_exp2f(mv[k] - nmx) * lv[k];
-          mx = nmx;
-        }
-        s_mx[r] = mx;
-        s_inv[r] = l > 0.f ? 1.f / l : 0.f;
-      }
-      __syncthreads();
-      // two output quads per thread and pass, all their loads in flight together
+      // two output quads per thread and pass; batches of 4 pieces where that is all
+      // there are (fewer redundant loads), else of 8
       constexpr int DQ = D / 4;
       constexpr int NIT = 2;
+      auto merge = [&](auto pb) __attribute__((always_inline)) {
+      constexpr int PB = decltype(pb)::value;
       for (int i0 = tid; i0 < M * DQ; i0 += 256 * NIT) {
-        float acc[NIT][4];
+        f32x4_t acc[NIT];
+        float mx[NIT], l[NIT];
         int rr[NIT], dd[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const int i = i0 + it * 256 < M * DQ ? i0 + it * 256 : i0;
           rr[it] = i / DQ;
           dd[it] = (i - rr[it] * DQ) * 4;
-          acc[it][0] = acc[it][1] = acc[it][2] = acc[it][3] = 0.f;
+          acc[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          mx[it] = kNegInf;
+          l[it] = 0.f;
         }
         for (int w0 = first; w0 < wend; w0 += PB) {
-          float mv[NIT][PB];
+          float mv[NIT][PB], lv[NIT][PB];
           f32x4_t v[NIT][PB];
 #pragma unroll
           for (int it = 0; it < NIT; ++it)
 #pragma unroll
             for (int k = 0; k < PB; ++k) {
-              mv[it][k] = ld_ml(w0 + k, rr[it], 0);
+              const int wk = w0 + k < wend ? w0 + k : wend - 1;
+              mv[it][k] = ld_ml(wk, rr[it], 0);
+              lv[it][k] = ld_ml(wk, rr[it], 1);
               v[it][k] = __builtin_amdgcn_raw_buffer_load_b128(
-                  acc_rsrc, (uint32_t)((((int64_t)(w0 + k) * M + rr[it]) * D + dd[it]) * 4), 0, kCoherent);
+                  acc_rsrc, (uint32_t)((((int64_t)wk * M + rr[it]) * D + dd[it]) * 4), 0, kCoherent);
             }
 #pragma unroll
           for (int it = 0; it < NIT; ++it) {
-            const float mx = s_mx[rr[it]];
+            // a piece that saw no key of this row has m = -inf and acc = 0
+            float nmx = mx[it];
+#pragma unroll
+            for (int k = 0; k < PB; ++k) nmx = (w0 + k < wend) ? fmaxf(nmx, mv[it][k]) : nmx;
+            if (nmx == kNegInf) continue;
+            if (mx[it] != nmx) {
+              const float a = mx[it] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx[it] - nmx);
+              l[it] *= a;
+              acc[it][0] *= a; acc[it][1] *= a; acc[it][2] *= a; acc[it][3] *= a;
+              mx[it] = nmx;
+            }
 #pragma unroll
             for (int k = 0; k < PB; ++k) {
-              // a piece that saw no key of this row has m = -inf and acc = 0
-              const float f = (w0 + k < wend && mv[it][k] != kNegInf) ? __builtin_amdgcn_exp2f(mv[it][k] - mx) : 0.f;
+              const float f = (w0 + k < wend && mv[it][k] != kNegInf) ? __builtin_amdgcn_exp2f(mv[it][k] - nmx) : 0.f;
+              l[it] += f * lv[it][k];
               acc[it][0] += f * v[it][k][0]; acc[it][1] += f * v[it][k][1];
               acc[it][2] += f * v[it][k][2]; acc[it][3] += f * v[it][k][3];
             }
@@ -1017,13 +1011,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         for (int it = 0; it < NIT; ++it) {
           if (i0 + it * 256 >= M * DQ) continue;
           const int r = rr[it];
-          const float inv = s_inv[r];
+          const float inv = l[it] > 0.f ? 1.f / l[it] : 0.f;
           const int j = r / G, hg = r - (r / G) * G;
           uint16_t* out = (uint16_t*)p.out + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + dd[it];
           *(uint2*)out = make_uint2(pack_bf16x2(acc[it][0] * inv, acc[it][1] * inv),
                                     pack_bf16x2(acc[it][2] * inv, acc[it][3] * inv));
         }
       }
+      };
+      if (count <= 4) merge(std::integral_constant<int, 4>{});
+      else merge(std::integral_constant<int, 8>{});
     }
   }
 }
@@ -1120,20 +1117,40 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
     *(uint2*)(out + d0) = make_uint2(0, 0);
     return;
   }
-  float Mx = kNegInf;
-  for (int64_t w = w0; w <= w1; ++w) Mx = fmaxf(Mx, p.part_ml[(w * p.M + r) * 2]);
-  float l = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  if (Mx != kNegInf) {
-    for (int64_t w = w0; w <= w1; ++w) {
-      const int64_t slot = w;
-      const float m = p.part_ml[(slot * p.M + r) * 2];
-      if (m == kNegInf) continue;
-      const float f = exp2f(m - Mx);
-      l += f * p.part_ml[(slot * p.M + r) * 2 + 1];
-      const f32x4_t v = *(const f32x4_t*)(p.part_acc + (slot * p.M + r) * D + d0);
-      a0 += f * v[0]; a1 += f * v[1]; a2 += f * v[2]; a3 += f * v[3];
+  // one pass over the pieces in batches of PB, all of a batch's loads in flight:
+  // the running reference mx, the sum l and the output a rescaled to it (slots
+  // past the segment re-read its last piece and are masked out)
+  constexpr int PB = 8;
+  float mx = kNegInf, l = 0.f;
+  f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t wb = w0; wb <= w1; wb += PB) {
+    float mv[PB], lv[PB];
+    f32x4_t v[PB];
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int64_t slot = wb + k <= w1 ? wb + k : w1;
+      mv[k] = p.part_ml[(slot * p.M + r) * 2];
+      lv[k] = p.part_ml[(slot * p.M + r) * 2 + 1];
+      v[k] = *(const f32x4_t*)(p.part_acc + (slot * p.M + r) * D + d0);
+    }
+    float nmx = mx;
+#pragma unroll
+    for (int k = 0; k < PB; ++k) nmx = wb + k <= w1 ? fmaxf(nmx, mv[k]) : nmx;
+    if (nmx == kNegInf) continue;  // a piece that saw no key of this row has m = -inf, acc = 0
+    if (mx != nmx) {
+      const float c = mx == kNegInf ? 0.f : exp2f(mx - nmx);
+      l *= c;
+      a[0] *= c; a[1] *= c; a[2] *= c; a[3] *= c;
+      mx = nmx;
+    }
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const float f = (wb + k <= w1 && mv[k] != kNegInf) ? exp2f(mv[k] - nmx) : 0.f;
+      l += f * lv[k];
+      a[0] += f * v[k][0]; a[1] += f * v[k][1]; a[2] += f * v[k][2]; a[3] += f * v[k][3];
     }
   }
+  const float a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
   const float inv = l > 0.f ? 1.f / l : 0.f;
   *(uint2*)(out + d0) = make_uint2(pack_bf16x2(a0 * inv, a1 * inv), pack_bf16x2(a2 * inv, a3 * inv));
 }
