@@ -62,8 +62,7 @@ __device__ __forceinline__ bool seq_ok(const AttnParams& p, int64_t L) {
   return L <= p.cap;
 }
 
-__device__ __forceinline__ void seq_range(const AttnParams& p, int b, int64_t& lo, int64_t& len) {
-  const int64_t L = p.cache_len[b];
+__device__ __forceinline__ void seq_range_of(const AttnParams& p, int64_t L, int64_t& lo, int64_t& len) {
   lo = 0;
   len = 0;
   if (!seq_ok(p, L)) return;
@@ -78,6 +77,9 @@ __device__ __forceinline__ void seq_range(const AttnParams& p, int b, int64_t& l
   }
   lo = l0;
   len = hi > l0 ? hi - l0 : 0;
+}
+__device__ __forceinline__ void seq_range(const AttnParams& p, int b, int64_t& lo, int64_t& len) {
+  seq_range_of(p, p.cache_len[b], lo, len);
 }
 
 // Work split: each (sequence, kv head) segment of keys is cut into pieces of
@@ -98,6 +100,7 @@ struct Pieces {
 };
 struct BatchLens {
   int len[kPlanGroups];  // key count of sequence lane + 64 g (0 past the batch)
+  int L[kPlanGroups];    // its committed length
 };
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -127,8 +130,10 @@ __device__ __forceinline__ BatchLens batch_lens(const AttnParams& p) {
   for (int g = 0; g < kPlanGroups; ++g) {
     const int b = lane + 64 * g;
     int64_t lo = 0, len = 0;
-    if (b < p.B) seq_range(p, b, lo, len);
+    const int L = b < p.B ? p.cache_len[b] : 0;
+    if (b < p.B) seq_range_of(p, L, lo, len);
     bl.len[g] = (int)len;
+    bl.L[g] = L;
   }
   return bl;
 }
@@ -190,7 +195,8 @@ __device__ __forceinline__ Pieces piece_plan(const AttnParams& p, const BatchLen
 // piece q -> sequence b, kv head kvh, its keys [a0, a1), and the pieces of its
 // segment [first, first + count)
 __device__ __forceinline__ void piece_locate(const AttnParams& p, const BatchLens& bl, int chunk, int q, int& b,
-                                             int& kvh, int64_t& a0, int64_t& a1, int& first, int& count) {
+                                             int& kvh, int64_t& a0, int64_t& a1, int& first, int& count,
+                                             int64_t& Lb) {
   const int lane = threadIdx.x & 63;
   int base = 0;  // pieces of the sequences before this group
   b = -1;
@@ -208,7 +214,8 @@ __device__ __forceinline__ void piece_locate(const AttnParams& p, const BatchLen
       kvh = rem / nb;
       const int pi = rem - kvh * nb;
       int64_t lo, len;
-      seq_range(p, b, lo, len);
+      Lb = __shfl(bl.L[g], l, 64);  // the committed length, without reloading it
+      seq_range_of(p, Lb, lo, len);
       a0 = lo + (int64_t)pi * chunk;
       a1 = lo + ((int64_t)(pi + 1) * chunk < len ? (int64_t)(pi + 1) * chunk : len);
       first = q - pi;
@@ -222,6 +229,7 @@ __device__ __forceinline__ void piece_locate(const AttnParams& p, const BatchLen
     a0 = a1 = 0;
     first = q;
     count = 1;
+    Lb = 0;
   }
 }
 
@@ -485,14 +493,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   if (slot >= pc.n) return;
   int b, kvh, first, count;
   int64_t a0, a1;  // keys [a0, a1) of sequence b, kv head kvh
-  piece_locate(p, bl, pc.chunk, slot, b, kvh, a0, a1, first, count);
+  int64_t L;       // committed length of sequence b
+  piece_locate(p, bl, pc.chunk, slot, b, kvh, a0, a1, first, count, L);
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
   const unsigned char* kcache = (const unsigned char*)p.k_cache;
   const unsigned char* vcache = (const unsigned char*)p.v_cache;
   {
     {
-      const int64_t L = p.cache_len[b];
       const int64_t last = L + p.n_new - 1;
       const int ntiles = (int)((a1 - a0 + TK - 1) / TK);
 
