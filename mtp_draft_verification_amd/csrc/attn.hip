@@ -773,8 +773,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             sc[j][i] = (full || (kl >= lo_l && kl <= hi_l)) ? sacc[j][i] * p.scale_log2 : kNegInf;
             mx = fmaxf(mx, sc[j][i]);
           }
-          mx = fmaxf(mx, shfl_xor_f(mx, 16));
-          mx = fmaxf(mx, shfl_xor_f(mx, 32));
+          mx = row4_max(mx);
           if (lg == 0) s_max[pkt[j]][pmt[j]][lr] = mx;
           over |= mx > pick(m_run, pmt[j]) + 8.f;
         }
@@ -799,8 +798,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             s_p[pkt[j]][pmt[j]][lane] = w2;
             // the normaliser sums exactly the (bf16) weights the PV product uses
             float rs = bf16_lo(w2.x) + bf16_hi(w2.x) + bf16_lo(w2.y) + bf16_hi(w2.y);
-            rs += shfl_xor_f(rs, 16);
-            rs += shfl_xor_f(rs, 32);
+            rs = row4_sum(rs);
             rsum[j] = rs;
           }
         };

@@ -61,6 +61,24 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), with the
+// gfx950 row-swap instructions (plain vector ALU ops, no trip through the LDS unit like
+// a general shuffle).  v_permlane16_swap(x, x) leaves rows (0,0,2,2) in its first result
+// and (1,1,3,3) in its second; v_permlane32_swap(y, y) leaves (0,1,0,1) and (2,3,2,3).
+// The sum is (x0 + x1) + (x2 + x3) in every row, as the xor-16-then-32 shuffle gives.
+__device__ __forceinline__ float row4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // "a beats b" in the order (value descending, id ascending); id < 0 is an empty slot.
 // Written with bitwise operators and selects below, so that lanes never diverge.
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
