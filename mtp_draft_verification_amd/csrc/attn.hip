@@ -770,7 +770,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int kl = pkt[j] * 16 + lg * 4 + i;
-            sc[j][i] = (full || (kl >= lo_l && kl <= hi_l)) ? sacc[j][i] * p.scale_log2 : kNegInf;
+            // (full tiles keep lo_l = -1, hi_l = TK; the test is written with bitwise
+            // operators so that it compiles to compares and a select, not branches)
+            sc[j][i] = ((kl >= lo_l) & (kl <= hi_l)) ? sacc[j][i] * p.scale_log2 : kNegInf;
             mx = fmaxf(mx, sc[j][i]);
           }
           mx = row4_max(mx);
