@@ -495,6 +495,21 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   int64_t a0, a1;  // keys [a0, a1) of sequence b, kv head kvh
   int64_t L;       // committed length of sequence b
   piece_locate(p, bl, pc.chunk, slot, b, kvh, a0, a1, first, count, L);
+  // the piece is the same for the whole workgroup: in scalar registers, every tile-level
+  // decision below (tile count, stage waits, masking, the last partial tile) is a
+  // scalar branch rather than an exec-mask one
+  auto uni64 = [](int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+  };
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  first = __builtin_amdgcn_readfirstlane(first);
+  count = __builtin_amdgcn_readfirstlane(count);
+  a0 = uni64(a0);
+  a1 = uni64(a1);
+  L = uni64(L);
 
   const uint16_t* qrot = (const uint16_t*)p.q_rot;
   const unsigned char* kcache = (const unsigned char*)p.k_cache;
