@@ -822,20 +822,27 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         weights();
         lds_barrier();  // weights, maxima and flags of every wave visible
 
-        if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {  // same decision on every wave
+        // the same decision on every wave (a scalar branch: the rescale of the output
+        // accumulators then stays inside this rare path)
+        if (__builtin_amdgcn_readfirstlane(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3])) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const float tmax = fmaxf(fmaxf(s_max[0][mt][lr], s_max[1][mt][lr]), fmaxf(s_max[2][mt][lr], s_max[3][mt][lr]));
-            if (tmax > m_run[mt] + 8.f) {
-              const float m_new = tmax;
-              const float alpha = m_run[mt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[mt] - m_new);
-              l_run[mt] *= alpha;
-              m_run[mt] = m_new;
+            // rows whose maximum moved get the new reference; the others keep theirs
+            // (alpha = 1), without a branch per lane
+            const bool mv = tmax > m_run[mt] + 8.f;
+            const float m_new = mv ? tmax : m_run[mt];
+            const float alpha = !mv ? 1.f : (m_run[mt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[mt] - m_new));
+            l_run[mt] *= alpha;
+            m_run[mt] = m_new;
 #pragma unroll
-              for (int dt = 0; dt < DT; ++dt) {
-                O[dt][mt][0] *= alpha; O[dt][mt][1] *= alpha;
-                O[dt][mt][2] *= alpha; O[dt][mt][3] *= alpha;
-              }
+            for (int dt = 0; dt < DT; ++dt) {
+              // (an empty statement that takes the accumulators where the MFMAs keep
+              // them: their copies for the multiply are then made here, in this rare
+              // branch, and not at the top of every tile)
+              asm volatile("" : "+a"(O[dt][mt]));
+              O[dt][mt][0] *= alpha; O[dt][mt][1] *= alpha;
+              O[dt][mt][2] *= alpha; O[dt][mt][3] *= alpha;
             }
           }
           weights();
