@@ -1020,13 +1020,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             float nmx = mx[it];
 #pragma unroll
             for (int k = 0; k < PB; ++k) nmx = (w0 + k < wend) ? fmaxf(nmx, mv[it][k]) : nmx;
-            if (nmx == kNegInf) continue;
-            if (mx[it] != nmx) {
-              const float a = mx[it] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx[it] - nmx);
-              l[it] *= a;
-              acc[it][0] *= a; acc[it][1] *= a; acc[it][2] *= a; acc[it][3] *= a;
-              mx[it] = nmx;
-            }
+            // without per-lane branches: a = 1 leaves the state as it is (also when no
+            // piece so far saw a key of this row, nmx = -inf, where every f below is 0)
+            const float a = mx[it] == nmx ? 1.f : (mx[it] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mx[it] - nmx));
+            l[it] *= a;
+            acc[it][0] *= a; acc[it][1] *= a; acc[it][2] *= a; acc[it][3] *= a;
+            mx[it] = nmx;
 #pragma unroll
             for (int k = 0; k < PB; ++k) {
               const float f = (w0 + k < wend && mv[it][k] != kNegInf) ? __builtin_amdgcn_exp2f(mv[it][k] - nmx) : 0.f;
@@ -1165,13 +1164,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
     float nmx = mx;
 #pragma unroll
     for (int k = 0; k < PB; ++k) nmx = wb + k <= w1 ? fmaxf(nmx, mv[k]) : nmx;
-    if (nmx == kNegInf) continue;  // a piece that saw no key of this row has m = -inf, acc = 0
-    if (mx != nmx) {
-      const float c = mx == kNegInf ? 0.f : exp2f(mx - nmx);
-      l *= c;
-      a[0] *= c; a[1] *= c; a[2] *= c; a[3] *= c;
-      mx = nmx;
-    }
+    // a piece that saw no key of this row has m = -inf, acc = 0; c = 1 leaves the state
+    // as it is, without a per-lane branch
+    const float c = mx == nmx ? 1.f : (mx == kNegInf ? 0.f : exp2f(mx - nmx));
+    l *= c;
+    a[0] *= c; a[1] *= c; a[2] *= c; a[3] *= c;
+    mx = nmx;
 #pragma unroll
     for (int k = 0; k < PB; ++k) {
       const float f = (wb + k <= w1 && mv[k] != kNegInf) ? exp2f(mv[k] - nmx) : 0.f;
