@@ -113,6 +113,21 @@ def test_head_dims_and_row_tiles(D):
 
 
 @gpu
+@pytest.mark.parametrize("kind", ["global", "local"])
+def test_fused_merge_many_pieces(kind):
+    """Few segments over long key ranges: each (sequence, KV head) segment is cut into
+    tens of pieces, so the merge that the last piece of a small-block segment runs
+    takes several batches of pieces, with the running reference moving between them."""
+    if kind == "global":
+        ly = configs.AttnLayer("global", 4, 2, 128, 0, 32, 1e6, True)
+        lens = [4096, 1500]
+    else:
+        ly = configs.AttnLayer("local", 4, 2, 256, 3000, 256, 1e4, False)
+        lens = [4096, 2999]
+    run_case(ly, 2, 5, lens, 4200, 21, tag=f"many-pieces-{kind}")
+
+
+@gpu
 def test_many_sequences_work_split():
     """70 sequences x 4 KV heads: more segments than compute units (one piece per
     segment), sequences past the first 64 lanes of the work-split scan, empty and
