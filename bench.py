@@ -364,7 +364,23 @@ def run_workload(cfg, W, steps, warmup, seed, dev, time_calls=None):
     ok = all(np.array_equal(L.decode_accept_out(vs.acc)["n_accepted"], rec_n[-1]) for _ in [0])
     assert ok, "replay diverged from the recorded trajectory"
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_t[dominant]]))
+
+    # per-step spread: one more replay with events around every step
+    cl.fill_(cfg.ctx)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    step_ev = []
+    for s in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        vs.step(rec_tok[s], rec_dr[s])
+        e1.record(st)
+        step_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    step_pct = np.percentile([a.elapsed_time(b) for a, b in step_ev], [10, 50, 90])
     res = dict(B=B, steps=steps, ms_total=ms, ms_per_step=ms / steps, committed=committed,
+               step_ms_p10_p50_p90=[round(float(x), 4) for x in step_pct],
                tokens_per_s=committed / (ms / 1e3), mean_accepted=float(np.mean(np.stack(rec_n))),
                call_ms=call_ms, call_bytes=byts, dominant=dominant, dominant_ms=dom_ms,
                first_tokens=rec_tok[0], first_len=rec_len[0], caches=caches)
@@ -665,6 +681,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep_tokens_per_s": sweep,
         "mean_accepted": round(main_res["mean_accepted"], 3),
+        "step_ms_p10_p50_p90": main_res["step_ms_p10_p50_p90"],
         "kernels": kern,
         "drafter": drafter,
         "fp8_kv_attention": fp8_kv,
