@@ -358,28 +358,54 @@ def run_workload(cfg, W, steps, warmup, seed, dev, time_calls=None):
     if time_calls:
         dominant = time_calls
 
-    # timed replay: the whole step, plus events around the dominant call only
+    # eager replay of the whole step, with events around the dominant call only
     dom_t = {dominant: []}
-    ms = replay(dom_t)
+    ms_eager = replay(dom_t)
     ok = all(np.array_equal(L.decode_accept_out(vs.acc)["n_accepted"], rec_n[-1]) for _ in [0])
     assert ok, "replay diverged from the recorded trajectory"
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_t[dominant]]))
 
-    # per-step spread: one more replay with events around every step
+    # timed replay: the step's launches captured once in a HIP graph, one replay per
+    # step on input buffers that take each step's tokens and drafts (no launch gaps
+    # from the host); then once more with events around every step for the spread
+    tok_buf = torch.empty_like(rec_tok[0])
+    dr_buf = torch.empty_like(rec_dr[0])
     cl.fill_(cfg.ctx)
     torch.cuda.synchronize()
-    st = torch.cuda.current_stream()
-    step_ev = []
-    for s in range(steps):
+    graph = vs.capture(tok_buf, dr_buf)
+
+    def replay_graph(step_ev=None):
+        cl.fill_(cfg.ctx)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(st)
-        vs.step(rec_tok[s], rec_dr[s])
+        for s in range(steps):
+            tok_buf.copy_(rec_tok[s])
+            dr_buf.copy_(rec_dr[s])
+            if step_ev is not None:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                graph.replay()
+                b.record(st)
+                step_ev.append((a, b))
+            else:
+                graph.replay()
         e1.record(st)
-        step_ev.append((e0, e1))
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    replay_graph()  # untimed: the first launch of a new graph also uploads it
+    ms = replay_graph()
+    ok = all(np.array_equal(L.decode_accept_out(vs.acc)["n_accepted"], rec_n[-1]) for _ in [0])
+    assert ok, "graph replay diverged from the recorded trajectory"
+    step_ev = []
+    replay_graph(step_ev)
     step_pct = np.percentile([a.elapsed_time(b) for a, b in step_ev], [10, 50, 90])
     res = dict(B=B, steps=steps, ms_total=ms, ms_per_step=ms / steps, committed=committed,
+               ms_per_step_eager=ms_eager / steps,
                step_ms_p10_p50_p90=[round(float(x), 4) for x in step_pct],
                tokens_per_s=committed / (ms / 1e3), mean_accepted=float(np.mean(np.stack(rec_n))),
                call_ms=call_ms, call_bytes=byts, dominant=dominant, dominant_ms=dom_ms,
@@ -682,6 +708,8 @@ def main():
         "sweep_tokens_per_s": sweep,
         "mean_accepted": round(main_res["mean_accepted"], 3),
         "step_ms_p10_p50_p90": main_res["step_ms_p10_p50_p90"],
+        "step_launch": "one HIP graph replay per step (the step's launches captured once)",
+        "ms_per_step_eager": round(main_res["ms_per_step_eager"], 4),
         "kernels": kern,
         "drafter": drafter,
         "fp8_kv_attention": fp8_kv,

@@ -261,3 +261,16 @@ class VerifyStack:
         h = self.forward(tokens, stream)
         self.select(h, drafts, stream)
         self.accept(drafts, stream)
+
+    def capture(self, tokens: torch.Tensor, drafts: torch.Tensor):
+        """Record one verify step on the input buffers `tokens` [B, k+1] and `drafts`
+        [B, k] into a HIP graph and return it (torch.cuda.CUDAGraph).  The step
+        allocates nothing, never waits on the host and clears nothing with a memset,
+        so every launch of it is captured as it is; each replay() runs the step on
+        whatever the two buffers hold at that time and commits on device like step()."""
+        if self.timers is not None:
+            raise RuntimeError("capture with per-call timers set")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(tokens, drafts)
+        return g
