@@ -203,6 +203,8 @@ def time_one(args, only) -> dict:
     gbs = byts / (us * 1e-6) / 1e9
     return {"call": only, "batch": B, "k": cfg.k, "ctx": cfg.ctx, "us_per_call": round(us, 2),
             "alg_bytes": int(byts), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            # verified positions per second (attention, LM head): the B (k+1) rows one call serves
+            "positions_per_s": round(B * nq / (us * 1e-6), 1) if only.startswith(("attn", "lmhead")) else None,
             "source_digest": source_digest()}
 
 
