@@ -573,14 +573,25 @@ def cpu_baseline(cfg, W, caches, tokens, lens, dev):
     model = om.OracleModel(cfg1, hw)
     state = om.new_state(hc, [L0])
     tok = tokens[:1].cpu().numpy()
-    log(f"cpu baseline: oracle step on {oracle.num_threads()} threads")
+    cores = oracle.num_threads()
+    log(f"cpu baseline: oracle step on {cores} threads")
     t0 = time.perf_counter()
     r = model.greedy_step(state, tok)
     dt = time.perf_counter() - t0
     n = int(r["n"][0]) + 1
-    return dict(value=n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    # the same step on one thread (from the same starting state)
+    log("cpu baseline: oracle step on 1 thread")
+    oracle.set_threads(1)
+    state1 = om.new_state(hc, [L0])
+    t0 = time.perf_counter()
+    model.greedy_step(state1, tok)
+    dt1 = time.perf_counter() - t0
+    oracle.set_threads(cores)
+    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
+                single_thread_value=n / dt1,
                 sample=f"one verify step of sequence 0 ({cfg.k + 1} rows, all 6 layers, LM head, accept) "
-                       f"of the same workload at its first recorded step: {n} tokens committed in {dt:.1f} s")
+                       f"of the same workload at its first recorded step: {n} tokens committed in {dt:.1f} s "
+                       f"on {cores} threads, {dt1:.1f} s on one")
 
 
 def pmc_summary(dirs):

@@ -107,6 +107,12 @@ def num_threads() -> int:
     return int(lib().svo_num_threads())
 
 
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (for timing; results do not
+    depend on the count)."""
+    lib().svo_set_threads(ctypes.c_int(int(n)))
+
+
 def _ptr(a: np.ndarray | None):
     if a is None:
         return None

@@ -44,6 +44,16 @@
 #include <omp.h>
 #endif
 
+/* threads the parallel loops use from now on (n >= 1); timing only, results do not
+ * depend on it */
+void svo_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int svo_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
