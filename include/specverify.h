@@ -27,7 +27,8 @@
  *   - Tensors are dense row-major with the last dimension contiguous.
  *     Positions: query row j of sequence b sits at absolute position
  *     cache_len[b] + q_pos_offset + j.
- *   - The library holds no mutable global state: calls on different streams
+ *   - The library holds no mutable global state (the one exception is the
+ *     static scratch of sv_verify_attn_noalloc): calls on different streams
  *     that touch disjoint memory may overlap.
  */
 #ifndef SPECVERIFY_H
@@ -46,7 +47,9 @@ typedef enum {
   SV_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. a head_dim with no kernel) */
   SV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace() query */
   SV_ERR_LAUNCH = -4,       /* the HIP runtime rejected a kernel launch */
-  SV_ERR_DEVICE = -5        /* no usable gfx950 device is current */
+  SV_ERR_DEVICE = -5,       /* no usable gfx950 device is current */
+  SV_ERR_SCRATCH = -6       /* sv_verify_attn_noalloc: the call needs more scratch than
+                               SV_NOALLOC_SCRATCH_BYTES */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -147,6 +150,27 @@ int sv_verify_attn_fp8(const sv_attn_desc* desc, const void* q, const void* k_ne
                        void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* cache_len, void* out, void* workspace, size_t workspace_bytes,
                        int32_t* dev_status, void* stream);
+
+/* For callers that cannot allocate device memory: code recorded under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc.  sv_verify_attn
+ * with the workspace replaced by a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES bytes inside the library: one copy per GPU, taken when
+ * the library's code is loaded on that GPU and held until the process ends.  The
+ * call allocates nothing and frees nothing.  Results are those of sv_verify_attn
+ * (the same kernels).
+ *   Arguments, layouts and device-side errors: as sv_verify_attn.
+ *   Every call on one GPU uses that GPU's single array, and each call sets what it
+ *   reads there itself (counters, work split), so calls ordered on one stream are
+ *   independent; calls that overlap in time on one GPU (several streams or host
+ *   threads) race on the array and give wrong results.
+ *   Returns SV_ERR_SCRATCH (nothing launched) when the descriptor needs more than
+ *   SV_NOALLOC_SCRATCH_BYTES of scratch on the current device: roughly
+ *   (compute units + B*Hkv) * (Hq/Hkv) * n_q * (head_dim + 2) * 4 bytes plus the
+ *   rotated queries, about 25 MiB for B = 8, 32 q / 4 KV heads, head_dim 512, n_q 5. */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int sv_verify_attn_noalloc(const sv_attn_desc* desc, const void* q, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* cache_len, void* out,
+                           int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* LM head + select                                                          */

@@ -15,7 +15,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
-SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE = 0, -1, -2, -3, -4, -5
+SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE, SV_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
+SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL, SV_SELECT_SAMPLE_RS = 0, 1, 2, 3
 SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU, SV_EPI_SPLIT_F32 = 0, 1, 2, 3
@@ -24,7 +25,8 @@ SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn", "sv_verify_attn_fp8",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
            "sv_add_rmsnorm", "sv_draft_input", "sv_linear_splits", "sv_linear_workspace", "sv_linear",
-           "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed", "sv_lmhead_select_rs", "sv_accept_rs")
+           "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed", "sv_lmhead_select_rs", "sv_accept_rs",
+           "sv_verify_attn_noalloc")
 
 
 class SvError(RuntimeError):
@@ -97,6 +99,8 @@ def load():
     L.sv_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
     L.sv_verify_attn.restype = ctypes.c_int
     L.sv_verify_attn.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, sz, P, P]
+    L.sv_verify_attn_noalloc.restype = ctypes.c_int
+    L.sv_verify_attn_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P]
     L.sv_verify_attn_fp8.restype = ctypes.c_int
     L.sv_verify_attn_fp8.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P, sz, P, P]
     L.sv_lmhead_workspace.restype = sz
@@ -184,6 +188,13 @@ def sv_verify_attn(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_len,
                                _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(workspace), ws_bytes,
                                _ptr(dev_status), _stream(stream))
     _check("sv_verify_attn", rc)
+
+
+def sv_verify_attn_noalloc(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_len, out, dev_status=None,
+                           stream=None) -> None:
+    rc = load().sv_verify_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(dev_status), _stream(stream))
+    _check("sv_verify_attn_noalloc", rc)
 
 
 def sv_verify_attn_fp8(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_len, out,

@@ -50,6 +50,7 @@ extern "C" const char* sv_status_string(int status) {
     case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace missing or too small";
     case SV_ERR_LAUNCH: return "SV_ERR_LAUNCH: kernel launch failed";
     case SV_ERR_DEVICE: return "SV_ERR_DEVICE: no gfx950 device is current";
+    case SV_ERR_SCRATCH: return "SV_ERR_SCRATCH: the call needs more than the library's static scratch";
     default: return "unknown sv_status";
   }
 }

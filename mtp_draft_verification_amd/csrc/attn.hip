@@ -19,6 +19,8 @@
 #include "sv_device.h"
 #include "sv_host.h"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace sv {
@@ -1192,13 +1194,18 @@ struct AttnPlan {
   int M, slots;
 };
 
-static AttnPlan attn_plan(const sv_attn_desc& d) {
+// Workspace layout.  The attention cuts the keys into at most max(nwg, B * Hkv)
+// pieces (nwg = the device's compute units), each with one partial slot; the
+// public size query allows nwg up to kAttnNwgMax so that it does not depend on the
+// device, the static scratch of sv_verify_attn_noalloc is laid out for the
+// current device's nwg.
+static AttnPlan attn_plan(const sv_attn_desc& d, int nwg_max = kAttnNwgMax) {
   AttnPlan pl{};
   const size_t elt = d.dtype == SV_BF16 ? 2 : 4;
   pl.M = (d.n_heads_q / d.n_heads_kv) * d.n_q;
   pl.q_rot_bytes = align_up((size_t)d.batch * d.n_q * d.n_heads_q * d.head_dim * elt, 256);
   if (d.dtype == SV_BF16) {
-    pl.slots = kAttnNwgMax + d.batch * d.n_heads_kv;
+    pl.slots = nwg_max + d.batch * d.n_heads_kv;
     pl.acc_bytes = align_up((size_t)pl.slots * pl.M * d.head_dim * 4, 256);
     pl.ml_bytes = align_up((size_t)pl.slots * pl.M * 2 * 4, 256);
     pl.cnt_bytes = align_up((size_t)d.batch * d.n_heads_kv * 4, 256);
@@ -1285,7 +1292,7 @@ extern "C" size_t sv_verify_attn_workspace(const sv_attn_desc* d) {
 static int verify_attn(const sv_attn_desc* d, const void* q, const void* k_new, const void* v_new, void* k_cache,
                        void* v_cache, const float* k_scale, const float* v_scale, bool fp8,
                        const int32_t* cache_len, void* out, void* workspace, size_t workspace_bytes,
-                       int32_t* dev_status, void* stream) {
+                       int32_t* dev_status, void* stream, int nwg_max = kAttnNwgMax) {
   int rc = validate_attn(d);
   if (rc != SV_OK) return rc;
   if (fp8) {
@@ -1299,10 +1306,11 @@ static int verify_attn(const sv_attn_desc* d, const void* q, const void* k_new, 
   if (d->k_is_v && (v_cache || v_new)) return SV_ERR_ARG;
   if (!d->k_is_v && !v_cache) return SV_ERR_ARG;
   if (!d->k_is_v && d->append && !v_new) return SV_ERR_ARG;
-  const AttnPlan pl = attn_plan(*d);
+  const AttnPlan pl = attn_plan(*d, nwg_max);
   if (!workspace || workspace_bytes < pl.total) return SV_ERR_WORKSPACE;
   rc = check_device();
   if (rc != SV_OK) return rc;
+  if (device_cus() > nwg_max) return SV_ERR_UNSUPPORTED;  // more pieces than partial slots
 
   AttnParams p{};
   p.q = q;
@@ -1379,4 +1387,59 @@ extern "C" int sv_verify_attn_fp8(const sv_attn_desc* d, const void* q, const vo
                                   int32_t* dev_status, void* stream) {
   return verify_attn(d, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, true, cache_len, out, workspace,
                      workspace_bytes, dev_status, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The variant that allocates nothing: the workspace is a static device array.
+// ---------------------------------------------------------------------------
+// One copy per GPU, held from the library's first use on that GPU until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels get the address that hipGetSymbolAddress returns for
+// the current device (kept per device in g_scratch).
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<char*> g_scratch[kScratchDevices];
+
+// The current device's copy of `scratch` (nullptr if the runtime cannot give it).
+char* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  char* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptr = (char*)a;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+}  // namespace
+
+extern "C" int sv_verify_attn_noalloc(const sv_attn_desc* d, const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* cache_len, void* out,
+                                      int32_t* dev_status, void* stream) {
+  int rc = validate_attn(d);
+  if (rc != SV_OK) return rc;
+  rc = check_device();  // (also caches the compute-unit count the layout uses)
+  if (rc != SV_OK) return rc;
+  const int nwg = device_cus();
+  if (attn_plan(*d, nwg).total > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  char* ws = device_scratch();
+  if (!ws) return SV_ERR_DEVICE;
+  // every call sets what the kernels need at a known value itself (arrival
+  // counters, work split), so nothing left by an earlier call is read
+  return verify_attn(d, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr, false, cache_len, out, ws,
+                     (size_t)SV_NOALLOC_SCRATCH_BYTES, dev_status, stream, nwg);
 }
