@@ -97,6 +97,13 @@ typedef struct {
   int64_t q_row_stride;  /* elements between query rows (b, j) and (b, j+1); 0 = Hq*D */
   int64_t kv_row_stride; /* same for k_new / v_new; 0 = Hkv*D.  Lets q, k_new, v_new be
                             column slices of one fused projection output */
+  int32_t act_f32;       /* 0: as above.  1 (dtype SV_BF16): fp32 activations -- q, k_new and
+                            v_new are fp32 (or, with in_splits, their fp32 slice sums are used
+                            without the bf16 rounding), so q and the new keys are rotated from
+                            their fp32 values and k, v are rounded to the cache type only when
+                            stored; out [B, n_q, Hq, D] is written in fp32.  The caches and
+                            the rotated queries the products read stay bf16 */
+  int32_t reserved_i;    /* must be 0 */
 } sv_attn_desc;
 
 /* Bytes of workspace sv_verify_attn needs for this descriptor (0 on an invalid
@@ -442,6 +449,13 @@ typedef struct {
   int32_t out_features;  /* N, a multiple of 64 */
   sv_dtype dtype;        /* of x and w (and y for SV_EPI_STORE) */
   sv_epilogue epilogue;
+  int32_t act_f32;       /* 0: as above.  1 (dtype SV_BF16, weights bf16): the activations
+                            are fp32 -- x [R, K] is fp32 (16-byte aligned rows) and each value
+                            enters the bf16 product as hi = bf16(x) plus lo = bf16(x - hi)
+                            (two MFMAs; the product is x W^T up to 2^-17 |x| per element);
+                            SV_EPI_STORE writes y in fp32, SV_EPI_GEGLU writes
+                            gelu_tanh(g) * u in fp32 from the fp32 g and u (no bf16
+                            rounding); ADD_F32 and SPLIT_F32 are unchanged */
 } sv_linear_desc;
 
 /* S of SV_EPI_SPLIT_F32 for this shape on the current device (1 <= S <= the

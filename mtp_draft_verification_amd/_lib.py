@@ -42,7 +42,8 @@ class AttnDesc(ctypes.Structure):
                 ("q_pos_offset", ctypes.c_int32), ("dtype", ctypes.c_int32), ("in_splits", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
                 ("reserved_f", ctypes.c_float), ("cache_capacity", ctypes.c_int64),
-                ("q_row_stride", ctypes.c_int64), ("kv_row_stride", ctypes.c_int64)]
+                ("q_row_stride", ctypes.c_int64), ("kv_row_stride", ctypes.c_int64),
+                ("act_f32", ctypes.c_int32), ("reserved_i", ctypes.c_int32)]
 
 
 class LMHeadDesc(ctypes.Structure):
@@ -58,7 +59,8 @@ class AcceptDesc(ctypes.Structure):
 
 class LinearDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("in_features", ctypes.c_int32),
-                ("out_features", ctypes.c_int32), ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32)]
+                ("out_features", ctypes.c_int32), ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32),
+                ("act_f32", ctypes.c_int32)]
 
 
 class ClusterDesc(ctypes.Structure):

@@ -39,6 +39,8 @@ struct AttnParams {
   int32_t* seg_cnt;       // workspace: [B * Hkv] arrivals of a segment's pieces
   int32_t* plan;          // workspace: the work split {chunk, pieces}, set by rope_append
   int in_splits;          // > 0: q, k_new, v_new are fp32 K-split partial products
+  int act_f32;            // fp32 activations: q, k_new, v_new read as fp32 (no bf16 rounding
+                          // before RoPE / the cache store), out written fp32
   int fp8;                // caches hold fp8 E4M3 codes seen through per-channel scales
   const float* k_scale;   // fp8: [Hkv, D] scales of the key cache (also the values when K = V)
   const float* v_scale;   // fp8: [Hkv, D] scales of the value cache
@@ -271,20 +273,29 @@ __device__ __forceinline__ void st_elem(void* base, int64_t i, double v) {
 // An input tensor (q, k_new or v_new): values in T, or (splits > 0, bf16 only) the
 // fp32 K-split partial products of a projection, `splits` slices `slice` elements
 // apart, summed in slice order and rounded to bf16 -- the value the projection would
-// have stored.
+// have stored.  With f32 (fp32 activations) the values are fp32 (the split sum is
+// used as it is).
 struct InView {
   const void* base;
   int64_t slice;
   int splits;
+  int f32;
 };
 
 template <typename T>
 __device__ __forceinline__ double ld_in(const InView& v, int64_t i) {
-  if (v.splits == 0) return ld_elem<T>(v.base, i);
+  if (v.splits == 0) return v.f32 ? ld_elem<float>(v.base, i) : ld_elem<T>(v.base, i);
   const float* f = (const float*)v.base + i;
   float a = 0.f;
   for (int s = 0; s < v.splits; ++s) a += f[(int64_t)s * v.slice];
+  if (v.f32) return (double)a;
   return (double)bf16_to_f32((uint16_t)f32_to_bf16_bits(a));
+}
+
+// four consecutive output elements (bf16, or fp32 with fp32 activations)
+__device__ __forceinline__ void st_out4(const AttnParams& p, int64_t i, float a0, float a1, float a2, float a3) {
+  if (p.act_f32) *(f32x4_t*)((float*)p.out + i) = f32x4_t{a0, a1, a2, a3};
+  else *(uint2*)((uint16_t*)p.out + i) = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
 }
 
 // rotate-half RoPE of element d of a head vector x (pre-rotation values) at position pos
@@ -362,7 +373,11 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
     if (hs < p.Hq && d < p.D && seq_ok(p, p.cache_len[b])) {
       int64_t lo, len;
       seq_range(p, b, lo, len);
-      if (len == 0) ((uint16_t*)p.out)[(((int64_t)b * p.nq + j) * p.Hq + hs) * p.D + d] = 0;
+      if (len == 0) {
+        const int64_t oi = (((int64_t)b * p.nq + j) * p.Hq + hs) * p.D + d;
+        if (p.act_f32) ((float*)p.out)[oi] = 0.f;
+        else ((uint16_t*)p.out)[oi] = 0;
+      }
     }
   }
   const int64_t L = p.cache_len[b];
@@ -376,13 +391,13 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
   if (hs < p.Hq) {
     const int64_t src = ((int64_t)b * p.nq + j) * p.q_stride + (int64_t)hs * D;
     const int64_t dst = (((int64_t)b * p.nq + j) * p.Hq + hs) * D;
-    const InView qv{p.q, (int64_t)p.B * p.nq * p.q_stride, p.in_splits};
+    const InView qv{p.q, (int64_t)p.B * p.nq * p.q_stride, p.in_splits, p.act_f32};
     st_elem<T>(p.q_rot, dst + d, rope_elem<T>(qv, src, d, p.rope_dims, p.log2_base, pos));
   } else if (hs < p.Hq + p.Hkv) {
     const int h = hs - p.Hq;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-    const InView kv{p.k_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits};
+    const InView kv{p.k_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits, p.act_f32};
     const double kr = rope_elem<T>(kv, src, d, p.rope_dims, p.log2_base, pos);
     if constexpr (sizeof(T) == 2) st_cache(p, p.k_cache, p.k_scale, dst + d, h * D + d, kr);
     else st_elem<T>(p.k_cache, dst + d, kr);
@@ -390,7 +405,7 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
     const int h = hs - p.Hq - p.Hkv;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-    const InView vv{p.v_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits};
+    const InView vv{p.v_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits, p.act_f32};
     if constexpr (sizeof(T) == 2) st_cache(p, p.v_cache, p.v_scale, dst + d, h * D + d, ld_in<T>(vv, src + d));
     else st_elem<T>(p.v_cache, dst + d, ld_in<T>(vv, src + d));
   }
@@ -1043,9 +1058,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           const int r = rr[it];
           const float inv = l[it] > 0.f ? 1.f / l[it] : 0.f;
           const int j = r / G, hg = r - (r / G) * G;
-          uint16_t* out = (uint16_t*)p.out + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + dd[it];
-          *(uint2*)out = make_uint2(pack_bf16x2(acc[it][0] * inv, acc[it][1] * inv),
-                                    pack_bf16x2(acc[it][2] * inv, acc[it][3] * inv));
+          st_out4(p, (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D + dd[it], acc[it][0] * inv,
+                  acc[it][1] * inv, acc[it][2] * inv, acc[it][3] * inv);
         }
       }
       };
@@ -1140,11 +1154,11 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
   const int64_t w0 = first, w1 = (int64_t)first + nb - 1;
   const int D = p.D, G = p.G;
   const int j = r / G, hg = r % G;
-  uint16_t* out = (uint16_t*)p.out + (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D;
+  const int64_t out0 = (((int64_t)b * p.nq + j) * p.Hq + kvh * G + hg) * D;
   const int d0 = threadIdx.x * 4;
   if (d0 >= D) return;
   if (len == 0) {
-    *(uint2*)(out + d0) = make_uint2(0, 0);
+    st_out4(p, out0 + d0, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   // one pass over the pieces in batches of PB, all of a batch's loads in flight:
@@ -1181,7 +1195,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p) {
   }
   const float a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  *(uint2*)(out + d0) = make_uint2(pack_bf16x2(a0 * inv, a1 * inv), pack_bf16x2(a2 * inv, a3 * inv));
+  st_out4(p, out0 + d0, a0 * inv, a1 * inv, a2 * inv, a3 * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1224,7 +1238,9 @@ static int validate_attn(const sv_attn_desc* d) {
   if (d->k_is_v != 0 && d->k_is_v != 1) return SV_ERR_ARG;
   if (d->append != 0 && d->append != 1) return SV_ERR_ARG;
   if (d->append && d->q_pos_offset != 0) return SV_ERR_ARG;
-  if (d->in_splits < 0 || d->reserved_f != 0.f) return SV_ERR_ARG;
+  if (d->in_splits < 0 || d->reserved_f != 0.f || d->reserved_i != 0) return SV_ERR_ARG;
+  if (d->act_f32 != 0 && d->act_f32 != 1) return SV_ERR_ARG;
+  if (d->act_f32 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->in_splits > 0 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->cache_capacity <= 0) return SV_ERR_ARG;
   if (d->q_row_stride < 0 || d->kv_row_stride < 0) return SV_ERR_ARG;
@@ -1350,6 +1366,7 @@ static int verify_attn(const sv_attn_desc* d, const void* q, const void* k_new, 
   p.nwg = device_cus();
   p.min_chunk = 64;
   p.in_splits = d->in_splits;
+  p.act_f32 = d->act_f32;
   p.fp8 = fp8 ? 1 : 0;
   p.k_scale = k_scale;
   p.v_scale = d->k_is_v ? k_scale : v_scale;

@@ -18,7 +18,7 @@
 namespace sv {
 
 enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_GEGLU = 5,
-                      GM_SPLIT = 6, GM_SAMPLE_RS = 7 };
+                      GM_SPLIT = 6, GM_SAMPLE_RS = 7, GM_STORE_F32 = 8 };
 
 struct SelPart {   // per (workgroup, row) partial of the select epilogue
   float t1v, t2v;  // top-2 logits (RESIDUAL: residual-draw scores)
@@ -35,7 +35,8 @@ constexpr bool select_mode(int m) { return m <= GM_RESIDUAL || m == GM_SAMPLE_RS
 constexpr int kRsCand = 4;  // first-pass candidates per draft row (single-pass sampling)
 
 struct GemmParams {
-  const uint16_t* x;     // [R, K] rows (RESIDUAL: the hidden states, gathered per slot)
+  const void* x;         // [R, K] rows, bf16 (fp32 when the kernel's XF is set; RESIDUAL:
+                         // the hidden states, gathered per slot)
   const uint16_t* w;     // [N, K]
   int R, K, N;
   int nblk, kch;         // feature blocks, 64-wide K chunks
@@ -342,11 +343,14 @@ __device__ __forceinline__ RowState from_part(const SelPart& p) {
 // spans several workgroups leaves one fp32 partial per workgroup; per wave slice
 // an arrival counter picks the last arriver, which adds the partials in
 // workgroup order (deterministic) and runs the epilogue.
-template <int MT, int T>
+// With XF (fp32 activations) a chunk of x is 16 MT rows x 256 B, staged as two
+// halves of 32 dims (one per k-step), each laid out like a bf16 chunk: 128 B per
+// row, 16-byte slots swizzled by row.
+template <int MT, int T, int XF = 0>
 struct RingCfg {
   static constexpr int NB = 64 * T;            // output features per block
   static constexpr int WI = 2 * T;             // W DMA instructions per wave per chunk
-  static constexpr int XI = 2 * MT;            // x DMA instructions per chunk (workgroup)
+  static constexpr int XI = 2 * MT * (XF ? 2 : 1);  // x DMA instructions per chunk (workgroup)
   static constexpr int NX = (XI + 3) / 4;      // x DMA instructions per wave
   static constexpr int NI = WI + NX;           // DMA instructions per wave per chunk
   static constexpr int WSTAGE = NB * 128;
@@ -370,9 +374,9 @@ __device__ __forceinline__ int logical_wg(int b, int P) {
 }
 
 
-template <int MT, int T, int MODE>
+template <int MT, int T, int MODE, int XF = 0>
 __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
-  using C = RingCfg<MT, T>;
+  using C = RingCfg<MT, T, XF>;
   constexpr bool SELECT = select_mode(MODE);
   constexpr int NB = C::NB, NS = C::NS, WROWS = 16 * T;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGEB];
@@ -396,12 +400,15 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
   uint32_t woff[C::WI];
 #pragma unroll
   for (int i = 0; i < C::WI; ++i) woff[i] = (uint32_t)((i * 8 + dl8) * K * 2 + cq[i & 1] * 16);
-  uint32_t xoff[C::NX], xlds[C::NX];
-  int xpar[C::NX];
+  uint32_t xoff[C::NX], xlds[C::NX], xadj[C::NX];
 #pragma unroll
   for (int ii = 0; ii < C::NX; ++ii) {
     const int j = (wave + 4 * ii) < C::XI ? (wave + 4 * ii) : C::XI - 1;
-    const int r = j * 8 + dl8;
+    // XF: instruction j moves half j / (2 MT) (dims 32h..32h+31 of the chunk) of the
+    // rows of 8-row block j % (2 MT)
+    const int half = XF ? j / (2 * MT) : 0;
+    const int jb = XF ? j % (2 * MT) : j;
+    const int r = jb * 8 + dl8;
     int xr = 0;
     if (r < nx) {
       if constexpr (MODE == GM_RESIDUAL) {
@@ -411,8 +418,13 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
         xr = r;
       }
     }
-    xpar[ii] = j & 1;
-    xoff[ii] = (uint32_t)(xr * K * 2 + cq[j & 1] * 16);
+    if constexpr (XF) {
+      xoff[ii] = (uint32_t)(xr * K * 4 + half * 128 + cq[jb & 1] * 16);
+      xadj[ii] = half ? 128u : 0u;  // a 32-dim last chunk has no second half: re-read the first
+    } else {
+      xoff[ii] = (uint32_t)(xr * K * 2 + cq[jb & 1] * 16);
+      xadj[ii] = adj[jb & 1];
+    }
     xlds[ii] = (uint32_t)(C::WSTAGE + j * 1024);
   }
 
@@ -438,9 +450,9 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < C::WI; ++i)
       dma16(wb, woff[i] - (tail ? adj[i & 1] : 0u), dst + (uint32_t)((wave * C::WI + i) * 1024));
-    const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * 128;
+    const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * (XF ? 256 : 128);
 #pragma unroll
-    for (int ii = 0; ii < C::NX; ++ii) dma16(xb, xoff[ii] - (tail ? adj[xpar[ii]] : 0u), dst + xlds[ii]);
+    for (int ii = 0; ii < C::NX; ++ii) dma16(xb, xoff[ii] - (tail ? xadj[ii] : 0u), dst + xlds[ii]);
   };
 
   // ---- stream-K bookkeeping ----
@@ -558,15 +570,26 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
           select_push4<MODE>(st[mt], ctx[mt], z, v0);
         } else if constexpr (MODE == GM_GEGLU) {
           // tile 0 holds the gate, tile 1 the up projection of the same 16 features
-          // (weights interleaved by 16 rows); both pass through bf16 as stored values
+          // (weights interleaved by 16 rows).  bf16 activations: both pass through bf16
+          // as stored values and the product is stored bf16; fp32 activations (XF): the
+          // product of the fp32 gate and up values is stored fp32
           if (t == 1 && r < nx) {
-            float f[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              f[e] = gelu_tanh(round_bf16(acc[0][mt][e])) * round_bf16(acc[1][mt][e]);
             const int c0 = row0 / 2 + lg * 4;
-            *(uint2*)((uint16_t*)p.y + (int64_t)r * (p.N / 2) + c0) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+            if constexpr (XF) {
+              f32x4_t f;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) f[e] = gelu_tanh(acc[0][mt][e]) * acc[1][mt][e];
+              *(f32x4_t*)((float*)p.y + (int64_t)r * (p.N / 2) + c0) = f;
+            } else {
+              float f[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                f[e] = gelu_tanh(round_bf16(acc[0][mt][e])) * round_bf16(acc[1][mt][e]);
+              *(uint2*)((uint16_t*)p.y + (int64_t)r * (p.N / 2) + c0) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+            }
           }
+        } else if constexpr (MODE == GM_STORE_F32) {
+          if (r < nx) *(f32x4_t*)((float*)p.y + (int64_t)r * p.N + v0) = acc[t][mt];
         } else if constexpr (MODE == GM_STORE_BF16) {
           if (r < nx)
             *(uint2*)((uint16_t*)p.y + (int64_t)r * p.N + v0) = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
@@ -609,15 +632,43 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
     const uint8_t* xs = xrd + s * C::STAGEB;
     for (int js = 0; js < nks; ++js) {
       const int so = ((js * 4 + lg) ^ fsw) << 4;
-      V16 a[T], bx[MT];
+      V16 a[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) a[t].u = *(const uint4*)(ws + t * 2048 + so);
+      if constexpr (XF) {
+        // the lane's 8 fp32 dims (32 B: slots 2 lg and 2 lg + 1 of half js) enter the
+        // product as hi = bf16(x) and lo = bf16(x - hi): x W^T = hi W^T + lo W^T up to
+        // 2^-17 |x| per element
+        const uint8_t* xh = xs + js * (MT * 2048);
+        V16 bh[MT], bl[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) bx[mt].u = *(const uint4*)(xs + mt * 2048 + so);
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4_t v0 = *(const f32x4_t*)(xh + mt * 2048 + (((2 * lg) ^ fsw) << 4));
+          const f32x4_t v1 = *(const f32x4_t*)(xh + mt * 2048 + (((2 * lg + 1) ^ fsw) << 4));
+          const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-      for (int t = 0; t < T; ++t)
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+            bh[mt].w[e] = h;
+            bl[mt].w[e] = pack_bf16x2(v[2 * e] - bf16_lo(h), v[2 * e + 1] - bf16_hi(h));
+          }
+        }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a[t].b, bx[mt].b, acc[t][mt]);
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            acc[t][mt] = mfma16x16x32(a[t].b, bh[mt].b, acc[t][mt]);
+            acc[t][mt] = mfma16x16x32(a[t].b, bl[mt].b, acc[t][mt]);
+          }
+      } else {
+        V16 bx[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) bx[mt].u = *(const uint4*)(xs + mt * 2048 + so);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a[t].b, bx[mt].b, acc[t][mt]);
+      }
     }
     s = s + 1 == NS ? 0 : s + 1;
     if (ckc == KCH - 1 || it == n_it - 1) {
@@ -1231,18 +1282,18 @@ static int validate_lmhead(const sv_lmhead_desc* d) {
   return SV_OK;
 }
 
-template <int MT, int T, int MODE>
+template <int MT, int T, int MODE, int XF>
 static void launch_ring(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_ring_kernel<MT, T, MODE>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_ring_kernel<MT, T, MODE, XF>), dim3(grid), dim3(256), 0, s, p);
 }
 
-template <int T, int MODE>
+template <int T, int MODE, int XF = 0>
 static int dispatch_ring(const GemmParams& p, int nx, int grid, hipStream_t s) {
   switch ((nx + 15) / 16) {
-    case 1: launch_ring<1, T, MODE>(p, grid, s); break;
-    case 2: launch_ring<2, T, MODE>(p, grid, s); break;
-    case 3: launch_ring<3, T, MODE>(p, grid, s); break;
-    case 4: launch_ring<4, T, MODE>(p, grid, s); break;
+    case 1: launch_ring<1, T, MODE, XF>(p, grid, s); break;
+    case 2: launch_ring<2, T, MODE, XF>(p, grid, s); break;
+    case 3: launch_ring<3, T, MODE, XF>(p, grid, s); break;
+    case 4: launch_ring<4, T, MODE, XF>(p, grid, s); break;
     default: return SV_ERR_UNSUPPORTED;
   }
   return SV_OK;
@@ -1255,6 +1306,8 @@ static int validate_linear(const sv_linear_desc* d) {
       d->epilogue != SV_EPI_SPLIT_F32)
     return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_SPLIT_F32 && d->dtype != SV_BF16) return SV_ERR_ARG;
+  if (d->act_f32 != 0 && d->act_f32 != 1) return SV_ERR_ARG;
+  if (d->act_f32 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->out_features % 64) return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_GEGLU && (d->dtype != SV_BF16 || d->out_features % 128)) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
@@ -1546,7 +1599,7 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
     if (p.splits == 0) return SV_ERR_UNSUPPORTED;
     pl.grid = pl.nblk * p.splits;
   }
-  p.x = (const uint16_t*)x;
+  p.x = x;
   p.w = (const uint16_t*)w;
   p.R = d->rows;
   p.K = d->in_features;
@@ -1556,6 +1609,22 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   p.y = y;
   p.cnt = (int32_t*)workspace;
   p.part = (float*)((char*)workspace + pl.cnt_bytes);
+  if (d->act_f32) {
+    // fp32 activations: x read as fp32 (hi + lo bf16 operands); STORE and GEGLU write fp32
+    if (d->epilogue == SV_EPI_GEGLU)
+      rc = dispatch_ring<2, GM_GEGLU, 1>(p, d->rows, pl.grid, s);
+    else if (d->epilogue == SV_EPI_SPLIT_F32)
+      rc = pl.T == 1 ? dispatch_ring<1, GM_SPLIT, 1>(p, d->rows, pl.grid, s)
+                     : dispatch_ring<2, GM_SPLIT, 1>(p, d->rows, pl.grid, s);
+    else if (pl.T == 1)
+      rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<1, GM_STORE_F32, 1>(p, d->rows, pl.grid, s)
+                                       : dispatch_ring<1, GM_ADD_F32, 1>(p, d->rows, pl.grid, s);
+    else
+      rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<2, GM_STORE_F32, 1>(p, d->rows, pl.grid, s)
+                                       : dispatch_ring<2, GM_ADD_F32, 1>(p, d->rows, pl.grid, s);
+    if (rc != SV_OK) return rc;
+    return launch_status();
+  }
   if (d->epilogue == SV_EPI_GEGLU)
     rc = dispatch_ring<2, GM_GEGLU>(p, d->rows, pl.grid, s);
   else if (d->epilogue == SV_EPI_SPLIT_F32)

@@ -6,7 +6,7 @@ then accept_longest_prefix.  Here that forward is, per layer,
 
     a = rmsnorm(x)                 sv_rmsnorm      (x: fp32 residual stream)
     qkv = a Wqkv^T                 sv_linear       (q, k, v in one projection; K-split
-                                   partials, summed and rounded by the attention call)
+                                   partials, summed by the attention call)
     o = attn(q, k, v; cache)       sv_verify_attn  (appends the k+1 new rows)
     x += o Wo^T                    sv_linear (SV_EPI_SPLIT_F32: the K-split partial
                                    products), added into x by the next norm
@@ -19,6 +19,13 @@ then accept_longest_prefix.  Here that forward is, per layer,
 
 then h = rmsnorm(x), sv_lmhead_select over the tied embedding and sv_accept.  The
 fp32 stack (no norms) adds into x with SV_EPI_ADD_F32 instead.
+
+In the bf16 stack the weights and the caches are bf16 and the activations between
+the calls are fp32 (act_f32): the norm outputs, q / k / v (their K-split sums),
+the attention output and the GeGLU output.  Each projection takes its fp32 input as
+a hi + lo pair of bf16 MFMA operands; only the new cache rows and the final hidden
+state that the LM head reads are rounded to bf16.
+
 Every call is enqueued on one stream with no host synchronisation; all buffers
 are allocated once up front, so a step allocates nothing.  This module only
 marshals arguments: the arithmetic is the library's.
@@ -34,14 +41,14 @@ from . import _lib as L
 
 def attn_desc(layer, batch: int, n_q: int, cap: int, dtype: str, append: bool = True,
               q_pos_offset: int = 0, q_row_stride: int = 0, kv_row_stride: int = 0,
-              in_splits: int = 0) -> L.AttnDesc:
+              in_splits: int = 0, act_f32: bool = False) -> L.AttnDesc:
     return L.AttnDesc(batch=batch, n_q=n_q, n_heads_q=layer.n_heads_q, n_heads_kv=layer.n_heads_kv,
                       head_dim=layer.head_dim, window=layer.window, rope_dims=layer.rope_dims,
                       k_is_v=int(layer.k_is_v), append=int(append), q_pos_offset=q_pos_offset,
                       dtype=L.SV_BF16 if dtype == "bf16" else L.SV_F32, in_splits=int(in_splits),
                       rope_base=float(layer.rope_base), softmax_scale=float(layer.scale), reserved_f=0.0,
                       cache_capacity=int(cap), q_row_stride=int(q_row_stride),
-                      kv_row_stride=int(kv_row_stride))
+                      kv_row_stride=int(kv_row_stride), act_f32=int(bool(act_f32)), reserved_i=0)
 
 
 def interleave_gate_up(wgu: torch.Tensor) -> torch.Tensor:
@@ -64,9 +71,10 @@ class VerifyStack:
         self.dev = torch.device(device)
         self.bf16 = cfg.dtype == "bf16"
         self.dt = L.SV_BF16 if self.bf16 else L.SV_F32
-        tdt = torch.bfloat16 if self.bf16 else torch.float32
+        self.act = int(self.bf16)  # bf16 weights and caches, fp32 activations
         if not cfg.norm and self.bf16:
-            raise ValueError("a bf16 stack needs the RMSNorm to produce its bf16 activations")
+            raise ValueError("a bf16 stack needs its final RMSNorm to produce the bf16 hidden state "
+                             "the LM head reads")
         B, k, d = cfg.batch, cfg.k, cfg.d_model
         self.R = R = B * (k + 1)
         self.cap = caches[0]["k"].shape[2]
@@ -75,8 +83,8 @@ class VerifyStack:
         self.wgu_il = ([interleave_gate_up(lw["wgu"]) for lw in weights["layers"]]
                        if self.fused_geglu else None)
         dev = self.dev
-        z = lambda *s, dtype=tdt: torch.zeros(*s, dtype=dtype, device=dev)
-        self.x = z(R, d, dtype=torch.float32)
+        z = lambda *s, dtype=torch.float32: torch.zeros(*s, dtype=dtype, device=dev)
+        self.x = z(R, d)
         self.a = z(R, d)
         nout = max(ly.n_heads_q * ly.head_dim + (1 if ly.k_is_v else 2) * ly.n_heads_kv * ly.head_dim
                    for ly in cfg.layers)
@@ -84,7 +92,8 @@ class VerifyStack:
         self.o = z(R, max(ly.n_heads_q * ly.head_dim for ly in cfg.layers))
         self.gu = z(R, 2 * cfg.d_ff) if cfg.d_ff and not self.fused_geglu else None
         self.f = z(R, cfg.d_ff) if cfg.d_ff else None
-        self.h = self.a  # final norm output reuses the activation buffer
+        # the final hidden state, in the LM head's dtype
+        self.h = z(R, d, dtype=torch.bfloat16) if self.bf16 else self.a
         # residual projections leave K-split partials that the next norm adds into x
         self.split = {}
         if self.bf16:
@@ -92,7 +101,7 @@ class VerifyStack:
                 for K in (ly.n_heads_q * ly.head_dim, cfg.d_ff):
                     if K:
                         S = L.sv_linear_splits(L.LinearDesc(rows=R, in_features=K, out_features=d, dtype=self.dt,
-                                                            epilogue=L.SV_EPI_SPLIT_F32))
+                                                            epilogue=L.SV_EPI_SPLIT_F32, act_f32=self.act))
                         if S > 0:
                             self.split[K] = S
         self.parts = z(max(self.split.values()) * R * d, dtype=torch.float32) if self.split else None
@@ -102,7 +111,8 @@ class VerifyStack:
             S = 0
             if self.bf16:
                 S = max(0, L.sv_linear_splits(L.LinearDesc(rows=R, in_features=d, out_features=self._nout(ly),
-                                                           dtype=self.dt, epilogue=L.SV_EPI_SPLIT_F32)))
+                                                           dtype=self.dt, epilogue=L.SV_EPI_SPLIT_F32,
+                                                           act_f32=self.act)))
             self.qkv_split.append(S)
         nout_max = max(self._nout(ly) for ly in cfg.layers)
         self.qkv_parts = (z(max(self.qkv_split) * R * nout_max, dtype=torch.float32) if max(self.qkv_split) else None)
@@ -121,7 +131,7 @@ class VerifyStack:
         self.timers = None   # {call name: [(start event, end event), ...]} when timing
         self.attn_descs = [
             attn_desc(ly, B, k + 1, self.cap, cfg.dtype, q_row_stride=self._nout(ly), kv_row_stride=self._nout(ly),
-                      in_splits=S) for ly, S in zip(cfg.layers, self.qkv_split)]
+                      in_splits=S, act_f32=self.act) for ly, S in zip(cfg.layers, self.qkv_split)]
 
     def _ev(self, name: str, stream):
         """Record a HIP event pair around a named call when that call is being timed."""
@@ -154,12 +164,12 @@ class VerifyStack:
 
     def _lin_ws(self, R, K, N, epi) -> int:
         return L.sv_linear_workspace(L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt,
-                                                  epilogue=epi))
+                                                  epilogue=epi, act_f32=self.act))
 
     def _linear(self, x, w, y, epi, stream):
         R, K = self.R, w.shape[1]
         N = w.shape[0]
-        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi)
+        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi, act_f32=self.act)
         L.sv_linear(desc, x, w, y, self.lin_ws, stream)
 
     def _residual(self, inp, w, stream):
@@ -175,11 +185,11 @@ class VerifyStack:
 
     def _norm(self, x, y, stream, pending=None):
         if self.cfg.norm:
+            odt = L.SV_BF16 if y.dtype == torch.bfloat16 else L.SV_F32
             if pending is not None:
-                L.sv_add_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, pending[0], pending[1], None, y, self.dt,
-                                 stream)
+                L.sv_add_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, pending[0], pending[1], None, y, odt, stream)
             else:
-                L.sv_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, None, y, self.dt, stream)
+                L.sv_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, None, y, odt, stream)
             return y
         assert pending is None
         return x  # fp32 stack without norms feeds the residual stream directly
@@ -234,7 +244,7 @@ class VerifyStack:
                     self._linear(m, lw["wgu"], self.gu, L.SV_EPI_STORE, stream)
                     self._end(t)
                     t = self._ev(f"L{i}.geglu", stream)
-                    L.sv_geglu(self.R, cfg.d_ff, self.dt, self.gu, self.f, stream)
+                    L.sv_geglu(self.R, cfg.d_ff, L.SV_F32, self.gu, self.f, stream)
                     self._end(t)
                 t = self._ev(f"L{i}.down", stream)
                 pending = self._residual(self.f, lw["wd"], stream)

@@ -15,10 +15,11 @@ of a pre-norm decoder layer and of the speculative step:
       m = norm(x); x += (gelu_tanh(m Wg) * (m Wu)) Wd;  final h = norm(x);
       logits = h E^T with the embedding E tied to the LM head, x0 = sqrt(d) E[tok].
 
-Values the GPU path stores are rounded to its storage type here at the same
-points (bf16 in bf16 mode, fp32 in fp32 mode: cache rows, q/k/v, attention
-output, normed activations, gate/up/GeGLU outputs, final hidden); all
-arithmetic stays fp64 and the residual stream is never rounded.
+Values the GPU path stores are rounded here at the same points: activations
+between the ops (normed inputs, q/k/v, attention output, GeGLU output) are
+stored in fp32; in bf16 mode the appended cache rows and the final hidden state
+(the LM head's input) are stored in bf16, in fp32 mode in fp32.  All arithmetic
+stays fp64 and the residual stream is never rounded.
 """
 from __future__ import annotations
 
@@ -47,11 +48,15 @@ class OracleModel:
         self.W = weights
         self.bf16 = cfg.dtype == "bf16"
 
-    def _r(self, x):
-        """Round to the storage type of the GPU path (bf16, or fp32 in fp32 mode)."""
-        if self.bf16:
-            return bf16_round(x)
+    @staticmethod
+    def _r(x):
+        """Round an activation to its storage type (fp32)."""
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+    def _rh(self, x):
+        """Round the final hidden state to the LM head's input type (bf16, or fp32 in
+        fp32 mode)."""
+        return bf16_round(x) if self.bf16 else self._r(x)
 
     def embed(self, tokens: np.ndarray) -> np.ndarray:
         E = self.W["E"]
@@ -85,11 +90,11 @@ class OracleModel:
             x = x + linear(o, lw["wo"])
             if cfg.d_ff:
                 m = self._r(rmsnorm(x, cfg.eps) if cfg.norm else x)
-                g = self._r(linear(m, lw["wgu"][:cfg.d_ff]))
-                u = self._r(linear(m, lw["wgu"][cfg.d_ff:]))
+                g = linear(m, lw["wgu"][:cfg.d_ff])
+                u = linear(m, lw["wgu"][cfg.d_ff:])
                 f = self._r(geglu(g, u))
                 x = x + linear(f, lw["wd"])
-        h = self._r(rmsnorm(x, cfg.eps) if cfg.norm else x)
+        h = self._rh(rmsnorm(x, cfg.eps) if cfg.norm else x)
         z = lmhead(h, self.W["E"])
         return h, z
 

@@ -182,6 +182,74 @@ def test_split_partial_inputs(kind):
 
 
 @gpu
+@pytest.mark.parametrize("kind", ["local", "global"])
+def test_fp32_activation_inputs(kind):
+    """act_f32: q, k_new, v_new as fp32 (K-split partials or their fp32 sum) and an
+    fp32 output.  The split and the summed forms give identical bits; the result
+    matches the oracle fed the same fp32 values (no bf16 rounding before RoPE; the
+    new rows rounded to bf16 when stored)."""
+    dev = need_gpu()
+    ly = configs.local_layer(16, 8, 256, 64) if kind == "local" else configs.global_layer(16, 4, 512)
+    B, nq, S, cap = 3, 5, 4, 700
+    Hq, Hkv, D = ly.n_heads_q, ly.n_heads_kv, ly.head_dim
+    G = Hq // Hkv
+    nout = Hq * D + (1 if ly.k_is_v else 2) * Hkv * D
+    say(f"[attn f32 inputs] {kind} S={S}")
+    parts = inputs.normal((S, B * nq, nout), 0.5, 24, "parts", dev, "f32")
+    acc = parts[0].clone()
+    for s in range(1, S):
+        acc = acc + parts[s]          # the slice sum in slice order, as the kernel forms it
+    lens = [10, 300, 640]
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    kc0 = inputs.normal((B, Hkv, cap, D), 1.0, 24, "kc", dev)
+    vc0 = None if ly.k_is_v else inputs.normal((B, Hkv, cap, D), 1.0, 24, "vc", dev)
+    outs, caches = [], []
+    for split in (False, True):
+        src = parts if split else acc
+        base = src.data_ptr()
+        kp = base + Hq * D * 4
+        vp = None if ly.k_is_v else base + (Hq + Hkv) * D * 4
+        kc = kc0.clone()
+        vc = None if vc0 is None else vc0.clone()
+        out = torch.full((B, nq, Hq, D), float("nan"), dtype=torch.float32, device=dev)
+        desc = attn_desc(ly, B, nq, cap, "bf16", q_row_stride=nout, kv_row_stride=nout,
+                         in_splits=S if split else 0, act_f32=True)
+        ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
+        L.sv_verify_attn(desc, base, kp, vp, kc, vc, lt, out, ws, None)
+        outs.append(out)
+        caches.append((kc, vc))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(caches[0][0], caches[1][0])
+    if vc0 is not None:
+        assert torch.equal(caches[0][1], caches[1][1])
+    ah = host(acc).reshape(B, nq, nout)
+    q = ah[:, :, :Hq * D].reshape(B, nq, Hq, D)
+    kn = ah[:, :, Hq * D:(Hq + Hkv) * D].reshape(B, nq, Hkv, D)
+    vn = None if ly.k_is_v else ah[:, :, (Hq + Hkv) * D:].reshape(B, nq, Hkv, D)
+    outh = host(outs[0])
+    for b in range(B):
+        got, want = [], []
+        for g in range(Hkv):
+            kcg = host(kc0[b, g])
+            vcg = None if vc0 is None else host(vc0[b, g])
+            o = oracle.attn_group(q=q[b, :, g * G:(g + 1) * G], k_new=kn[b, :, g],
+                                  v_new=None if vn is None else vn[b, :, g], k_cache=kcg, v_cache=vcg, L=lens[b],
+                                  window=ly.window, rope_dims=ly.rope_dims, rope_base=ly.rope_base, scale=ly.scale,
+                                  k_is_v=ly.k_is_v, append=True, round_bf16=True)
+            got.append(outh[b, :, g * G:(g + 1) * G])
+            want.append(o)
+            rows = host(caches[0][0][b, g, lens[b]:lens[b] + nq])
+            ref_rows = kcg[lens[b]:lens[b] + nq]
+            assert np.all(np.abs(rows - ref_rows) <= np.abs(ref_rows) * 2.0 ** -7 + 1e-30), (b, g)
+            if vcg is not None:
+                np.testing.assert_array_equal(host(caches[0][1][b, g, lens[b]:lens[b] + nq]), vcg[lens[b]:lens[b] + nq])
+        e = rel_l2(np.stack(got), np.stack(want))
+        assert e <= TOL["bf16"], (b, e)
+    say(f"[attn f32 inputs] {kind} ok")
+
+
+@gpu
 def test_read_only_drafter_queries():
     ly = configs.global_layer(16, 4, 512)
     run_case(ly, 3, 1, [50, 0, 777], 800, 5, append=False, qoff=0, tag="read-only-global")
@@ -249,11 +317,10 @@ def test_full_size_local_config():
 
 
 @gpu
-def test_full_size_global_config_sampled():
+def test_full_size_global_config():
     """Global workload at its full size (B=8, 32q/4kv, D=512, L ~ U[8192, 32768]);
-    the oracle checks three (sequence, KV head) groups in full."""
+    the oracle recomputes all 32 (sequence, KV head) groups."""
     cfg = configs.GLOBAL_ATTN
     lens = inputs.randint((cfg.batch,), cfg.ctx_lo, cfg.ctx_hi, 0, "cache_len", "cpu").tolist()
     cap = max(lens) + cfg.k + 1
-    run_case(cfg.layer, cfg.batch, cfg.k + 1, lens, cap, 0, std=cfg.std,
-             check_groups=[(0, 0), (3, 2), (7, 3)], tag="global-full")
+    run_case(cfg.layer, cfg.batch, cfg.k + 1, lens, cap, 0, std=cfg.std, tag="global-full")

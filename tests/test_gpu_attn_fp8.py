@@ -144,10 +144,10 @@ def test_fp8_read_only_drafter_queries():
 
 
 @gpu
-def test_fp8_full_size_global_config_sampled():
-    """The global workload at full size over an fp8 cache; three groups in full."""
+def test_fp8_full_size_global_config():
+    """The global workload at full size over an fp8 cache; all 32 (sequence, KV head)
+    groups recomputed by the oracle."""
     cfg = configs.GLOBAL_ATTN
     lens = inputs.randint((cfg.batch,), cfg.ctx_lo, cfg.ctx_hi, 0, "cache_len", "cpu").tolist()
     cap = max(lens) + cfg.k + 1
-    run_case(cfg.layer, cfg.batch, cfg.k + 1, lens, cap, 0, std=cfg.std,
-             check_groups=[(0, 0), (3, 2), (7, 3)], tag="global-full")
+    run_case(cfg.layer, cfg.batch, cfg.k + 1, lens, cap, 0, std=cfg.std, tag="global-full")

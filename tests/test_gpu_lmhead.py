@@ -108,11 +108,11 @@ def test_greedy_ties_lowest_id():
 
 
 @gpu
-def test_full_size_greedy_sampled_rows():
-    """262,144-entry vocabulary, d = 3840, B = 8, k = 4 (40 rows); the oracle
-    recomputes four rows in full."""
-    cfg = configs.LMHEAD_B8
-    greedy_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0, rows=[0, 4, 21, 39])
+@pytest.mark.parametrize("cfg", [configs.LMHEAD_B8, configs.LMHEAD_B1], ids=["B8", "B1"])
+def test_full_size_greedy(cfg):
+    """262,144-entry vocabulary, d = 3840, k = 4, B = 8 (40 rows) and B = 1 (5 rows):
+    every row recomputed by the oracle."""
+    greedy_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0)
 
 
 def stats_tensor(top1, dev):
@@ -231,6 +231,7 @@ def sampling_case(B, k, d, V, seed, rows_check=None, alpha=0.1, q_from_p=None):
         assert int(ga[b]["residual_row"]) == (-1 if n == k else b * (k + 1) + n)
     say(f"[lmhead sample] checked {n_checked} sequences, excused {excused}; "
         f"n = {ga['n_accepted'].tolist()}")
+    assert n_checked > 0, "every sequence was excused: nothing was checked"
     return ga
 
 
@@ -246,6 +247,12 @@ def test_sampling_small_accepts():
 
 
 @gpu
-def test_full_size_sampling_sampled_sequences():
-    cfg = configs.LMHEAD_B8
-    sampling_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0, rows_check=[0, 5])
+@pytest.mark.parametrize("cfg", [configs.LMHEAD_B8, configs.LMHEAD_B1], ids=["B8", "B1"])
+def test_full_size_sampling(cfg):
+    """Both sampling passes and the accept at full vocabulary; every sequence
+    recomputed by the oracle.  Drafter distributions Dirichlet(0.1) (B = 8) or close
+    to the target's own rows (B = 1, so its bonus path is taken too)."""
+    if cfg.batch == 1:
+        sampling_case(1, cfg.k, cfg.d_model, cfg.vocab, 3, q_from_p=0.05)
+    else:
+        sampling_case(cfg.batch, cfg.k, cfg.d_model, cfg.vocab, 0)

@@ -2,11 +2,17 @@
 the oracle, in lockstep over many steps.
 
 Drafts follow the workloads' recipe: the target's own greedy continuation
-(computed by the oracle) with each draft replaced by a uniform random token with
-probability 1 - draft_match.  Per step the GPU's row statistics must match the
-oracle's within 2e-2, and accept lengths / emitted tokens bit for bit wherever
-the oracle's deciding top-2 margin exceeds 1e-2.  Where the margin rule excuses
-a difference both sides commit the oracle's decision (lockstep)."""
+(computed by the oracle) with each draft replaced by a random token with
+probability 1 - draft_match (the continuation is computed only up to the first
+replaced draft: acceptance stops there, and later drafts are random tokens).  Per
+step the GPU's row statistics (top-1 and top-2 logits, log-sum-exp, draft logit)
+must match the oracle's within 2e-2 absolute, and accept lengths, emitted tokens,
+new lengths, keep / drop ranges and the drafter's hidden row bit for bit wherever
+the oracle's deciding top-2 margin exceeds 1e-2.  Where the margin rule excuses a
+difference both sides commit the oracle's decision (lockstep).  The worst
+differences per run are printed and asserted."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -52,26 +58,30 @@ def host_caches(caches, seqs, cfg, cap, only_window=False):
 
 
 def make_drafts(model, state, last_tokens, k, match, vocab, rng):
-    """Greedy continuation of each sequence (oracle, batch 1 per sequence) with each
-    draft replaced by a random other token with probability 1 - match."""
+    """Greedy continuation of each sequence (oracle, one row per forward) with each
+    draft kept with probability `match`.  The continuation runs only up to the first
+    replaced draft m; drafts m.. are uniform random tokens.  The forwards write cache
+    rows from L_b on through views of the state's caches; the verify step rewrites
+    those rows before it reads them, so nothing needs copying."""
     B = len(last_tokens)
-    drafts = np.zeros((B, k), dtype=np.int32)
+    drafts = rng.integers(0, vocab, (B, k)).astype(np.int32)
     for b in range(B):
-        st = {"caches": [{"k": c["k"][b:b + 1].copy(), "v": None if c["v"] is None else c["v"][b:b + 1].copy()}
+        keep = rng.random(k) < match
+        m = k if keep.all() else int(np.argmin(keep))
+        if m == 0:
+            continue
+        st = {"caches": [{"k": c["k"][b:b + 1], "v": None if c["v"] is None else c["v"][b:b + 1]}
                          for c in state["caches"]],
               "L": state["L"][b:b + 1].copy()}
-        cont = om.ar_greedy(model, st, int(last_tokens[b]), k)
-        for i in range(k):
-            if rng.random() < match:
-                drafts[b, i] = cont[i]
-            else:
-                t = int(rng.integers(0, vocab - 1))
-                drafts[b, i] = t if t < cont[i] else t + 1
+        drafts[b, :m] = om.ar_greedy(model, st, int(last_tokens[b]), m)
     return drafts
 
 
-def compare_step(vs, ref, k, B, seqs, tag):
-    """Returns the per-sequence (n, y) the step must commit (oracle's on excused rows)."""
+def compare_step(vs, ref, k, B, seqs, tag, worst=None):
+    """Returns the per-sequence (n, y) the step must commit (oracle's on excused rows).
+    `worst` (a dict) collects the largest differences of the row statistics and the
+    number of decisions checked / excused by the margin rule."""
+    worst = {} if worst is None else worst
     gs = L.decode_row_stats(vs.stats)
     ga = L.decode_accept_out(vs.acc)
     commit = []
@@ -79,37 +89,48 @@ def compare_step(vs, ref, k, B, seqs, tag):
         st = ref["stats"][bi]
         for i in range(k + 1):
             g, o = gs[b * (k + 1) + i], st[i]
-            assert abs(float(g["top1"]) - o["top1"]) <= ATOL, (tag, b, i, g, o)
-            assert abs(float(g["lse"]) - o["lse"]) <= ATOL, (tag, b, i, g, o)
-            if not np.isnan(o["draft_logit"]):
-                assert abs(float(g["draft_logit"]) - o["draft_logit"]) <= ATOL, (tag, b, i, g, o)
+            for key in ("top1", "top2", "lse") + (("draft_logit",) if not np.isnan(o["draft_logit"]) else ()):
+                e = abs(float(g[key]) - o[key])
+                worst[key] = max(worst.get(key, 0.0), e)
+                assert e <= ATOL, (tag, b, i, key, g, o)
         n = int(ref["n"][bi])
+        L0 = int(ref["old_len"][bi])
         deciding = [st[i]["top1"] - st[i]["top2"] for i in range(n + 1)]
         if min(deciding) > MARGIN:
-            assert int(ga[b]["n_accepted"]) == n, (tag, b, ga[b], n)
-            assert int(ga[b]["next_token"]) == int(ref["y"][bi]), (tag, b)
-            assert int(ga[b]["new_len"]) == int(ref["new_len"][bi])
-            assert int(ga[b]["hidden_row"]) == b * (k + 1) + n
+            a = ga[b]
+            assert int(a["n_accepted"]) == n, (tag, b, a, n)
+            assert int(a["next_token"]) == int(ref["y"][bi]), (tag, b)
+            assert int(a["new_len"]) == int(ref["new_len"][bi]) == L0 + n + 1
+            assert (int(a["keep_begin"]), int(a["keep_end"])) == (L0, L0 + n + 1), (tag, b, a)
+            assert (int(a["drop_begin"]), int(a["drop_end"])) == (L0 + n + 1, L0 + k + 1), (tag, b, a)
+            assert int(a["hidden_row"]) == b * (k + 1) + n
+            assert vs.out_tokens[b].tolist() == [int(t) for t in ref["tokens"][bi]], (tag, b)
+            worst["checked"] = worst.get("checked", 0) + 1
+        else:
+            worst["excused"] = worst.get("excused", 0) + 1
         commit.append((n, int(ref["y"][bi])))
     return commit
 
 
-def lockstep(cfg, steps, seed=0, check_drafter=False):
+def lockstep(cfg, steps, seed=0, check_drafter=False, full=False):
+    """`full`: workload sizes -- the local layers' caches hold (and the host copies)
+    only the rows their windows can reach."""
     dev = need_gpu()
     B, k = cfg.batch, cfg.k
     cap = cfg.ctx + (k + 1) * (steps + 1) + 8
     say(f"[stack] {cfg.name}: d={cfg.d_model} layers={len(cfg.layers)} V={cfg.vocab} B={B} k={k} "
         f"ctx={cfg.ctx} steps={steps} seed={seed}")
     W = inputs.stack_weights(cfg, seed, dev)
-    caches = inputs.stack_caches(cfg, seed, dev, capacity=cap)
+    caches = inputs.stack_caches(cfg, seed, dev, capacity=cap, fill_from=0 if full else None)
     model = om.OracleModel(cfg, host_weights(W, cfg.dtype == "bf16"))
-    state = om.new_state(host_caches(caches, range(B), cfg, cap), [cfg.ctx] * B)
+    state = om.new_state(host_caches(caches, range(B), cfg, cap, only_window=full), [cfg.ctx] * B)
     cl = torch.full((B,), cfg.ctx, dtype=torch.int32, device=dev)
     vs = VerifyStack(cfg, W, caches, cl, dev)
     rng = np.random.default_rng(seed)
     last = inputs.randint((B,), 0, cfg.vocab - 1, seed, "first_tokens", "cpu").numpy()
     accepted = []
     worst_h = 0.0
+    worst = {}
     for s in range(steps):
         drafts = make_drafts(model, state, last, k, cfg.draft_match, cfg.vocab, rng)
         tokens = np.concatenate([last[:, None], drafts], axis=1).astype(np.int32)
@@ -123,7 +144,7 @@ def lockstep(cfg, steps, seed=0, check_drafter=False):
         e = rel_l2(hg, ref["h"])
         worst_h = max(worst_h, e)
         assert e <= (1e-2 if cfg.dtype == "bf16" else 1e-5), f"step {s}: final hidden rel L2 {e:.2e}"
-        commit = compare_step(vs, ref, k, B, range(B), f"step {s} (final hidden rel L2 {e:.2e})")
+        commit = compare_step(vs, ref, k, B, range(B), f"step {s} (final hidden rel L2 {e:.2e})", worst)
         # lockstep: both sides continue from the oracle's decision
         new_len = np.array([old[b] + commit[b][0] + 1 for b in range(B)], dtype=np.int32)
         state["L"] = new_len.copy()
@@ -131,11 +152,14 @@ def lockstep(cfg, steps, seed=0, check_drafter=False):
         last = np.array([c[1] for c in commit], dtype=np.int32)
         accepted.extend(c[0] for c in commit)
         assert int(vs.dev_status.item()) == 0
-    say(f"[stack] {cfg.name}: worst final-hidden rel L2 {worst_h:.2e}; mean accepted "
-        f"{np.mean(accepted):.2f} (tokens/step/seq {np.mean(accepted) + 1:.2f})")
+    say(f"[stack] {cfg.name} seed {seed}: worst final-hidden rel L2 {worst_h:.2e}; worst |d top1| "
+        f"{worst.get('top1', 0):.2e} |d top2| {worst.get('top2', 0):.2e} |d lse| {worst.get('lse', 0):.2e} "
+        f"|d draft logit| {worst.get('draft_logit', 0):.2e} (bar {ATOL}); decisions checked "
+        f"{worst.get('checked', 0)}, excused {worst.get('excused', 0)}; mean accepted {np.mean(accepted):.2f}")
+    assert worst.get("checked", 0) > 0
     if check_drafter:
         drafter_reads(cfg, vs, state, seed, dev)
-    return accepted
+    return accepted, worst, worst_h
 
 
 def drafter_reads(cfg, vs, state, seed, dev):
@@ -171,44 +195,37 @@ def drafter_reads(cfg, vs, state, seed, dev):
 @gpu
 def test_tiny_f32_verify_steps():
     """One-layer fp32 model, d=128, 2q/1kv, D=64, 64-token cache, k=3, vocab 1024."""
-    acc = lockstep(configs.TINY_F32, steps=8)
+    acc, _, _ = lockstep(configs.TINY_F32, steps=8)
     assert len(acc) == 8
 
 
 @gpu
-def test_scaled_stack_lockstep():
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_scaled_stack_lockstep(seed):
     """The 6-layer 5:1 local/global stack at sizes the oracle finishes in seconds,
-    16 verify steps with drafts matching the target at rate 0.8."""
+    16 verify steps with drafts matching the target at rate 0.8.  The statistics stay
+    within half the 2e-2 bar and the final hidden state within 3e-3."""
     cfg = configs.scaled_stack(steps=16)
-    acc = lockstep(cfg, steps=16, check_drafter=True)
+    acc, worst, worst_h = lockstep(cfg, steps=16, seed=seed, check_drafter=seed == 0)
     assert np.mean(acc) > 1.0        # drafts at rate 0.8 are mostly accepted
+    assert max(worst["top1"], worst["top2"], worst["lse"]) <= ATOL / 2
+    assert worst_h <= 3e-3
 
 
 @gpu
-def test_full_size_stack_step_one_sequence():
-    """The full stack (d=3840, d_ff=15360, 6 layers, vocab 262,144, context 131,072,
-    B=4, k=4): one verify step on the GPU, checked against the oracle on sequence 0
-    (sequences are independent), with random drafts."""
-    dev = need_gpu()
+def test_full_size_stack_lockstep():
+    """The stack workload at full size (d=3840, d_ff=15360, 6 layers, vocab 262,144,
+    context 131,072, B=4, k=4): 16 lockstep verify steps, drafts the target's greedy
+    continuation kept at rate 0.8, every sequence checked every step."""
     cfg = configs.STACK
-    B, k = cfg.batch, cfg.k
-    cap = cfg.ctx + 2 * (k + 1) + 8
-    say(f"[stack-full] generating weights and caches (cap={cap})")
-    W = inputs.stack_weights(cfg, 0, dev)
-    caches = inputs.stack_caches(cfg, 0, dev, capacity=cap, fill_from=0)
-    cl = torch.full((B,), cfg.ctx, dtype=torch.int32, device=dev)
-    tokens = inputs.randint((B, k + 1), 0, cfg.vocab - 1, 0, "full_tokens", dev)
-    drafts = tokens[:, 1:].contiguous()
-    say("[stack-full] host copies for sequence 0")
-    model = om.OracleModel(cfg, host_weights(W, True))
-    state = om.new_state(host_caches(caches, [0], cfg, cap, only_window=True), [cfg.ctx])
-    vs = VerifyStack(cfg, W, caches, cl, dev)
-    vs.step(tokens, drafts)
-    torch.cuda.synchronize()
-    say("[stack-full] oracle step for sequence 0")
-    ref = model.greedy_step(state, tokens[:1].cpu().numpy())
-    e = rel_l2(host(vs.h[:k + 1]), ref["h"])
-    say(f"[stack-full] final hidden rel L2 {e:.2e}")
-    assert e <= 1e-2
-    compare_step(vs, ref, k, B, [0], "full")
-    assert int(vs.dev_status.item()) == 0
+    acc, worst, worst_h = lockstep(cfg, steps=16, seed=0, full=True)
+    assert np.mean(acc) > 1.0
+    assert max(worst["top1"], worst["top2"], worst["lse"]) <= ATOL / 2
+
+
+@gpu
+def test_full_size_stack_batch8_steps():
+    """The batch the benchmark times (B=8, k=4, full size): two lockstep steps, all
+    eight sequences checked."""
+    cfg = dataclasses.replace(configs.STACK, batch=8)
+    lockstep(cfg, steps=2, seed=1, full=True)

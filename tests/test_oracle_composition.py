@@ -104,19 +104,21 @@ class DenseStack:
     x = sqrt(d) E[tok]; per layer a = norm(x), q/k/v = a W, RoPE on q and the new
     keys at positions L+j, the new rows appended to the layer's cache, causal
     (sliding-window) attention, x += o Wo; m = norm(x), x += (gelu(m Wg) (m Wu)) Wd;
-    h = norm(x); z = h E^T.  Values the GPU stores are rounded to its storage type
-    (bf16 or fp32) at the same points as in the oracle's reading of the stack."""
+    h = norm(x); z = h E^T.  Stored values are rounded as the stack stores them:
+    activations between the ops in fp32; new cache rows and the final hidden state
+    in the stack's type (bf16 or fp32)."""
 
     def __init__(self, cfg, weights):
         self.cfg = cfg
         self.E = as_f64(weights["E"])
         self.layers = [{k: as_f64(v) for k, v in lw.items()} for lw in weights["layers"]]
-        self.store = bf16_rne if cfg.dtype == "bf16" else f32_rne
+        self.store = f32_rne
+        self.store_kv = bf16_rne if cfg.dtype == "bf16" else f32_rne
 
     def forward(self, caches, L, tokens):
         """caches: per layer {"k": [B, Hkv, cap, D], "v": same or None} (fp32, updated);
         L [B]; tokens [B, n].  Returns (h [B*n, d], z [B*n, V])."""
-        cfg, st = self.cfg, self.store
+        cfg, st, skv = self.cfg, self.store, self.store_kv
         B, n = tokens.shape
         hs, zs = [], []
         for b in range(B):
@@ -130,11 +132,11 @@ class DenseStack:
                 q = st(a @ wq.T).reshape(n, H, D)
                 kn = st(a @ wk.T).reshape(n, Hk, D)
                 q = rope_complex(q, pos[:, None], ly.rope_dims, ly.rope_base)
-                kn = st(rope_complex(kn, pos[:, None], ly.rope_dims, ly.rope_base))
+                kn = skv(rope_complex(kn, pos[:, None], ly.rope_dims, ly.rope_base))
                 c["k"][b, :, pos[0]:pos[-1] + 1] = kn.transpose(1, 0, 2)
                 if not ly.k_is_v:
                     wv = lw["wqkv"][(H + Hk) * D:]
-                    vn = st(a @ wv.T).reshape(n, Hk, D)
+                    vn = skv(st(a @ wv.T)).reshape(n, Hk, D)
                     c["v"][b, :, pos[0]:pos[-1] + 1] = vn.transpose(1, 0, 2)
                 keys = c["k"][b].astype(np.float64)
                 vals = keys if ly.k_is_v else c["v"][b].astype(np.float64)
@@ -142,10 +144,10 @@ class DenseStack:
                 x = x + st(o.reshape(n, H * D)) @ lw["wo"].T
                 if cfg.d_ff:
                     m = st(rms_norm(x, cfg.eps) if cfg.norm else x)
-                    g = st(m @ lw["wgu"][:cfg.d_ff].T)
-                    u = st(m @ lw["wgu"][cfg.d_ff:].T)
+                    g = m @ lw["wgu"][:cfg.d_ff].T
+                    u = m @ lw["wgu"][cfg.d_ff:].T
                     x = x + st(gelu_logistic(g) * u) @ lw["wd"].T
-            h = st(rms_norm(x, cfg.eps) if cfg.norm else x)
+            h = skv(rms_norm(x, cfg.eps) if cfg.norm else x)
             hs.append(h)
             zs.append(h @ self.E.T)
         return np.concatenate(hs), np.concatenate(zs)
