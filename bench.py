@@ -112,12 +112,13 @@ def time_one(args, only) -> dict:
             kc = torch.zeros((B, ly.n_heads_kv, cap, ly.head_dim), dtype=torch.bfloat16, device=dev)
             kc[:, :, lo:cfg.ctx] = inputs.normal((B, ly.n_heads_kv, cfg.ctx - lo, ly.head_dim), 1.0, 0, "kc", dev)
         vc = None if ly.k_is_v else kc.clone()
-        q = inputs.normal((B, nq, ly.n_heads_q, ly.head_dim), 1.0, 0, "q", dev)
-        kn = inputs.normal((B, nq, ly.n_heads_kv, ly.head_dim), 1.0, 0, "kn", dev)
+        # as in the stack: fp32 queries and new rows, a bf16-pair output; bf16 (or fp8) caches
+        q = inputs.normal((B, nq, ly.n_heads_q, ly.head_dim), 1.0, 0, "q", dev, "f32")
+        kn = inputs.normal((B, nq, ly.n_heads_kv, ly.head_dim), 1.0, 0, "kn", dev, "f32")
         vn = None if ly.k_is_v else kn.clone()
         cl = torch.full((B,), cfg.ctx, dtype=torch.int32, device=dev)
-        out = torch.empty_like(q)
-        desc = attn_desc(ly, B, nq, cap, "bf16")
+        out = torch.empty((2,) + tuple(q.shape), dtype=torch.bfloat16, device=dev)
+        desc = attn_desc(ly, B, nq, cap, "bf16", act_pair=True)
         ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
         if fp8:
             vs = None if ly.k_is_v else ks.clone()
@@ -174,11 +175,12 @@ def time_one(args, only) -> dict:
                      "o_global": (glo.n_heads_q * glo.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
                      "gu": (cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_GEGLU),
                      "down": (cfg.d_ff, cfg.d_model, L.SV_EPI_ADD_F32)}[only]
-        x = inputs.normal((R, K), 1.0, 0, "x", dev)
+        # as in the stack: bf16-pair activations, bf16 weights
+        x = inputs.normal((2, R, K), 1.0, 0, "x", dev)
         W = inputs.normal((N, K), K ** -0.5, 0, "W", dev)
-        y = torch.zeros((R, N // 2 if epi == L.SV_EPI_GEGLU else N),
-                        dtype=torch.float32 if epi == L.SV_EPI_ADD_F32 else torch.bfloat16, device=dev)
-        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi)
+        y = (torch.zeros((2, R, N // 2), dtype=torch.bfloat16, device=dev) if epi == L.SV_EPI_GEGLU
+             else torch.zeros((R, N), dtype=torch.float32, device=dev))
+        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_pair=1)
         ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
         # rotate over copies of W (1 GiB in all) so that, as inside the step, no call
         # finds its weights in the last-level cache
@@ -188,7 +190,7 @@ def time_one(args, only) -> dict:
         def call():
             turn[0] += 1
             L.sv_linear(desc, x, Ws[turn[0] % len(Ws)], y, ws, stream)
-        byts = 2 * (N * K + R * K) + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 1 if epi == L.SV_EPI_GEGLU else 2)
+        byts = 2 * N * K + 4 * R * K + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 2 if epi == L.SV_EPI_GEGLU else 4)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -238,7 +240,8 @@ def call_bytes(cfg, lens, kv_bytes: int = 2) -> dict:
     sequence); kv_bytes per cache element (2 bf16, 1 fp8)."""
     B, k, d, R = cfg.batch, cfg.k, cfg.d_model, cfg.batch * (cfg.k + 1)
     nq = k + 1
-    e = 2  # bf16
+    e = 2  # bf16 weights and cache rows
+    a = 4  # activations between the ops: fp32, or bf16 pairs (the final hidden state is bf16)
     out = {"lmhead": cfg.vocab * d * e + R * d * e}
     for i, ly in enumerate(cfg.layers):
         H, Hk, D = ly.n_heads_q, ly.n_heads_kv, ly.head_dim
@@ -248,14 +251,14 @@ def call_bytes(cfg, lens, kv_bytes: int = 2) -> dict:
             n = L + nq
             keys += min(n, ly.window + k) if ly.window else n
         kv = keys * Hk * D * kv_bytes * tensors
-        qio = B * nq * H * D * e * 2 + B * nq * Hk * D * e * tensors
+        qio = B * nq * H * D * a * 2 + B * nq * Hk * D * a * tensors
         out[f"L{i}.attn"] = kv + qio
         nout = H * D + Hk * D * tensors
-        out[f"L{i}.qkv"] = nout * d * e + R * d * e + R * nout * e
-        out[f"L{i}.o"] = d * H * D * e + R * H * D * e + R * d * 4 * 2
+        out[f"L{i}.qkv"] = nout * d * e + R * d * a + R * nout * a
+        out[f"L{i}.o"] = d * H * D * e + R * H * D * a + R * d * 4 * 2
         if cfg.d_ff:
-            out[f"L{i}.gu"] = 2 * cfg.d_ff * d * e + R * d * e + R * cfg.d_ff * e  # fused GeGLU output
-            out[f"L{i}.down"] = d * cfg.d_ff * e + R * cfg.d_ff * e + R * d * 4 * 2
+            out[f"L{i}.gu"] = 2 * cfg.d_ff * d * e + R * d * a + R * cfg.d_ff * a  # fused GeGLU output
+            out[f"L{i}.down"] = d * cfg.d_ff * e + R * cfg.d_ff * a + R * d * 4 * 2
     return out
 
 

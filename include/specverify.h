@@ -52,7 +52,10 @@ typedef enum {
                                SV_NOALLOC_SCRATCH_BYTES */
 } sv_status;
 
-typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+/* SV_BF16X2 (an output type of the norms): a bf16 pair, two planes [2, ...] holding
+ * hi = bf16(v) and lo = bf16(v - hi) of an fp32 value v -- hi + lo is within 2^-16 |v|
+ * of v, and a bf16 MFMA takes it as two operands. */
+typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_BF16X2 = 2 } sv_dtype;
 
 /* device status bits */
 #define SV_DEV_CACHE_OVERFLOW 0x1  /* cache_len[b] + appended rows > cache_capacity */
@@ -97,12 +100,14 @@ typedef struct {
   int64_t q_row_stride;  /* elements between query rows (b, j) and (b, j+1); 0 = Hq*D */
   int64_t kv_row_stride; /* same for k_new / v_new; 0 = Hkv*D.  Lets q, k_new, v_new be
                             column slices of one fused projection output */
-  int32_t act_f32;       /* 0: as above.  1 (dtype SV_BF16): fp32 activations -- q, k_new and
+  int32_t act_pair;      /* 0: as above.  1 (dtype SV_BF16): pair activations -- q, k_new and
                             v_new are fp32 (or, with in_splits, their fp32 slice sums are used
                             without the bf16 rounding), so q and the new keys are rotated from
                             their fp32 values and k, v are rounded to the cache type only when
-                            stored; out [B, n_q, Hq, D] is written in fp32.  The caches and
-                            the rotated queries the products read stay bf16 */
+                            stored; out is written as a bf16 pair [2, B, n_q, Hq, D]: plane 0
+                            hi = bf16(o), plane 1 lo = bf16(o - hi), together within 2^-16 |o|
+                            of the fp32 result (the input sv_linear takes with act_pair).  The
+                            caches and the rotated queries the products read stay bf16 */
   int32_t reserved_i;    /* must be 0 */
 } sv_attn_desc;
 
@@ -396,7 +401,8 @@ int sv_embed(int32_t rows, int32_t d_model, int32_t vocab, sv_dtype dtype,
              int32_t* dev_status, void* stream);
 
 /* y = x / sqrt(mean(x^2) + eps) * gain (gain NULL = unit gain); x [rows, dim] fp32,
- * gain [dim] fp32, y [rows, dim] in `out_dtype`. */
+ * gain [dim] fp32, y [rows, dim] in `out_dtype` (SV_BF16X2: [2, rows, dim], the pair
+ * input of sv_linear with act_pair). */
 int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float* gain,
                void* y, sv_dtype out_dtype, void* stream);
 
@@ -420,8 +426,8 @@ int sv_draft_input(int32_t batch, int32_t d_main, int32_t d_draft, float eps, co
  * y = rmsnorm(x)"): x (fp32 [rows, dim], updated in place) += the sum of the
  * `splits` slices of parts (fp32 [splits, rows, dim], as SV_EPI_SPLIT_F32 writes
  * them; added in slice order, the sum then added to x), then y = rmsnorm(x) as
- * sv_rmsnorm.  parts NULL or splits 0: no add.  dim % 4 == 0, x / parts / gain /
- * y 16-byte aligned. */
+ * sv_rmsnorm (out_dtype SV_F32, SV_BF16 or SV_BF16X2).  parts NULL or splits 0: no
+ * add.  dim % 4 == 0, x / parts / gain / y 16-byte aligned. */
 int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, const float* parts, int32_t splits,
                    const float* gain, void* y, sv_dtype out_dtype, void* stream);
 
@@ -449,13 +455,13 @@ typedef struct {
   int32_t out_features;  /* N, a multiple of 64 */
   sv_dtype dtype;        /* of x and w (and y for SV_EPI_STORE) */
   sv_epilogue epilogue;
-  int32_t act_f32;       /* 0: as above.  1 (dtype SV_BF16, weights bf16): the activations
-                            are fp32 -- x [R, K] is fp32 (16-byte aligned rows) and each value
-                            enters the bf16 product as hi = bf16(x) plus lo = bf16(x - hi)
-                            (two MFMAs; the product is x W^T up to 2^-17 |x| per element);
-                            SV_EPI_STORE writes y in fp32, SV_EPI_GEGLU writes
-                            gelu_tanh(g) * u in fp32 from the fp32 g and u (no bf16
-                            rounding); ADD_F32 and SPLIT_F32 are unchanged */
+  int32_t act_pair;      /* 0: as above.  1 (dtype SV_BF16, weights bf16): pair activations --
+                            x is a bf16 pair [2, R, K] (plane 0 hi = bf16(v), plane 1
+                            lo = bf16(v - hi) of an fp32 activation v, together within
+                            2^-16 |v|), multiplied as hi W^T + lo W^T (two MFMAs, fp32
+                            accumulation); SV_EPI_STORE writes y in fp32; SV_EPI_GEGLU writes
+                            gelu_tanh(g) * u, from the fp32 g and u (no bf16 rounding), as a
+                            bf16 pair [2, R, N/2]; ADD_F32 and SPLIT_F32 are unchanged */
 } sv_linear_desc;
 
 /* S of SV_EPI_SPLIT_F32 for this shape on the current device (1 <= S <= the

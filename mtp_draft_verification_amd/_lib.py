@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE, SV_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
 SV_NOALLOC_SCRATCH_BYTES = 32 << 20
-SV_F32, SV_BF16 = 0, 1
+SV_F32, SV_BF16, SV_BF16X2 = 0, 1, 2
 SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL, SV_SELECT_SAMPLE_RS = 0, 1, 2, 3
 SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU, SV_EPI_SPLIT_F32 = 0, 1, 2, 3
 SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
@@ -43,7 +43,7 @@ class AttnDesc(ctypes.Structure):
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
                 ("reserved_f", ctypes.c_float), ("cache_capacity", ctypes.c_int64),
                 ("q_row_stride", ctypes.c_int64), ("kv_row_stride", ctypes.c_int64),
-                ("act_f32", ctypes.c_int32), ("reserved_i", ctypes.c_int32)]
+                ("act_pair", ctypes.c_int32), ("reserved_i", ctypes.c_int32)]
 
 
 class LMHeadDesc(ctypes.Structure):
@@ -60,7 +60,7 @@ class AcceptDesc(ctypes.Structure):
 class LinearDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("in_features", ctypes.c_int32),
                 ("out_features", ctypes.c_int32), ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32),
-                ("act_f32", ctypes.c_int32)]
+                ("act_pair", ctypes.c_int32)]
 
 
 class ClusterDesc(ctypes.Structure):

@@ -39,8 +39,9 @@ struct AttnParams {
   int32_t* seg_cnt;       // workspace: [B * Hkv] arrivals of a segment's pieces
   int32_t* plan;          // workspace: the work split {chunk, pieces}, set by rope_append
   int in_splits;          // > 0: q, k_new, v_new are fp32 K-split partial products
-  int act_f32;            // fp32 activations: q, k_new, v_new read as fp32 (no bf16 rounding
-                          // before RoPE / the cache store), out written fp32
+  int act_pair;           // pair activations: q, k_new, v_new read as fp32 (no bf16 rounding
+                          // before RoPE / the cache store), out written as a bf16 pair
+  int64_t out_plane;      // pair activations: elements between out's hi and lo planes
   int fp8;                // caches hold fp8 E4M3 codes seen through per-channel scales
   const float* k_scale;   // fp8: [Hkv, D] scales of the key cache (also the values when K = V)
   const float* v_scale;   // fp8: [Hkv, D] scales of the value cache
@@ -292,10 +293,14 @@ __device__ __forceinline__ double ld_in(const InView& v, int64_t i) {
   return (double)bf16_to_f32((uint16_t)f32_to_bf16_bits(a));
 }
 
-// four consecutive output elements (bf16, or fp32 with fp32 activations)
+// four consecutive output elements: bf16, or with pair activations the bf16 pair
+// hi = bf16(a), lo = bf16(a - hi) in two planes
 __device__ __forceinline__ void st_out4(const AttnParams& p, int64_t i, float a0, float a1, float a2, float a3) {
-  if (p.act_f32) *(f32x4_t*)((float*)p.out + i) = f32x4_t{a0, a1, a2, a3};
-  else *(uint2*)((uint16_t*)p.out + i) = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+  const uint32_t h01 = pack_bf16x2(a0, a1), h23 = pack_bf16x2(a2, a3);
+  *(uint2*)((uint16_t*)p.out + i) = make_uint2(h01, h23);
+  if (p.act_pair)
+    *(uint2*)((uint16_t*)p.out + p.out_plane + i) =
+        make_uint2(pack_bf16x2(a0 - bf16_lo(h01), a1 - bf16_hi(h01)), pack_bf16x2(a2 - bf16_lo(h23), a3 - bf16_hi(h23)));
 }
 
 // rotate-half RoPE of element d of a head vector x (pre-rotation values) at position pos
@@ -375,8 +380,8 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
       seq_range(p, b, lo, len);
       if (len == 0) {
         const int64_t oi = (((int64_t)b * p.nq + j) * p.Hq + hs) * p.D + d;
-        if (p.act_f32) ((float*)p.out)[oi] = 0.f;
-        else ((uint16_t*)p.out)[oi] = 0;
+        ((uint16_t*)p.out)[oi] = 0;
+        if (p.act_pair) ((uint16_t*)p.out)[p.out_plane + oi] = 0;
       }
     }
   }
@@ -391,13 +396,13 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
   if (hs < p.Hq) {
     const int64_t src = ((int64_t)b * p.nq + j) * p.q_stride + (int64_t)hs * D;
     const int64_t dst = (((int64_t)b * p.nq + j) * p.Hq + hs) * D;
-    const InView qv{p.q, (int64_t)p.B * p.nq * p.q_stride, p.in_splits, p.act_f32};
+    const InView qv{p.q, (int64_t)p.B * p.nq * p.q_stride, p.in_splits, p.act_pair};
     st_elem<T>(p.q_rot, dst + d, rope_elem<T>(qv, src, d, p.rope_dims, p.log2_base, pos));
   } else if (hs < p.Hq + p.Hkv) {
     const int h = hs - p.Hq;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-    const InView kv{p.k_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits, p.act_f32};
+    const InView kv{p.k_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits, p.act_pair};
     const double kr = rope_elem<T>(kv, src, d, p.rope_dims, p.log2_base, pos);
     if constexpr (sizeof(T) == 2) st_cache(p, p.k_cache, p.k_scale, dst + d, h * D + d, kr);
     else st_elem<T>(p.k_cache, dst + d, kr);
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(512) void rope_append_kernel(AttnParams p) {
     const int h = hs - p.Hq - p.Hkv;
     const int64_t src = ((int64_t)b * p.nq + j) * p.kv_stride + (int64_t)h * D;
     const int64_t dst = (((int64_t)b * p.Hkv + h) * p.cap + L + j) * D;
-    const InView vv{p.v_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits, p.act_f32};
+    const InView vv{p.v_new, (int64_t)p.B * p.nq * p.kv_stride, p.in_splits, p.act_pair};
     if constexpr (sizeof(T) == 2) st_cache(p, p.v_cache, p.v_scale, dst + d, h * D + d, ld_in<T>(vv, src + d));
     else st_elem<T>(p.v_cache, dst + d, ld_in<T>(vv, src + d));
   }
@@ -1239,8 +1244,8 @@ static int validate_attn(const sv_attn_desc* d) {
   if (d->append != 0 && d->append != 1) return SV_ERR_ARG;
   if (d->append && d->q_pos_offset != 0) return SV_ERR_ARG;
   if (d->in_splits < 0 || d->reserved_f != 0.f || d->reserved_i != 0) return SV_ERR_ARG;
-  if (d->act_f32 != 0 && d->act_f32 != 1) return SV_ERR_ARG;
-  if (d->act_f32 && d->dtype != SV_BF16) return SV_ERR_ARG;
+  if (d->act_pair != 0 && d->act_pair != 1) return SV_ERR_ARG;
+  if (d->act_pair && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->in_splits > 0 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->cache_capacity <= 0) return SV_ERR_ARG;
   if (d->q_row_stride < 0 || d->kv_row_stride < 0) return SV_ERR_ARG;
@@ -1366,7 +1371,8 @@ static int verify_attn(const sv_attn_desc* d, const void* q, const void* k_new, 
   p.nwg = device_cus();
   p.min_chunk = 64;
   p.in_splits = d->in_splits;
-  p.act_f32 = d->act_f32;
+  p.act_pair = d->act_pair;
+  p.out_plane = (int64_t)d->batch * d->n_q * d->n_heads_q * d->head_dim;
   p.fp8 = fp8 ? 1 : 0;
   p.k_scale = k_scale;
   p.v_scale = d->k_is_v ? k_scale : v_scale;

@@ -35,8 +35,9 @@ constexpr bool select_mode(int m) { return m <= GM_RESIDUAL || m == GM_SAMPLE_RS
 constexpr int kRsCand = 4;  // first-pass candidates per draft row (single-pass sampling)
 
 struct GemmParams {
-  const void* x;         // [R, K] rows, bf16 (fp32 when the kernel's XF is set; RESIDUAL:
-                         // the hidden states, gathered per slot)
+  const void* x;         // [R, K] rows, bf16 (with the kernel's XF: two bf16 planes [2, R, K],
+                         // hi then lo, of pair activations; RESIDUAL: the hidden states,
+                         // gathered per slot)
   const uint16_t* w;     // [N, K]
   int R, K, N;
   int nblk, kch;         // feature blocks, 64-wide K chunks
@@ -343,9 +344,9 @@ __device__ __forceinline__ RowState from_part(const SelPart& p) {
 // spans several workgroups leaves one fp32 partial per workgroup; per wave slice
 // an arrival counter picks the last arriver, which adds the partials in
 // workgroup order (deterministic) and runs the epilogue.
-// With XF (fp32 activations) a chunk of x is 16 MT rows x 256 B, staged as two
-// halves of 32 dims (one per k-step), each laid out like a bf16 chunk: 128 B per
-// row, 16-byte slots swizzled by row.
+// With XF (pair activations) a chunk of x is staged twice, the hi plane then the lo
+// plane, each laid out like a bf16 chunk: 16 MT rows x 128 B, 16-byte slots
+// swizzled by row.
 template <int MT, int T, int XF = 0>
 struct RingCfg {
   static constexpr int NB = 64 * T;            // output features per block
@@ -404,9 +405,9 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
   for (int ii = 0; ii < C::NX; ++ii) {
     const int j = (wave + 4 * ii) < C::XI ? (wave + 4 * ii) : C::XI - 1;
-    // XF: instruction j moves half j / (2 MT) (dims 32h..32h+31 of the chunk) of the
-    // rows of 8-row block j % (2 MT)
-    const int half = XF ? j / (2 * MT) : 0;
+    // XF: instruction j moves plane j / (2 MT) (0 = hi, 1 = lo) of the rows of 8-row
+    // block j % (2 MT)
+    const int plane = XF ? j / (2 * MT) : 0;
     const int jb = XF ? j % (2 * MT) : j;
     const int r = jb * 8 + dl8;
     int xr = 0;
@@ -418,13 +419,8 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
         xr = r;
       }
     }
-    if constexpr (XF) {
-      xoff[ii] = (uint32_t)(xr * K * 4 + half * 128 + cq[jb & 1] * 16);
-      xadj[ii] = half ? 128u : 0u;  // a 32-dim last chunk has no second half: re-read the first
-    } else {
-      xoff[ii] = (uint32_t)(xr * K * 2 + cq[jb & 1] * 16);
-      xadj[ii] = adj[jb & 1];
-    }
+    xoff[ii] = (uint32_t)(((int64_t)plane * nx + xr) * K * 2 + cq[jb & 1] * 16);
+    xadj[ii] = adj[jb & 1];
     xlds[ii] = (uint32_t)(C::WSTAGE + j * 1024);
   }
 
@@ -450,7 +446,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < C::WI; ++i)
       dma16(wb, woff[i] - (tail ? adj[i & 1] : 0u), dst + (uint32_t)((wave * C::WI + i) * 1024));
-    const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * (XF ? 256 : 128);
+    const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * 128;
 #pragma unroll
     for (int ii = 0; ii < C::NX; ++ii) dma16(xb, xoff[ii] - (tail ? xadj[ii] : 0u), dst + xlds[ii]);
   };
@@ -571,15 +567,21 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
         } else if constexpr (MODE == GM_GEGLU) {
           // tile 0 holds the gate, tile 1 the up projection of the same 16 features
           // (weights interleaved by 16 rows).  bf16 activations: both pass through bf16
-          // as stored values and the product is stored bf16; fp32 activations (XF): the
-          // product of the fp32 gate and up values is stored fp32
+          // as stored values and the product is stored bf16; pair activations (XF): the
+          // product of the fp32 gate and up values is stored as a bf16 pair (hi plane,
+          // lo plane [2, R, N/2])
           if (t == 1 && r < nx) {
             const int c0 = row0 / 2 + lg * 4;
             if constexpr (XF) {
-              f32x4_t f;
+              float f[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) f[e] = gelu_tanh(acc[0][mt][e]) * acc[1][mt][e];
-              *(f32x4_t*)((float*)p.y + (int64_t)r * (p.N / 2) + c0) = f;
+              uint16_t* y = (uint16_t*)p.y + (int64_t)r * (p.N / 2) + c0;
+              const uint32_t h01 = pack_bf16x2(f[0], f[1]), h23 = pack_bf16x2(f[2], f[3]);
+              *(uint2*)y = make_uint2(h01, h23);
+              *(uint2*)(y + (int64_t)nx * (p.N / 2)) =
+                  make_uint2(pack_bf16x2(f[0] - bf16_lo(h01), f[1] - bf16_hi(h01)),
+                             pack_bf16x2(f[2] - bf16_lo(h23), f[3] - bf16_hi(h23)));
             } else {
               float f[4];
 #pragma unroll
@@ -636,30 +638,22 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
       for (int t = 0; t < T; ++t) a[t].u = *(const uint4*)(ws + t * 2048 + so);
       if constexpr (XF) {
-        // the lane's 8 fp32 dims (32 B: slots 2 lg and 2 lg + 1 of half js) enter the
-        // product as hi = bf16(x) and lo = bf16(x - hi): x W^T = hi W^T + lo W^T up to
-        // 2^-17 |x| per element
-        const uint8_t* xh = xs + js * (MT * 2048);
+        // x W^T = hi W^T + lo W^T: the hi products of every tile pair first, then the lo
+        // ones, so the two MFMAs into one accumulator are not back to back
         V16 bh[MT], bl[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const f32x4_t v0 = *(const f32x4_t*)(xh + mt * 2048 + (((2 * lg) ^ fsw) << 4));
-          const f32x4_t v1 = *(const f32x4_t*)(xh + mt * 2048 + (((2 * lg + 1) ^ fsw) << 4));
-          const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t h = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-            bh[mt].w[e] = h;
-            bl[mt].w[e] = pack_bf16x2(v[2 * e] - bf16_lo(h), v[2 * e + 1] - bf16_hi(h));
-          }
+          bh[mt].u = *(const uint4*)(xs + mt * 2048 + so);
+          bl[mt].u = *(const uint4*)(xs + (MT + mt) * 2048 + so);
         }
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            acc[t][mt] = mfma16x16x32(a[t].b, bh[mt].b, acc[t][mt]);
-            acc[t][mt] = mfma16x16x32(a[t].b, bl[mt].b, acc[t][mt]);
-          }
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a[t].b, bh[mt].b, acc[t][mt]);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a[t].b, bl[mt].b, acc[t][mt]);
       } else {
         V16 bx[MT];
 #pragma unroll
@@ -1306,8 +1300,8 @@ static int validate_linear(const sv_linear_desc* d) {
       d->epilogue != SV_EPI_SPLIT_F32)
     return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_SPLIT_F32 && d->dtype != SV_BF16) return SV_ERR_ARG;
-  if (d->act_f32 != 0 && d->act_f32 != 1) return SV_ERR_ARG;
-  if (d->act_f32 && d->dtype != SV_BF16) return SV_ERR_ARG;
+  if (d->act_pair != 0 && d->act_pair != 1) return SV_ERR_ARG;
+  if (d->act_pair && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->out_features % 64) return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_GEGLU && (d->dtype != SV_BF16 || d->out_features % 128)) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
@@ -1609,8 +1603,8 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   p.y = y;
   p.cnt = (int32_t*)workspace;
   p.part = (float*)((char*)workspace + pl.cnt_bytes);
-  if (d->act_f32) {
-    // fp32 activations: x read as fp32 (hi + lo bf16 operands); STORE and GEGLU write fp32
+  if (d->act_pair) {
+    // pair activations: x read as its hi and lo bf16 planes; STORE writes fp32, GEGLU a pair
     if (d->epilogue == SV_EPI_GEGLU)
       rc = dispatch_ring<2, GM_GEGLU, 1>(p, d->rows, pl.grid, s);
     else if (d->epilogue == SV_EPI_SPLIT_F32)

@@ -48,8 +48,32 @@ __global__ __launch_bounds__(256) void embed_kernel(int d_model, int vocab, int 
 // exchange between the four waves, then scaled and stored.
 constexpr int kNormVec = 8;  // rows up to 256 * 4 * 8 = 8192 elements take the register path
 
+// Norm output y[i..i+3] in the output type: 0 fp32, 1 bf16, 2 bf16 pair (hi plane,
+// then the lo plane `plane` elements further: hi = bf16(o), lo = bf16(o - hi)).
+__device__ __forceinline__ void st_norm4(void* y, int mode, int64_t i, int64_t plane, const f32x4_t& o) {
+  if (mode == 0) {
+    *(f32x4_t*)((float*)y + i) = o;
+    return;
+  }
+  const uint32_t h01 = pack_bf16x2(o[0], o[1]), h23 = pack_bf16x2(o[2], o[3]);
+  *(uint2*)((uint16_t*)y + i) = make_uint2(h01, h23);
+  if (mode == 2)
+    *(uint2*)((uint16_t*)y + plane + i) =
+        make_uint2(pack_bf16x2(o[0] - bf16_lo(h01), o[1] - bf16_hi(h01)), pack_bf16x2(o[2] - bf16_lo(h23), o[3] - bf16_hi(h23)));
+}
+__device__ __forceinline__ void st_norm1(void* y, int mode, int64_t i, int64_t plane, float o) {
+  if (mode == 0) {
+    ((float*)y)[i] = o;
+    return;
+  }
+  const uint32_t h = f32_to_bf16_bits(o);
+  ((uint16_t*)y)[i] = (uint16_t)h;
+  if (mode == 2) ((uint16_t*)y)[plane + i] = (uint16_t)f32_to_bf16_bits(o - bf16_to_f32((uint16_t)h));
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int dim, float eps, const float* x, const float* gain,
-                                                      void* y, int bf16) {
+                                                      void* y, int mode) {
+  const int64_t plane = (int64_t)gridDim.x * dim;
   __shared__ float s_red[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   const float* xr = x + (int64_t)r * dim;
@@ -87,18 +111,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int dim, float eps, const 
         const f32x4_t g = *(const f32x4_t*)(gain + 4 * i);
         o = f32x4_t{o[0] * g[0], o[1] * g[1], o[2] * g[2], o[3] * g[3]};
       }
-      if (bf16)
-        *(uint2*)((uint16_t*)y + (int64_t)r * dim + 4 * i) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      else
-        *(f32x4_t*)((float*)y + (int64_t)r * dim + 4 * i) = o;
+      st_norm4(y, mode, (int64_t)r * dim + 4 * i, plane, o);
     }
     return;
   }
   for (int i = tid; i < dim; i += 256) {
     float o = xr[i] * inv;
     if (gain) o *= gain[i];
-    if (bf16) ((uint16_t*)y)[(int64_t)r * dim + i] = (uint16_t)f32_to_bf16_bits(o);
-    else ((float*)y)[(int64_t)r * dim + i] = o;
+    st_norm1(y, mode, (int64_t)r * dim + i, plane, o);
   }
 }
 
@@ -111,7 +131,7 @@ constexpr int kAddThreads = 1024, kAddVec = 2, kSplitBatch = 8;
 
 __global__ __launch_bounds__(kAddThreads) void add_rmsnorm_kernel(int rows, int dim, float eps, float* x,
                                                                   const float* parts, int splits,
-                                                                  const float* gain, void* y, int bf16) {
+                                                                  const float* gain, void* y, int mode) {
   __shared__ float s_red[kAddThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n4 = dim / 4;
@@ -165,10 +185,7 @@ __global__ __launch_bounds__(kAddThreads) void add_rmsnorm_kernel(int rows, int 
       const f32x4_t g = *(const f32x4_t*)(gain + 4 * i);
       o = f32x4_t{o[0] * g[0], o[1] * g[1], o[2] * g[2], o[3] * g[3]};
     }
-    if (bf16)
-      *(uint2*)((uint16_t*)y + (int64_t)r * dim + 4 * i) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    else
-      *(f32x4_t*)((float*)y + (int64_t)r * dim + 4 * i) = o;
+    st_norm4(y, mode, (int64_t)r * dim + 4 * i, (int64_t)rows * dim, o);
   }
 }
 
@@ -253,25 +270,25 @@ extern "C" int sv_embed(int32_t rows, int32_t d_model, int32_t vocab, sv_dtype d
 extern "C" int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float* gain, void* y,
                           sv_dtype out_dtype, void* stream) {
   if (rows <= 0 || dim <= 0 || !x || !y || !(eps >= 0.f)) return SV_ERR_ARG;
-  if (out_dtype != SV_F32 && out_dtype != SV_BF16) return SV_ERR_ARG;
+  if (out_dtype != SV_F32 && out_dtype != SV_BF16 && out_dtype != SV_BF16X2) return SV_ERR_ARG;
   int rc = check_device();
   if (rc != SV_OK) return rc;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, (hipStream_t)stream, dim, eps, x, gain, y,
-                     out_dtype == SV_BF16 ? 1 : 0);
+                     out_dtype == SV_F32 ? 0 : out_dtype == SV_BF16 ? 1 : 2);
   return launch_status();
 }
 
 extern "C" int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, const float* parts, int32_t splits,
                               const float* gain, void* y, sv_dtype out_dtype, void* stream) {
   if (rows <= 0 || dim <= 0 || !x || !y || !(eps >= 0.f) || splits < 0) return SV_ERR_ARG;
-  if (out_dtype != SV_F32 && out_dtype != SV_BF16) return SV_ERR_ARG;
+  if (out_dtype != SV_F32 && out_dtype != SV_BF16 && out_dtype != SV_BF16X2) return SV_ERR_ARG;
   if (!parts) splits = 0;
   if (dim % 4 || (((uintptr_t)x | (uintptr_t)parts | (uintptr_t)gain | (uintptr_t)y) & 15)) return SV_ERR_ARG;
   if (dim > kAddThreads * 4 * kAddVec) return SV_ERR_UNSUPPORTED;
   int rc = check_device();
   if (rc != SV_OK) return rc;
   hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(rows), dim3(kAddThreads), 0, (hipStream_t)stream, rows, dim, eps, x,
-                     parts, splits, gain, y, out_dtype == SV_BF16 ? 1 : 0);
+                     parts, splits, gain, y, out_dtype == SV_F32 ? 0 : out_dtype == SV_BF16 ? 1 : 2);
   return launch_status();
 }
 

@@ -21,10 +21,11 @@ then h = rmsnorm(x), sv_lmhead_select over the tied embedding and sv_accept.  Th
 fp32 stack (no norms) adds into x with SV_EPI_ADD_F32 instead.
 
 In the bf16 stack the weights and the caches are bf16 and the activations between
-the calls are fp32 (act_f32): the norm outputs, q / k / v (their K-split sums),
-the attention output and the GeGLU output.  Each projection takes its fp32 input as
-a hi + lo pair of bf16 MFMA operands; only the new cache rows and the final hidden
-state that the LM head reads are rounded to bf16.
+the calls keep fp32 precision: q / k / v are fp32 K-split partial sums, and the norm
+outputs, the attention output and the GeGLU output -- the inputs of the projections
+-- are bf16 pairs (act_pair: hi = bf16(v) and lo = bf16(v - hi) in two planes,
+within 2^-16 |v|, multiplied as two bf16 MFMA operands).  Only the new cache rows
+and the final hidden state that the LM head reads are rounded to bf16.
 
 Every call is enqueued on one stream with no host synchronisation; all buffers
 are allocated once up front, so a step allocates nothing.  This module only
@@ -41,14 +42,14 @@ from . import _lib as L
 
 def attn_desc(layer, batch: int, n_q: int, cap: int, dtype: str, append: bool = True,
               q_pos_offset: int = 0, q_row_stride: int = 0, kv_row_stride: int = 0,
-              in_splits: int = 0, act_f32: bool = False) -> L.AttnDesc:
+              in_splits: int = 0, act_pair: bool = False) -> L.AttnDesc:
     return L.AttnDesc(batch=batch, n_q=n_q, n_heads_q=layer.n_heads_q, n_heads_kv=layer.n_heads_kv,
                       head_dim=layer.head_dim, window=layer.window, rope_dims=layer.rope_dims,
                       k_is_v=int(layer.k_is_v), append=int(append), q_pos_offset=q_pos_offset,
                       dtype=L.SV_BF16 if dtype == "bf16" else L.SV_F32, in_splits=int(in_splits),
                       rope_base=float(layer.rope_base), softmax_scale=float(layer.scale), reserved_f=0.0,
                       cache_capacity=int(cap), q_row_stride=int(q_row_stride),
-                      kv_row_stride=int(kv_row_stride), act_f32=int(bool(act_f32)), reserved_i=0)
+                      kv_row_stride=int(kv_row_stride), act_pair=int(bool(act_pair)), reserved_i=0)
 
 
 def interleave_gate_up(wgu: torch.Tensor) -> torch.Tensor:
@@ -71,27 +72,34 @@ class VerifyStack:
         self.dev = torch.device(device)
         self.bf16 = cfg.dtype == "bf16"
         self.dt = L.SV_BF16 if self.bf16 else L.SV_F32
-        self.act = int(self.bf16)  # bf16 weights and caches, fp32 activations
+        self.act = int(self.bf16)  # bf16 weights and caches, pair activations
         if not cfg.norm and self.bf16:
             raise ValueError("a bf16 stack needs its final RMSNorm to produce the bf16 hidden state "
                              "the LM head reads")
         B, k, d = cfg.batch, cfg.k, cfg.d_model
         self.R = R = B * (k + 1)
         self.cap = caches[0]["k"].shape[2]
-        # fused GeGLU projection where the layout applies (bf16, 2*d_ff a multiple of 128)
+        # fused GeGLU projection where the layout applies (bf16, 2*d_ff a multiple of 128); the
+        # bf16 stack's pair activations come only from the fused one
         self.fused_geglu = bool(self.bf16 and cfg.d_ff and (2 * cfg.d_ff) % 128 == 0)
+        if self.bf16 and cfg.d_ff and not self.fused_geglu:
+            raise ValueError("a bf16 stack needs d_ff to be a multiple of 64 (the fused GeGLU projection)")
         self.wgu_il = ([interleave_gate_up(lw["wgu"]) for lw in weights["layers"]]
                        if self.fused_geglu else None)
         dev = self.dev
         z = lambda *s, dtype=torch.float32: torch.zeros(*s, dtype=dtype, device=dev)
+        # projection inputs: bf16 pairs [2, R, n] (bf16 stack) or fp32 [R, n]
+        act = (lambda n: z(2, R, n, dtype=torch.bfloat16)) if self.bf16 else (lambda n: z(R, n))
+        self.act_dt = L.SV_BF16X2 if self.bf16 else L.SV_F32
         self.x = z(R, d)
-        self.a = z(R, d)
+        self.a = act(d)
         nout = max(ly.n_heads_q * ly.head_dim + (1 if ly.k_is_v else 2) * ly.n_heads_kv * ly.head_dim
                    for ly in cfg.layers)
         self.qkv = z(R, nout)
-        self.o = z(R, max(ly.n_heads_q * ly.head_dim for ly in cfg.layers))
+        self.hd_max = max(ly.n_heads_q * ly.head_dim for ly in cfg.layers)
+        self.o = act(self.hd_max)
         self.gu = z(R, 2 * cfg.d_ff) if cfg.d_ff and not self.fused_geglu else None
-        self.f = z(R, cfg.d_ff) if cfg.d_ff else None
+        self.f = act(cfg.d_ff) if cfg.d_ff else None
         # the final hidden state, in the LM head's dtype
         self.h = z(R, d, dtype=torch.bfloat16) if self.bf16 else self.a
         # residual projections leave K-split partials that the next norm adds into x
@@ -101,7 +109,7 @@ class VerifyStack:
                 for K in (ly.n_heads_q * ly.head_dim, cfg.d_ff):
                     if K:
                         S = L.sv_linear_splits(L.LinearDesc(rows=R, in_features=K, out_features=d, dtype=self.dt,
-                                                            epilogue=L.SV_EPI_SPLIT_F32, act_f32=self.act))
+                                                            epilogue=L.SV_EPI_SPLIT_F32, act_pair=self.act))
                         if S > 0:
                             self.split[K] = S
         self.parts = z(max(self.split.values()) * R * d, dtype=torch.float32) if self.split else None
@@ -112,7 +120,7 @@ class VerifyStack:
             if self.bf16:
                 S = max(0, L.sv_linear_splits(L.LinearDesc(rows=R, in_features=d, out_features=self._nout(ly),
                                                            dtype=self.dt, epilogue=L.SV_EPI_SPLIT_F32,
-                                                           act_f32=self.act)))
+                                                           act_pair=self.act)))
             self.qkv_split.append(S)
         nout_max = max(self._nout(ly) for ly in cfg.layers)
         self.qkv_parts = (z(max(self.qkv_split) * R * nout_max, dtype=torch.float32) if max(self.qkv_split) else None)
@@ -131,7 +139,7 @@ class VerifyStack:
         self.timers = None   # {call name: [(start event, end event), ...]} when timing
         self.attn_descs = [
             attn_desc(ly, B, k + 1, self.cap, cfg.dtype, q_row_stride=self._nout(ly), kv_row_stride=self._nout(ly),
-                      in_splits=S, act_f32=self.act) for ly, S in zip(cfg.layers, self.qkv_split)]
+                      in_splits=S, act_pair=self.act) for ly, S in zip(cfg.layers, self.qkv_split)]
 
     def _ev(self, name: str, stream):
         """Record a HIP event pair around a named call when that call is being timed."""
@@ -164,12 +172,12 @@ class VerifyStack:
 
     def _lin_ws(self, R, K, N, epi) -> int:
         return L.sv_linear_workspace(L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt,
-                                                  epilogue=epi, act_f32=self.act))
+                                                  epilogue=epi, act_pair=self.act))
 
     def _linear(self, x, w, y, epi, stream):
         R, K = self.R, w.shape[1]
         N = w.shape[0]
-        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi, act_f32=self.act)
+        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi, act_pair=self.act)
         L.sv_linear(desc, x, w, y, self.lin_ws, stream)
 
     def _residual(self, inp, w, stream):
@@ -183,9 +191,9 @@ class VerifyStack:
         self._linear(inp, w, self.x, L.SV_EPI_ADD_F32, stream)
         return None
 
-    def _norm(self, x, y, stream, pending=None):
+    def _norm(self, x, y, stream, pending=None, odt=None):
         if self.cfg.norm:
-            odt = L.SV_BF16 if y.dtype == torch.bfloat16 else L.SV_F32
+            odt = self.act_dt if odt is None else odt
             if pending is not None:
                 L.sv_add_rmsnorm(self.R, x.shape[1], self.cfg.eps, x, pending[0], pending[1], None, y, odt, stream)
             else:
@@ -193,6 +201,12 @@ class VerifyStack:
             return y
         assert pending is None
         return x  # fp32 stack without norms feeds the residual stream directly
+
+    def _act_view(self, buf, n):
+        """The first n columns of a projection-input buffer, densely packed (rows of n)."""
+        if self.bf16:
+            return buf.view(-1)[:2 * self.R * n].view(2, self.R, n)
+        return buf.view(-1)[:self.R * n].view(self.R, n)
 
     # ------------------------------------------------------------------
     def forward(self, tokens: torch.Tensor, stream=None) -> torch.Tensor:
@@ -226,7 +240,7 @@ class VerifyStack:
             base = qkv.data_ptr()
             k_ptr = base + nq_f * esz
             v_ptr = None if ly.k_is_v else base + (nq_f + nk_f) * esz
-            o = self.o.view(-1)[:self.R * nq_f].view(self.R, nq_f)
+            o = self._act_view(self.o, nq_f)
             t = self._ev(f"L{i}.attn", stream)
             L.sv_verify_attn(desc, base, k_ptr, v_ptr, cache["k"], cache["v"], self.cache_len, o,
                              self.attn_ws, self.dev_status, stream)
@@ -250,7 +264,7 @@ class VerifyStack:
                 pending = self._residual(self.f, lw["wd"], stream)
                 self._end(t)
         t = self._ev("final_norm", stream)
-        h = self._norm(self.x, self.h, stream, pending)
+        h = self._norm(self.x, self.h, stream, pending, odt=self.dt)
         self._end(t)
         return h
 

@@ -183,11 +183,11 @@ def test_split_partial_inputs(kind):
 
 @gpu
 @pytest.mark.parametrize("kind", ["local", "global"])
-def test_fp32_activation_inputs(kind):
-    """act_f32: q, k_new, v_new as fp32 (K-split partials or their fp32 sum) and an
-    fp32 output.  The split and the summed forms give identical bits; the result
-    matches the oracle fed the same fp32 values (no bf16 rounding before RoPE; the
-    new rows rounded to bf16 when stored)."""
+def test_pair_activation_inputs(kind):
+    """act_pair: q, k_new, v_new as fp32 (K-split partials or their fp32 sum) and the
+    output as a bf16 pair.  The split and the summed forms give identical bits; the
+    result matches the oracle fed the same fp32 values (no bf16 rounding before RoPE;
+    the new rows rounded to bf16 when stored)."""
     dev = need_gpu()
     ly = configs.local_layer(16, 8, 256, 64) if kind == "local" else configs.global_layer(16, 4, 512)
     B, nq, S, cap = 3, 5, 4, 700
@@ -211,9 +211,9 @@ def test_fp32_activation_inputs(kind):
         vp = None if ly.k_is_v else base + (Hq + Hkv) * D * 4
         kc = kc0.clone()
         vc = None if vc0 is None else vc0.clone()
-        out = torch.full((B, nq, Hq, D), float("nan"), dtype=torch.float32, device=dev)
+        out = torch.full((2, B, nq, Hq, D), float("nan"), dtype=torch.bfloat16, device=dev)
         desc = attn_desc(ly, B, nq, cap, "bf16", q_row_stride=nout, kv_row_stride=nout,
-                         in_splits=S if split else 0, act_f32=True)
+                         in_splits=S if split else 0, act_pair=True)
         ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
         L.sv_verify_attn(desc, base, kp, vp, kc, vc, lt, out, ws, None)
         outs.append(out)
@@ -227,7 +227,7 @@ def test_fp32_activation_inputs(kind):
     q = ah[:, :, :Hq * D].reshape(B, nq, Hq, D)
     kn = ah[:, :, Hq * D:(Hq + Hkv) * D].reshape(B, nq, Hkv, D)
     vn = None if ly.k_is_v else ah[:, :, (Hq + Hkv) * D:].reshape(B, nq, Hkv, D)
-    outh = host(outs[0])
+    outh = host(outs[0][0]).astype(np.float64) + host(outs[0][1]).astype(np.float64)
     for b in range(B):
         got, want = [], []
         for g in range(Hkv):

@@ -152,34 +152,47 @@ def test_split_partials(R, K, N):
     assert torch.equal(y, y2), "repeat call differs"
 
 
-def f32_linear_bound(xh, W, K, extra_terms=2):
-    """fp32 activations: x enters the product as hi + lo with |x - hi - lo| <= 2^-16 |x|,
-    and the 2K exact bf16 products are summed in fp32 (any order): the result is within
-    (2^-16 + 2K 2^-24) sum |x w| of x W^T."""
+def pair_of(x):
+    """[2, ...] bf16 planes hi = bf16(x), lo = bf16(x - hi) of an fp32 tensor (torch's
+    round-to-nearest-even conversions)."""
+    hi = x.to(torch.bfloat16)
+    lo = (x - hi.float()).to(torch.bfloat16)
+    return torch.stack([hi, lo])
+
+
+def pair_value(y):
+    return host(y[0]).astype(np.float64) + host(y[1]).astype(np.float64)
+
+
+def pair_linear_bound(xh, W, K):
+    """Pair activations: hi + lo is within 2^-16 |x| of the fp32 x, and the 2K exact bf16
+    products are summed in fp32 (any order): the result is within (2^-16 + 2K 2^-24)
+    sum |x w| of x W^T."""
     mag = oracle.linear(np.abs(xh), np.abs(host(W)))
-    return (2.0 ** -16 + extra_terms * K * 2.0 ** -24) * mag + 1e-30
+    return (2.0 ** -16 + 2 * K * 2.0 ** -24) * mag + 1e-30
 
 
 @gpu
 @pytest.mark.parametrize("R,K,N,epi", [(40, 3840, 8192, L.SV_EPI_STORE), (20, 15360, 3840, L.SV_EPI_ADD_F32),
                                        (5, 96, 192, L.SV_EPI_STORE), (64, 4096 + 32, 320, L.SV_EPI_ADD_F32),
                                        (17, 256, 1024, L.SV_EPI_STORE)])
-def test_fp32_activations(R, K, N, epi):
-    """act_f32: fp32 x (full fp32 mantissas) against the oracle's fp64 x W^T; STORE
-    writes fp32."""
+def test_pair_activations(R, K, N, epi):
+    """act_pair: x given as the bf16 pair of an fp32 activation, against the oracle's
+    fp64 product of the fp32 x; STORE writes fp32."""
     dev = need_gpu()
-    say(f"[linear f32-act] R={R} K={K} N={N} epi={epi}")
-    x = inputs.normal((R, K), 1.0, 15, "xf", dev, "f32")
+    say(f"[linear pair] R={R} K={K} N={N} epi={epi}")
+    xf = inputs.normal((R, K), 1.0, 15, "xf", dev, "f32")
+    x = pair_of(xf)
     W = inputs.normal((N, K), K ** -0.5, 15, "W", dev)
-    desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_f32=1)
+    desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_pair=1)
     ws = torch.zeros(L.sv_linear_workspace(desc), dtype=torch.uint8, device=dev)
     y0 = inputs.normal((R, N), 1.0, 15, "y0", dev, "f32") if epi == L.SV_EPI_ADD_F32 else None
     y = y0.clone() if y0 is not None else torch.full((R, N), float("nan"), dtype=torch.float32, device=dev)
     L.sv_linear(desc, x, W, y, ws)
     torch.cuda.synchronize()
-    xh = host(x)
+    xh = host(xf)
     ref = oracle.linear(xh, inputs.bf16_bits(W))
-    bound = f32_linear_bound(xh, W, K)
+    bound = pair_linear_bound(xh, W, K)
     if y0 is not None:
         ref = ref + host(y0).astype(np.float64)
     bound = bound + 2.0 ** -23 * np.abs(ref)  # the fp32 store (and add)
@@ -187,63 +200,63 @@ def test_fp32_activations(R, K, N, epi):
     assert np.all(np.isfinite(got))
     err = np.abs(got - ref)
     assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
-    # a bf16 product of the rounded x would be off by ~2^-9 sum|x w|: the lo half counts
-    say(f"[linear f32-act] ok, max err/bound {float((err / bound).max()):.3f}")
+    say(f"[linear pair] ok, max err/bound {float((err / bound).max()):.3f}")
 
 
 @gpu
 @pytest.mark.parametrize("R,K,N", [(40, 15360, 3840), (7, 96, 192), (33, 8192 + 32, 640)])
-def test_fp32_activations_split(R, K, N):
+def test_pair_activations_split(R, K, N):
     dev = need_gpu()
     desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=L.SV_EPI_SPLIT_F32,
-                        act_f32=1)
+                        act_pair=1)
     S = L.sv_linear_splits(desc)
-    say(f"[linear f32-act split] R={R} K={K} N={N} S={S}")
-    x = inputs.normal((R, K), 1.0, 16, "xf", dev, "f32")
+    say(f"[linear pair split] R={R} K={K} N={N} S={S}")
+    xf = inputs.normal((R, K), 1.0, 16, "xf", dev, "f32")
     W = inputs.normal((N, K), K ** -0.5, 16, "W", dev)
     y = torch.full((S, R, N), float("nan"), dtype=torch.float32, device=dev)
-    L.sv_linear(desc, x, W, y, None)
+    L.sv_linear(desc, pair_of(xf), W, y, None)
     torch.cuda.synchronize()
     got = host(y)
     assert np.all(np.isfinite(got)), "a slice was left unwritten"
     total = got[0].astype(np.float64)
     for s in range(1, S):
         total = (total.astype(np.float32) + got[s]).astype(np.float64)
-    xh = host(x)
+    xh = host(xf)
     ref = oracle.linear(xh, inputs.bf16_bits(W))
-    bound = f32_linear_bound(xh, W, K) + S * 2.0 ** -24 * oracle.linear(np.abs(xh), np.abs(host(W)))
+    bound = pair_linear_bound(xh, W, K) + S * 2.0 ** -24 * oracle.linear(np.abs(xh), np.abs(host(W)))
     err = np.abs(total - ref)
     assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
 
 
 @gpu
 @pytest.mark.parametrize("R,K,dff", [(40, 3840, 15360), (7, 96, 64)])
-def test_fp32_activations_geglu(R, K, dff):
-    """act_f32 GeGLU: gelu_tanh(g) * u from the fp32 g and u, stored fp32, against
-    the oracle's exact product.  Bound: the g, u errors of the fp32-activation
-    product, gelu_tanh's slope below 1.13, and 2^-20 relative for the fp32
-    evaluation of gelu_tanh and the product."""
+def test_pair_activations_geglu(R, K, dff):
+    """act_pair GeGLU: gelu_tanh(g) * u from the fp32 g and u, stored as a bf16 pair,
+    against the oracle's exact product.  Bound: the g, u errors of the pair product,
+    gelu_tanh's slope below 1.13, 2^-20 relative for the fp32 evaluation of gelu_tanh
+    and the product, and 2^-16 for the pair store."""
     dev = need_gpu()
     from mtp_draft_verification_amd.step import interleave_gate_up
-    say(f"[linear f32-act geglu] R={R} K={K} d_ff={dff}")
-    x = inputs.normal((R, K), 1.0, 17, "xf", dev, "f32")
+    say(f"[linear pair geglu] R={R} K={K} d_ff={dff}")
+    xf = inputs.normal((R, K), 1.0, 17, "xf", dev, "f32")
     Wgu = inputs.normal((2 * dff, K), K ** -0.5, 17, "Wgu", dev)
     desc = L.LinearDesc(rows=R, in_features=K, out_features=2 * dff, dtype=L.SV_BF16, epilogue=L.SV_EPI_GEGLU,
-                        act_f32=1)
+                        act_pair=1)
     ws = torch.zeros(L.sv_linear_workspace(desc), dtype=torch.uint8, device=dev)
-    f = torch.full((R, dff), float("nan"), dtype=torch.float32, device=dev)
-    L.sv_linear(desc, x, interleave_gate_up(Wgu), f, ws)
+    f = torch.full((2, R, dff), float("nan"), dtype=torch.bfloat16, device=dev)
+    L.sv_linear(desc, pair_of(xf), interleave_gate_up(Wgu), f, ws)
     torch.cuda.synchronize()
-    xh = host(x)
+    xh = host(xf)
     GU = oracle.linear(xh, inputs.bf16_bits(Wgu))
-    e = f32_linear_bound(xh, Wgu, K)
+    e = pair_linear_bound(xh, Wgu, K)
     G, U = GU[:, :dff], GU[:, dff:]
     ref = oracle.geglu(G, U)
     dg, du = e[:, :dff], e[:, dff:]
     gel = np.abs(oracle.geglu(G, np.ones_like(G)))
-    bound = 1.13 * dg * (np.abs(U) + du) + gel * du + 2.0 ** -20 * (np.abs(G) + 1) * np.abs(U) + 1e-30
-    got = host(f)
+    bound = (1.13 * dg * (np.abs(U) + du) + gel * du + 2.0 ** -20 * (np.abs(G) + 1) * np.abs(U)
+             + 2.0 ** -16 * np.abs(ref) + 1e-30)
+    got = pair_value(f)
     assert np.all(np.isfinite(got))
     err = np.abs(got - ref)
     assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
-    say(f"[linear f32-act geglu] ok, max err/bound {float((err / bound).max()):.3f}")
+    say(f"[linear pair geglu] ok, max err/bound {float((err / bound).max()):.3f}")

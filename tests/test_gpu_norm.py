@@ -63,3 +63,34 @@ def test_add_rmsnorm(R, d, S, gain):
     bnd = norm_bound(ref, d, True)
     assert np.all(err <= bnd), f"norm: worst excess {(err - bnd).max():.3e}"
     say(f"[add_norm] ok, max err/bound {float((err / bnd).max()):.3f}")
+
+
+def pair_value(y):
+    """The value a bf16 pair [2, ...] holds: hi + lo (exact in fp64)."""
+    return host(y[0]).astype(np.float64) + host(y[1]).astype(np.float64)
+
+
+@gpu
+@pytest.mark.parametrize("R,d,S", [(40, 3840, 8), (5, 100, 0), (3, 8192, 2)])
+def test_norms_pair_output(R, d, S):
+    """SV_BF16X2 output: plane 0 holds bf16(y), plane 1 bf16(y - plane 0); their sum is
+    within 2^-16 |y| of the fp32 result, so the bound is the fp32 one plus 2^-16."""
+    dev = need_gpu()
+    say(f"[norm pair] R={R} d={d} S={S}")
+    x = inputs.normal((R, d), 1.5, 3, "x", dev, "f32")
+    if d % 4 == 0:
+        parts = inputs.normal((S, R, d), 0.5, 3, "parts", dev, "f32") if S else None
+        y = torch.full((2, R, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        L.sv_add_rmsnorm(R, d, EPS, x, parts, S, None, y, L.SV_BF16X2)
+    else:
+        y = torch.full((2, R, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        L.sv_rmsnorm(R, d, EPS, x, None, y, L.SV_BF16X2)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(host(x), EPS)
+    got = pair_value(y)
+    bnd = ((d / 2 + 4) * 2.0 ** -24 + 2.0 ** -16) * np.abs(ref) + 1e-30
+    err = np.abs(got - ref)
+    assert np.all(err <= bnd), f"worst excess {(err - bnd).max():.3e}"
+    # plane 0 is the bf16 rounding of the fp32 result: |hi - y| <= 2^-8 |y|
+    hi = host(y[0]).astype(np.float64)
+    assert np.all(np.abs(hi - ref) <= (2.0 ** -8 + d * 2.0 ** -24) * np.abs(ref) + 1e-30)
