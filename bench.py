@@ -53,7 +53,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--ctx", type=int, default=131072)
-    ap.add_argument("--sweep", default="1,4", help="extra batch sizes, comma separated ('' for none)")
+    ap.add_argument("--sweep", default="1,2,4,8", help="batch sizes of the sweep, comma separated ('' for none)")
+    ap.add_argument("--sweep-k", default="3,4", help="draft counts of the sweep, comma separated")
+    ap.add_argument("--no-configs", action="store_true", help="skip the standalone workload lines")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for profilers: no sweep, no oracle")
@@ -61,7 +63,7 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="time calls of the step in isolation at the workload's shapes; comma-separated "
                          f"from {', '.join(ONLY_CALLS)}")
-    ap.add_argument("--iters", type=int, default=50, help="iterations of --only")
+    ap.add_argument("--iters", type=int, default=100, help="iterations of --only and of the workload lines")
     return ap.parse_args()
 
 
@@ -546,6 +548,194 @@ def bench_drafter(cfg, W, caches, lens, dev, cycles: int = 10, warmup: int = 2) 
     return out
 
 
+def host_cpu() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed(call, iters, warm=3) -> float:
+    """Mean microseconds per call over `iters` back-to-back calls on the current
+    stream (HIP events), after `warm` untimed calls."""
+    import torch
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(iters):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def _rate(byts, us):
+    gbs = byts / (us * 1e-6) / 1e9
+    return {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def bench_configs(args) -> dict:
+    """Standalone lines for the other workloads, each call timed alone (`iters`
+    back-to-back calls after warm-up, HIP events), inputs generated as the parity
+    tests generate them:
+      tiny_f32_verify    -- the one-layer fp32 step (d=128, 2q/1kv, D=64, 64 cached
+                            tokens, k=3, vocab 1024): latency only;
+      local_attn_verify  -- B=1, 16q/8kv, D=256, L=4096, W=1024, k=4 (bf16);
+      global_attn_verify -- B=8, 32q/4kv, D=512, K=V, p-RoPE, L ~ U[8192, 32768],
+                            k=4, over a bf16 and over an fp8 cache;
+      lmhead_select_b1 / _b8 -- V=262,144, d=3840, k=4: the greedy select; a
+                            sampling step done two ways: two-pass (pass 1 with the
+                            bonus draw, accept, the residual pass) and single-pass
+                            (pass 1 with four candidates per draft row, accept,
+                            and the residual pass only for a sequence that refuses
+                            all four), drafter rows q ~ Dirichlet(0.1)."""
+    import numpy as np
+    import torch
+
+    from mtp_draft_verification_amd import _lib as L
+    from mtp_draft_verification_amd import configs, inputs
+    from mtp_draft_verification_amd.step import VerifyStack, attn_desc
+
+    dev = torch.device("cuda:0")
+    it = args.iters
+    out = {}
+
+    # tiny fp32 step
+    cfg = configs.TINY_F32
+    W = inputs.stack_weights(cfg, 0, dev)
+    caches = inputs.stack_caches(cfg, 0, dev, capacity=cfg.ctx + 16)
+    cl = torch.full((1,), cfg.ctx, dtype=torch.int32, device=dev)
+    vs = VerifyStack(cfg, W, caches, cl, dev)
+    tok = inputs.randint((1, cfg.k + 1), 0, cfg.vocab - 1, 0, "tok", dev)
+    dr = tok[:, 1:].contiguous()
+
+    def tiny():
+        cl.fill_(cfg.ctx)
+        vs.step(tok, dr)
+    out["tiny_f32_verify"] = {"us_per_step": round(_timed(tiny, it), 2),
+                              "note": "one verify step (embedding, attention with append, output projection, "
+                                      "LM head, accept) launched call by call; latency only"}
+    del vs, W, caches
+
+    # verify attention workloads
+    def attn_line(acfg, fp8):
+        ly = acfg.layer
+        B, nq = acfg.batch, acfg.k + 1
+        a = inputs.attn_inputs(acfg, 0, dev)
+        cap = a["cap"]
+        desc = attn_desc(ly, B, nq, cap, "bf16")
+        ws = torch.empty(L.sv_verify_attn_workspace(desc), dtype=torch.uint8, device=dev)
+        out_t = torch.empty_like(a["q"])
+        lens = a["cache_len"].cpu().numpy()
+        keys = sum(min(int(l) + nq, ly.window + acfg.k) if ly.window else int(l) + nq for l in lens)
+        tensors = 1 if ly.k_is_v else 2
+        qio = B * nq * ly.n_heads_q * ly.head_dim * 2 * 2 + B * nq * ly.n_heads_kv * ly.head_dim * 2 * tensors
+        if fp8:
+            ks = inputs.channel_scales((ly.n_heads_kv, ly.head_dim), acfg.std, 0, "ks", dev)
+            kc = inputs.fp8_codes(tuple(a["k_cache"].shape), acfg.std, ks, 0, "kc8", dev)
+            vsc = None if ly.k_is_v else ks.clone()
+            vc = None if ly.k_is_v else kc.clone()
+            call = lambda: L.sv_verify_attn_fp8(desc, a["q"], a["k_new"], a["v_new"], kc, vc, ks, vsc,
+                                                a["cache_len"], out_t, ws)
+            byts = keys * ly.n_heads_kv * ly.head_dim * 1 * tensors + qio
+        else:
+            call = lambda: L.sv_verify_attn(desc, a["q"], a["k_new"], a["v_new"], a["k_cache"], a["v_cache"],
+                                            a["cache_len"], out_t, ws)
+            byts = keys * ly.n_heads_kv * ly.head_dim * 2 * tensors + qio
+        us = _timed(call, it)
+        res = {"us_per_call": round(us, 2), "alg_bytes": int(byts), **_rate(byts, us),
+               "positions_per_s": round(B * nq / (us * 1e-6), 1)}
+        del a
+        return res
+
+    out["local_attn_verify"] = attn_line(configs.LOCAL_ATTN, False)
+    out["local_attn_verify"]["note"] = ("8.42 MB per call is below what one launch can stream at peak "
+                                        "(bandwidth x latency): latency-bound")
+    out["global_attn_verify"] = attn_line(configs.GLOBAL_ATTN, False)
+    out["global_attn_verify_fp8"] = attn_line(configs.GLOBAL_ATTN, True)
+    torch.cuda.empty_cache()
+
+    # LM head select, greedy and sampling
+    for lcfg in (configs.LMHEAD_B1, configs.LMHEAD_B8):
+        B, k, d, V = lcfg.batch, lcfg.k, lcfg.d_model, lcfg.vocab
+        R = B * (k + 1)
+        h = inputs.normal((R, d), 1.0, 0, "h", dev)
+        Wt = inputs.normal((V, d), d ** -0.5, 0, "W", dev)
+        wbytes = V * d * 2 + R * d * 2
+        drafts_g = inputs.randint((B, k), 0, V - 1, 0, "drafts", dev)
+        gdesc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=L.SV_SELECT_GREEDY, dtype=L.SV_BF16)
+        ws = torch.zeros(max(L.sv_lmhead_workspace(gdesc),
+                             L.sv_lmhead_workspace(L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V,
+                                                                mode=L.SV_SELECT_SAMPLE_RS, dtype=L.SV_BF16))),
+                         dtype=torch.uint8, device=dev)
+        stats = torch.empty((R, L.ROW_STATS_WORDS), dtype=torch.int32, device=dev)
+        us_g = _timed(lambda: L.sv_lmhead_select(gdesc, h, Wt, drafts_g, None, None, stats, None, None, ws), it)
+        line = {"greedy": {"us_per_call": round(us_g, 2), "alg_bytes": int(wbytes), **_rate(wbytes, us_g),
+                           "positions_per_s": round(R / (us_g * 1e-6), 1)}}
+        # sampling inputs: drafter rows q ~ Dirichlet(0.1), drafts ~ q, uniforms
+        q_rows = inputs.dirichlet_rows(B * k, V, lcfg.dirichlet_alpha, 0, "q", dev).view(B, k, V)
+        drafts = inputs.categorical(q_rows.view(B * k, V), 0, "drafts").view(B, k)
+        u_acc = inputs.uniform((B, k), 0, "u_acc", dev)
+        u_tok = inputs.uniform((B, V), 0, "u_tok", dev)
+        u_rs = inputs.uniform((B, L.RS_CANDIDATES), 0, "u_rs", dev)
+        sdesc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=L.SV_SELECT_SAMPLE, dtype=L.SV_BF16)
+        rdesc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=L.SV_SELECT_RESIDUAL, dtype=L.SV_BF16)
+        xdesc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=V, mode=L.SV_SELECT_SAMPLE_RS, dtype=L.SV_BF16)
+        adesc = L.AcceptDesc(batch=B, k=k, vocab=V, mode=L.SV_SELECT_SAMPLE)
+        xadesc = L.AcceptDesc(batch=B, k=k, vocab=V, mode=L.SV_SELECT_SAMPLE_RS)
+        cl = torch.zeros((B,), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        acc = torch.zeros((B, L.ACCEPT_OUT_WORDS), dtype=torch.int32, device=dev)
+        cands = torch.empty((B * k * L.RS_CANDIDATES, L.RS_CAND_WORDS), dtype=torch.int32, device=dev)
+
+        def two_pass():
+            L.sv_lmhead_select(sdesc, h, Wt, drafts, u_tok, None, stats, None, None, ws)
+            L.sv_accept(adesc, drafts, stats, q_rows, u_acc, cl, toks, acc)
+            L.sv_lmhead_select(rdesc, h, Wt, drafts, u_tok, q_rows, stats, acc, toks, ws)
+        us_two = _timed(two_pass, it)
+        n_two = L.decode_accept_out(acc)["n_accepted"]
+        key = [0]
+
+        def one_pass():
+            key[0] += 1
+            L.sv_lmhead_select_rs(xdesc, h, Wt, drafts, u_tok, key[0], 7, stats, cands, None, ws)
+            L.sv_accept_rs(xadesc, drafts, stats, cands, q_rows, u_acc, u_rs, cl, toks, acc)
+        us_one = _timed(one_pass, it)
+        us_res = _timed(lambda: L.sv_lmhead_select(rdesc, h, Wt, drafts, u_tok, q_rows, stats, acc, toks, ws), it)
+        # how often a rejecting sequence refuses all four candidates (new key per step)
+        rej = fb = 0
+        for _ in range(32):
+            one_pass()
+            a = L.decode_accept_out(acc)
+            rej += int((a["n_accepted"] < k).sum())
+            fb += int((a["residual_row"] >= 0).sum())
+        p_step = 1.0 - (1.0 - fb / max(rej, 1)) ** max(1, int(round(rej / 32)))  # a step needs pass 2
+        line["sampling"] = {
+            "two_pass_us_per_step": round(us_two, 2),
+            "single_pass_us_first_pass_and_accept": round(us_one, 2),
+            "residual_pass_us": round(us_res, 2),
+            "rejecting_sequences_per_step": round(rej / 32, 2),
+            "candidates_all_refused_fraction": round(fb / max(rej, 1), 4),
+            "single_pass_expected_us_per_step": round(us_one + p_step * us_res, 2),
+            "two_pass_n_accepted": n_two.tolist(),
+            "note": "two-pass always launches the residual pass (graph-friendly); the single-pass step "
+                    "launches it only when some rejecting sequence refused all four candidates, with the "
+                    "probability measured over 32 steps"}
+        out[lcfg.name] = line
+        del h, Wt, q_rows, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, W, caches, tokens, lens, dev):
     """Time the oracle on a bounded sample: one verify step of sequence 0."""
     import numpy as np
@@ -591,7 +781,7 @@ def cpu_baseline(cfg, W, caches, tokens, lens, dev):
     dt1 = time.perf_counter() - t0
     oracle.set_threads(cores)
     return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
-                single_thread_value=n / dt1,
+                single_thread_value=n / dt1, cpu_model=host_cpu(), host_threads=os.cpu_count(),
                 sample=f"one verify step of sequence 0 ({cfg.k + 1} rows, all 6 layers, LM head, accept) "
                        f"of the same workload at its first recorded step: {n} tokens committed in {dt:.1f} s "
                        f"on {cores} threads, {dt1:.1f} s on one")
@@ -678,16 +868,29 @@ def main():
     log(f"B={cfg.batch}: {main_res['tokens_per_s']:.1f} tokens/s, {main_res['ms_per_step']:.3f} ms/step, "
         f"mean accepted {main_res['mean_accepted']:.2f}")
 
-    sweep = {f"B{cfg.batch}": round(main_res["tokens_per_s"], 1)}
-    for b in [int(x) for x in args.sweep.split(",") if x.strip()]:
-        if b == cfg.batch:
-            continue
-        c2 = dataclasses.replace(cfg, batch=b)
-        r = run_workload(c2, W, args.steps, args.warmup, args.seed, dev)
-        sweep[f"B{b}"] = round(r["tokens_per_s"], 1)
-        log(f"B={b}: {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step")
-        del r
-        torch.cuda.empty_cache()
+    # the sweep: k x batch, each point the same protocol as the main line
+    sweep = {}
+    for kk in [int(x) for x in args.sweep_k.split(",") if x.strip()]:
+        row = {}
+        for b in [int(x) for x in args.sweep.split(",") if x.strip()]:
+            if (kk, b) == (cfg.k, cfg.batch):
+                row[f"B{b}"] = {"tokens_per_s": round(main_res["tokens_per_s"], 1),
+                                "ms_per_step": round(main_res["ms_per_step"], 4),
+                                "mean_accepted": round(main_res["mean_accepted"], 3)}
+                continue
+            c2 = dataclasses.replace(cfg, batch=b, k=kk)
+            r = run_workload(c2, W, args.steps, args.warmup, args.seed, dev)
+            row[f"B{b}"] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                            "mean_accepted": round(r["mean_accepted"], 3)}
+            log(f"k={kk} B={b}: {r['tokens_per_s']:.1f} tokens/s, {r['ms_per_step']:.3f} ms/step")
+            del r
+            torch.cuda.empty_cache()
+        sweep[f"k{kk}"] = row
+
+    config_lines = None
+    if not args.no_configs and not args.profile:
+        config_lines = bench_configs(args)
+        log("workload lines: " + ", ".join(config_lines))
 
     dom = main_res["dominant"]
     dom_bytes = main_res["call_bytes"][dom]
@@ -731,7 +934,8 @@ def main():
                    "vocab": cfg.vocab, "layers": "LLLLLG"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "sweep_tokens_per_s": sweep,
+        "sweep": sweep,
+        "workload_lines": config_lines,
         "mean_accepted": round(main_res["mean_accepted"], 3),
         "step_ms_p10_p50_p90": main_res["step_ms_p10_p50_p90"],
         "step_launch": main_res["step_launch"],

@@ -598,7 +598,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       // 1.5 % faster with bf16 keys, 9 % with fp8); otherwise the pairs go in
       // row-tile-major order, MT consecutive pairs per wave, and a wave scores at most
       // two row tiles (one unless MT == 3), so it holds only those rows of the queries.
-      constexpr bool KM = MT == 2;
+      constexpr bool KM = MT == 2 || MT == 3;
       constexpr int NQ = KM ? MT : (MT == 3 ? 2 : 1);
       const int mq0 = KM ? 0 : (wave * MT) >> 2;  // the wave's first row tile
       V16 qreg[NQ][KS];
