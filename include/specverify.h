@@ -55,7 +55,10 @@ typedef enum {
 /* SV_BF16X2 (an output type of the norms): a bf16 pair, two planes [2, ...] holding
  * hi = bf16(v) and lo = bf16(v - hi) of an fp32 value v -- hi + lo is within 2^-16 |v|
  * of v, and a bf16 MFMA takes it as two operands. */
-typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_BF16X2 = 2 } sv_dtype;
+/* The input enumerations of the ABI are fixed-width integers with named values, so
+ * any value a caller passes is well defined and an unknown one is rejected. */
+typedef int32_t sv_dtype;
+enum { SV_F32 = 0, SV_BF16 = 1, SV_BF16X2 = 2 };
 
 /* device status bits */
 #define SV_DEV_CACHE_OVERFLOW 0x1  /* cache_len[b] + appended rows > cache_capacity */
@@ -188,13 +191,14 @@ int sv_verify_attn_noalloc(const sv_attn_desc* desc, const void* q, const void* 
 /* LM head + select                                                          */
 /* ------------------------------------------------------------------------ */
 
-typedef enum {
+typedef int32_t sv_select_mode;
+enum {
   SV_SELECT_GREEDY = 0,    /* per-row argmax statistics */
   SV_SELECT_SAMPLE = 1,    /* GREEDY + a Gumbel-max draw from softmax(z) on bonus rows */
   SV_SELECT_RESIDUAL = 2,  /* draw from max(p - q, 0) for sequences that rejected */
   SV_SELECT_SAMPLE_RS = 3  /* SAMPLE + first-pass candidates for single-pass sampling
                               (sv_lmhead_select_rs, sv_accept_rs) */
-} sv_select_mode;
+};
 
 /* Per-row result of the LM head (logits themselves are never written). */
 typedef struct {
@@ -431,7 +435,8 @@ int sv_draft_input(int32_t batch, int32_t d_main, int32_t d_draft, float eps, co
 int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, const float* parts, int32_t splits,
                    const float* gain, void* y, sv_dtype out_dtype, void* stream);
 
-typedef enum {
+typedef int32_t sv_epilogue;
+enum {
   SV_EPI_STORE = 0,      /* y = x W^T stored in the descriptor dtype */
   SV_EPI_ADD_F32 = 1,    /* y (fp32) += x W^T: a residual add */
   SV_EPI_GEGLU = 2,      /* bf16 only: the GeGLU gate fused into the gate/up projection.
@@ -447,7 +452,7 @@ typedef enum {
                             sum over s in slice order is x W^T.  For a consumer that adds
                             the slices itself (sv_add_rmsnorm); the call needs no workspace
                             and writes every element of y. */
-} sv_epilogue;
+};
 
 typedef struct {
   int32_t rows;          /* R <= 64 */

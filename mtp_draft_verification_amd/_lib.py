@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspecverify.so")
+# SV_LIBRARY: another build of the library to load (e.g. one with host-side sanitizers)
+LIB_PATH = os.environ.get("SV_LIBRARY") or os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, SV_ERR_DEVICE, SV_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
 SV_NOALLOC_SCRATCH_BYTES = 32 << 20

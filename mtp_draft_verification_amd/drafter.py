@@ -100,7 +100,10 @@ class Drafter:
         self._attn = {}
         ws = max(L.sv_verify_attn_workspace(self._attn_desc(j, 0)) for j in range(len(self.reads)))
         self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
-        self.lm_ws = None
+        # the greedy unembed's workspace (its size does not depend on out_stride)
+        lm_desc = L.LMHeadDesc(batch=B, k=0, d_model=d, vocab=target_cfg.vocab, mode=L.SV_SELECT_GREEDY,
+                               dtype=L.SV_BF16, out_stride=1)
+        self.lm_ws = torch.zeros(max(256, L.sv_lmhead_workspace(lm_desc)), dtype=torch.uint8, device=dev)
         self.drafts = None
         # clustered unembedding: {"perm", "w_perm", "centroids", "top"} (None: full vocabulary)
         self.clusters = clusters
@@ -192,8 +195,6 @@ class Drafter:
             return
         desc = L.LMHeadDesc(batch=B, k=0, d_model=d, vocab=t.vocab, mode=L.SV_SELECT_GREEDY, dtype=L.SV_BF16,
                             out_stride=k)
-        if self.lm_ws is None:
-            self.lm_ws = torch.zeros(max(256, L.sv_lmhead_workspace(desc)), dtype=torch.uint8, device=self.dev)
         L.sv_lmhead_select(desc, self.h, self.E, None, None, None, self.stats, None, drafts.data_ptr() + 4 * i,
                            self.lm_ws, stream)
         self._end(tok)

@@ -19,6 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "svoracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# another build of svoracle.c to load instead (the sanitizer test's ASan/UBSan build)
+_LIB_OVERRIDE = os.environ.get("SVO_ORACLE_LIB")
 
 _lib = None
 
@@ -58,9 +60,12 @@ class Stats(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         L.svo_num_threads.restype = ctypes.c_int
