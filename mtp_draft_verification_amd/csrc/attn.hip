@@ -577,7 +577,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
             if (key > a1 - 1) key = a1 - 1;
             off = (uint32_t)((key - brow) * ROWB + (((lane % CPR) ^ swz(row)) << 4));
           }
-          dma16((const void*)(tbase + (head_row0 + brow) * ROWB), off, lds);
+          dma16<true, true>((const void*)(tbase + (head_row0 + brow) * ROWB), off, lds);
         }
       };
       auto issue = [&](int t, unsigned char* stage) __attribute__((always_inline)) {
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
                   const int ten = ii / (TK / RPI);
                   const int rb = ii % (TK / RPI);
                   const unsigned char* tbase = (KV_SAME || ten == 0) ? kcache : vcache;
-                  dma16<false>((const void*)(tbase + (head_row0 + tn0 + rb * RPI) * ROWB), off_pre[jj],
+                  dma16<false, true>((const void*)(tbase + (head_row0 + tn0 + rb * RPI) * ROWB), off_pre[jj],
                                lds_addr(nstage + ten * TILEB + rb * RPI * ROWB));
                 }
               }

@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
     const uint32_t dst = ring_lds + (uint32_t)(s * C::STAGEB);
 #pragma unroll
     for (int i = 0; i < C::WI; ++i)
-      dma16(wb, woff[i] - (tail ? adj[i & 1] : 0u), dst + (uint32_t)((wave * C::WI + i) * 1024));
+      dma16<true, true>(wb, woff[i] - (tail ? adj[i & 1] : 0u), dst + (uint32_t)((wave * C::WI + i) * 1024));
     const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * 128;
 #pragma unroll
     for (int ii = 0; ii < C::NX; ++ii) dma16(xb, xoff[ii] - (tail ? xadj[ii] : 0u), dst + xlds[ii]);
