@@ -15,6 +15,8 @@
 #include "sv_device.h"
 #include "sv_host.h"
 
+#include <type_traits>
+
 namespace sv {
 
 enum GemmMode : int { GM_GREEDY = 0, GM_SAMPLE = 1, GM_RESIDUAL = 2, GM_STORE_BF16 = 3, GM_ADD_F32 = 4, GM_GEGLU = 5,
@@ -565,17 +567,17 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
         if constexpr (SELECT) {
           select_push4<MODE>(st[mt], ctx[mt], z, v0);
         } else if constexpr (MODE == GM_GEGLU) {
-          // tile 0 holds the gate, tile 1 the up projection of the same 16 features
-          // (weights interleaved by 16 rows).  bf16 activations: both pass through bf16
+          // tile t - 1 holds the gate, tile t (odd) the up projection of the same 16
+          // features (weights interleaved by 16 rows).  bf16 activations: both pass through bf16
           // as stored values and the product is stored bf16; pair activations (XF): the
           // product of the fp32 gate and up values is stored as a bf16 pair (hi plane,
           // lo plane [2, R, N/2])
-          if (t == 1 && r < nx) {
-            const int c0 = row0 / 2 + lg * 4;
+          if ((t & 1) && r < nx) {
+            const int c0 = (row0 + 16 * (t - 1)) / 2 + lg * 4;
             if constexpr (XF) {
               float f[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) f[e] = gelu_tanh(acc[0][mt][e]) * acc[1][mt][e];
+              for (int e = 0; e < 4; ++e) f[e] = gelu_tanh(acc[t - 1][mt][e]) * acc[t][mt][e];
               uint16_t* y = (uint16_t*)p.y + (int64_t)r * (p.N / 2) + c0;
               const uint32_t h01 = pack_bf16x2(f[0], f[1]), h23 = pack_bf16x2(f[2], f[3]);
               *(uint2*)y = make_uint2(h01, h23);
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
               float f[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                f[e] = gelu_tanh(round_bf16(acc[0][mt][e])) * round_bf16(acc[1][mt][e]);
+                f[e] = gelu_tanh(round_bf16(acc[t - 1][mt][e])) * round_bf16(acc[t][mt][e]);
               *(uint2*)((uint16_t*)p.y + (int64_t)r * (p.N / 2) + c0) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
             }
           }
@@ -1605,17 +1607,17 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   p.part = (float*)((char*)workspace + pl.cnt_bytes);
   if (d->act_pair) {
     // pair activations: x read as its hi and lo bf16 planes; STORE writes fp32, GEGLU a pair
-    if (d->epilogue == SV_EPI_GEGLU)
-      rc = dispatch_ring<2, GM_GEGLU, 1>(p, d->rows, pl.grid, s);
-    else if (d->epilogue == SV_EPI_SPLIT_F32)
-      rc = pl.T == 1 ? dispatch_ring<1, GM_SPLIT, 1>(p, d->rows, pl.grid, s)
-                     : dispatch_ring<2, GM_SPLIT, 1>(p, d->rows, pl.grid, s);
-    else if (pl.T == 1)
-      rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<1, GM_STORE_F32, 1>(p, d->rows, pl.grid, s)
-                                       : dispatch_ring<1, GM_ADD_F32, 1>(p, d->rows, pl.grid, s);
-    else
-      rc = d->epilogue == SV_EPI_STORE ? dispatch_ring<2, GM_STORE_F32, 1>(p, d->rows, pl.grid, s)
-                                       : dispatch_ring<2, GM_ADD_F32, 1>(p, d->rows, pl.grid, s);
+    auto go = [&](auto tiles) {
+      constexpr int T = decltype(tiles)::value;
+      switch (d->epilogue) {
+        case SV_EPI_GEGLU: return T == 1 ? (int)SV_ERR_UNSUPPORTED : dispatch_ring<T, GM_GEGLU, 1>(p, d->rows, pl.grid, s);
+        case SV_EPI_SPLIT_F32: return dispatch_ring<T, GM_SPLIT, 1>(p, d->rows, pl.grid, s);
+        case SV_EPI_STORE: return dispatch_ring<T, GM_STORE_F32, 1>(p, d->rows, pl.grid, s);
+        default: return dispatch_ring<T, GM_ADD_F32, 1>(p, d->rows, pl.grid, s);
+      }
+    };
+    rc = pl.T == 1 ? go(std::integral_constant<int, 1>{})
+                   : pl.T == 2 ? go(std::integral_constant<int, 2>{}) : go(std::integral_constant<int, 4>{});
     if (rc != SV_OK) return rc;
     return launch_status();
   }
