@@ -225,17 +225,25 @@ __device__ __forceinline__ void select_fold(RowState& st, const RowCtx& c, const
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
 // 1, 2, 3", SC 2011): ten rounds of 32 x 32 -> 64-bit products of counter words 0
-// and 2 with the round multipliers; the key advances by the Weyl constants.
-__device__ __forceinline__ void philox4x32(uint32_t c[4], uint32_t k0, uint32_t k1) {
-#pragma unroll 1  // rolled: the callers' unrolled loops stay within the unroller's budget
+// and 2 with the round multipliers; the key advances by the Weyl constants.  NL
+// counters go through the rounds together: with one wave per SIMD nothing else
+// hides a multiply's latency, so independent chains fill it; each product is one
+// 64-bit multiply (high and low words at once).
+template <int NL>
+__device__ __forceinline__ void philox4x32(uint32_t (&c)[NL][4], uint32_t k0, uint32_t k1) {
+#pragma unroll 2  // two rounds a trip (no register rotation), the rest rolled
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const uint64_t p0 = (uint64_t)0xD2511F53u * c[l][0];
+      const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[l][2];
+      const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[l][1] ^ k0;
+      const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[l][3] ^ k1;
+      c[l][0] = n0;
+      c[l][1] = (uint32_t)p1;
+      c[l][2] = n2;
+      c[l][3] = (uint32_t)p0;
+    }
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -261,10 +269,12 @@ struct RsState {
       id[c] = -1;
     }
   }
+  // ids reach a lane's state in ascending order, so on a tie the state's (smaller)
+  // id stays: a strict compare decides, and the runner-up is max(s2, min(s1, sc))
   __device__ __forceinline__ void push(int c, float sc, int v, float zv) {
-    const bool w = beats(sc, v, s1[c], id[c]);
-    s2[c] = w ? s1[c] : fmaxf(s2[c], sc);
-    s1[c] = w ? sc : s1[c];
+    const bool w = sc > s1[c];
+    s2[c] = fmaxf(s2[c], fminf(s1[c], sc));
+    s1[c] = fmaxf(s1[c], sc);
     z[c] = w ? zv : z[c];
     id[c] = w ? v : id[c];
   }
@@ -282,23 +292,25 @@ struct RsState {
   }
 };
 
-// candidate draws over a wave tile's logits of one draft row: token v takes the
-// Philox block with counter (v, i, b, 0), word c for candidate c
-template <int T>
-__device__ __forceinline__ void rs_fold(RsState& rs, const RowCtx& c, const GemmParams& p, const f32x4_t (&z)[T],
-                                        int vbase) {
+// candidate draws over four consecutive logits z[0..3] (ids v0 + e) of one draft
+// row: token v takes the Philox block with counter (v, i, b, 0), word c for
+// candidate c
+__device__ __forceinline__ void rs_fold4(RsState& rs, const RowCtx& c, const GemmParams& p, const f32x4_t z,
+                                         int v0) {
   if (!c.valid || !c.rs) return;
+  uint32_t w[4][4];
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int e = 0; e < 4; ++e) {
+    w[e][0] = (uint32_t)(v0 + e);
+    w[e][1] = (uint32_t)c.ri;
+    w[e][2] = (uint32_t)c.rb;
+    w[e][3] = 0u;
+  }
+  philox4x32<4>(w, p.rs_key0, p.rs_key1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = vbase + t * 16 + e;
-      uint32_t w[4] = {(uint32_t)v, (uint32_t)c.ri, (uint32_t)c.rb, 0u};
-      philox4x32(w, p.rs_key0, p.rs_key1);
-      const float zv = z[t][e];
+  for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int k = 0; k < kRsCand; ++k) rs.push(k, zv + rs_gumbel(rs_uniform(w[k])), v, zv);
-    }
+    for (int k = 0; k < kRsCand; ++k) rs.push(k, z[e] + rs_gumbel(rs_uniform(w[e][k])), v0 + e, z[e]);
 }
 
 __device__ __forceinline__ void state_merge(RowState& a, const RowState& b) {
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
       wait_vm_n<0>();  // the partial stores have completed before the arrival is counted
       int old = 0;
       if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + b * 4 + wave, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __shfl(old, 0, 64);
+      old = __builtin_amdgcn_readfirstlane(old);
       const int w_lo = owner((int64_t)b * KCH), w_hi = owner((int64_t)b * KCH + KCH - 1);
       if (old != w_hi - w_lo) return;  // another workgroup finishes this slice
       asm volatile("" ::: "memory");
@@ -553,7 +565,9 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < T; ++t) zt[t] = acc[t][mt];
         select_fold<MODE, T>(st[mt], ctx[mt], zt, row0 + lg * 4);
-        if constexpr (MODE == GM_SAMPLE_RS) rs_fold<T>(rs[mt], ctx[mt], p, zt, row0 + lg * 4);
+        if constexpr (MODE == GM_SAMPLE_RS)
+#pragma unroll
+          for (int t = 0; t < T; ++t) rs_fold4(rs[mt], ctx[mt], p, zt[t], row0 + lg * 4 + t * 16);
       }
       return;
     }
