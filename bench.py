@@ -171,17 +171,25 @@ def time_one(args, only) -> dict:
         R = B * nq
         loc, glo = cfg.layers[0], cfg.layers[-1]
         nout = lambda ly: ly.n_heads_q * ly.head_dim + (1 if ly.k_is_v else 2) * ly.n_heads_kv * ly.head_dim
-        K, N, epi = {"qkv_local": (cfg.d_model, nout(loc), L.SV_EPI_STORE),
-                     "qkv_global": (cfg.d_model, nout(glo), L.SV_EPI_STORE),
-                     "o_local": (loc.n_heads_q * loc.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
-                     "o_global": (glo.n_heads_q * glo.head_dim, cfg.d_model, L.SV_EPI_ADD_F32),
-                     "gu": (cfg.d_model, 2 * cfg.d_ff, L.SV_EPI_GEGLU),
-                     "down": (cfg.d_ff, cfg.d_model, L.SV_EPI_ADD_F32)}[only]
-        # as in the stack: bf16-pair activations, bf16 weights
+        K, N, add = {"qkv_local": (cfg.d_model, nout(loc), False),
+                     "qkv_global": (cfg.d_model, nout(glo), False),
+                     "o_local": (loc.n_heads_q * loc.head_dim, cfg.d_model, True),
+                     "o_global": (glo.n_heads_q * glo.head_dim, cfg.d_model, True),
+                     "gu": (cfg.d_model, 2 * cfg.d_ff, False),
+                     "down": (cfg.d_ff, cfg.d_model, True)}[only]
+        # as in the stack: bf16-pair activations, bf16 weights, and the stack's epilogue:
+        # the fused GeGLU, else K-split fp32 partials (summed by the next call) where
+        # the split applies, else a plain fp32 store / add
         x = inputs.normal((2, R, K), 1.0, 0, "x", dev)
         W = inputs.normal((N, K), K ** -0.5, 0, "W", dev)
+        if only == "gu":
+            epi, S = L.SV_EPI_GEGLU, 0
+        else:
+            S = max(0, L.sv_linear_splits(L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16,
+                                                       epilogue=L.SV_EPI_SPLIT_F32, act_pair=1)))
+            epi = L.SV_EPI_SPLIT_F32 if S else (L.SV_EPI_ADD_F32 if add else L.SV_EPI_STORE)
         y = (torch.zeros((2, R, N // 2), dtype=torch.bfloat16, device=dev) if epi == L.SV_EPI_GEGLU
-             else torch.zeros((R, N), dtype=torch.float32, device=dev))
+             else torch.zeros((max(S, 1) * R, N), dtype=torch.float32, device=dev))
         desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_pair=1)
         ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
         # rotate over copies of W (1 GiB in all) so that, as inside the step, no call
@@ -192,7 +200,7 @@ def time_one(args, only) -> dict:
         def call():
             turn[0] += 1
             L.sv_linear(desc, x, Ws[turn[0] % len(Ws)], y, ws, stream)
-        byts = 2 * N * K + 4 * R * K + R * N * (8 if epi == L.SV_EPI_ADD_F32 else 2 if epi == L.SV_EPI_GEGLU else 4)
+        byts = 2 * N * K + 4 * R * K + R * N * (8 if add else 2 if epi == L.SV_EPI_GEGLU else 4)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -264,18 +272,30 @@ def call_bytes(cfg, lens, kv_bytes: int = 2) -> dict:
     return out
 
 
-def load_traffic(kernel_call: str) -> float | None:
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources (otherwise None)."""
+def only_call(cfg, name: str) -> str | None:
+    """The standalone (--only) call that times step call `name` at the step's shape."""
+    if name == "lmhead":
+        return "lmhead"
+    layer, _, op = name.partition(".")
+    if not layer.startswith("L") or op not in ("attn", "qkv", "o", "gu", "down"):
+        return None
+    ly = cfg.layers[int(layer[1:])]
+    kind = "global" if ly.window == 0 else "local"
+    return op if op in ("gu", "down") else f"{op}_{kind}"
+
+
+def load_traffic(call: str | None) -> float | None:
+    """HBM bytes per launch of standalone call `call` from the committed counter
+    summary, if it was taken on the current kernel sources (otherwise None)."""
     p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(p):
+    if call is None or not os.path.exists(p):
         return None
     try:
         with open(p) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = t.get("calls", {}).get(kernel_call)
+    ent = t.get("calls", {}).get(call)
     if not ent or t.get("source_digest") != source_digest():
         return None
     return float(ent["bytes_per_call"])
@@ -787,50 +807,60 @@ def cpu_baseline(cfg, W, caches, tokens, lens, dev):
                        f"on {cores} threads, {dt1:.1f} s on one")
 
 
-def pmc_summary(dirs):
-    """Write profiles/hbm_traffic.json from four rocprofv3 --pmc runs (csv output) of
-    `bench.py --only attn_global,lmhead,hbm_copy`: FETCH_SIZE, then WRITE_SIZE, each
-    scaled by what the same counter reads for the plain 1 GiB copy."""
+def pmc_summary(roots):
+    """Write profiles/hbm_traffic.json from rocprofv3 --pmc runs (csv output) of
+    `bench.py --only <call> --iters 3`, one run per call and counter:
+    roots[0]/<call>/ holds the FETCH_SIZE run, roots[1]/<call>/ the WRITE_SIZE run,
+    and <root>/<call>.json that run's own output line (for the algorithmic bytes).
+    A call's bytes: its library kernels' counter values summed over the run and
+    divided by the number of calls made (the dispatch count of its most frequent
+    kernel), each counter scaled by what it reads for the plain 1 GiB copy."""
     import csv
-    import glob
-    from collections import defaultdict
+    from collections import Counter
 
-    def per_call(d, counter):
+    def dispatches(d, counter):
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        by = defaultdict(list)  # kernel family -> per-dispatch values (KiB)
-        for r in rows:
-            n = r["Kernel_Name"]
-            fam = ("attn" if "attn_" in n or "rope_append" in n else "lmhead" if "gemm_ring" in n or "lmhead_" in n
-                   else "copy" if "copy" in n.lower() or "elementwise" in n.lower() else None)
-            if fam:
-                by[fam].append((n, float(r["Counter_Value"])))
-        return by
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+    def ours(name):
+        return name.startswith(("sv::", "void sv::"))
 
     out = {"source_digest": source_digest(), "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch)",
-           "calls": {}}
-    scale = {}
-    vals = {}
-    for key, d in (("FETCH_SIZE", dirs[0]), ("WRITE_SIZE", dirs[1])):
-        by = per_call(d, key)
-        copies = [v for n, v in by["copy"]]
-        # the copy moves COPY_BYTES each way; take the last (steady) dispatches
-        scale[key] = (COPY_BYTES / 1024) / (sum(copies[-3:]) / len(copies[-3:]))
-        vals[key] = by
-    for call, fam, per in (("L5.attn", "attn", 3), ("lmhead", "lmhead", 2)):
+           "method": "one rocprofv3 --pmc run per call and counter of bench.py --only <call> --iters 3; "
+                     "library kernels summed, divided by the calls made, scaled by the 1 GiB copy",
+           "copy_scale": {}, "calls": {}}
+    for key, root in (("FETCH_SIZE", roots[0]), ("WRITE_SIZE", roots[1])):
+        cp = [v for n, v in dispatches(os.path.join(root, "hbm_copy"), key) if not ours(n)]
+        cp = sorted(cp)[-3:]  # the copy's own dispatches are the largest
+        out["copy_scale"][key] = round((COPY_BYTES / 1024) / (sum(cp) / len(cp)), 4)
+    calls = sorted(os.path.basename(d) for d in glob.glob(os.path.join(roots[0], "*"))
+                   if os.path.isdir(d) and os.path.basename(d) != "hbm_copy")
+    for call in calls:
+        ent = {}
         tot = 0.0
-        for key in ("FETCH_SIZE", "WRITE_SIZE"):
-            v = [x for n, x in vals[key][fam]]
-            ncalls = len(v) // per
-            last = v[-per * 3:] if ncalls >= 3 else v
-            kib = sum(last) / (len(last) / per)
-            out["calls"].setdefault(call, {})[key + "_KiB_per_call_raw"] = round(kib, 1)
-            tot += kib * 1024 * scale[key]
-        out["calls"][call]["bytes_per_call"] = round(tot)
-    out["copy_scale"] = {k: round(v, 4) for k, v in scale.items()}
+        for key, root in (("FETCH_SIZE", roots[0]), ("WRITE_SIZE", roots[1])):
+            ds = [(n, v) for n, v in dispatches(os.path.join(root, call), key) if ours(n)]
+            if not ds:
+                break
+            ncalls = max(Counter(n for n, _ in ds).values())
+            kib = sum(v for _, v in ds) / ncalls
+            ent[key + "_KiB_per_call_raw"] = round(kib, 1)
+            ent["calls_counted"] = ncalls
+            tot += kib * 1024 * out["copy_scale"][key]
+        else:
+            ent["bytes_per_call"] = round(tot)
+            try:
+                with open(os.path.join(roots[0], call + ".json")) as f:
+                    alg = json.loads(f.read().strip().splitlines()[-1])["alg_bytes"]
+                ent["alg_bytes"] = alg
+                ent["traffic_over_alg"] = round(tot / alg, 4)
+            except (OSError, ValueError, KeyError, IndexError):
+                pass
+            out["calls"][call] = ent
     with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -896,7 +926,7 @@ def main():
     dom_bytes = main_res["call_bytes"][dom]
     ach = dom_bytes / (main_res["dominant_ms"] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom), "kernel": dom,
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(only_call(cfg, dom)), "kernel": dom,
             "alg_bytes_per_launch": int(dom_bytes), "mean_launch_us": round(main_res["dominant_ms"] * 1e3, 2)}
     kern = {}
     for n, ms in sorted(main_res["call_ms"].items(), key=lambda kv: -kv[1]):
@@ -905,6 +935,9 @@ def main():
         if b:
             kern[n]["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
             kern[n]["frac"] = round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
+            tr = load_traffic(only_call(cfg, n))
+            if tr:
+                kern[n]["traffic_over_alg"] = round(tr / b, 3)
 
     drafter = None
     if not args.no_drafter and not args.profile:

@@ -400,7 +400,10 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA bases live in SGPRs
   const int lr = lane & 15, lg = lane >> 4;
   const int K = p.K, KCH = p.kch, P = gridDim.x;
-  const int me = logical_wg(blockIdx.x, P);
+  // K-split slices (GM_SPLIT, workgroup me holds slice me % splits): where the slice
+  // count divides 8, the hardware numbering keeps every workgroup of an XCD on the
+  // same slice, so each XCD's L2 fetches only that slice's columns of x
+  const int me = (MODE == GM_SPLIT && 8 % p.splits == 0) ? (int)blockIdx.x : logical_wg(blockIdx.x, P);
   const int64_t tot = (int64_t)p.nblk * KCH;
   const int c_begin = (int)(tot * me / P);
   const int n_it = (int)(tot * (me + 1) / P) - c_begin;
