@@ -415,16 +415,19 @@ int sv_rmsnorm(int32_t rows, int32_t dim, float eps, const float* x, const float
  * and projects them down to its own width).  For each sequence b:
  *   h = hidden[hidden_row[b * row_stride]]           (bf16 [rows_h, d_main])
  *   e = emb_scale * emb[tokens[b * tok_stride]]       (bf16 [vocab, d_draft])
- *   cat[b] = [bf16(rmsnorm(h)), bf16(rmsnorm(e))]     (bf16 [batch, d_main + d_draft])
+ *   cat[b] = [rmsnorm(h), rmsnorm(e)]                 ([batch, d_main + d_draft] in cat_dtype:
+ *                                                     SV_BF16, or SV_BF16X2 for the pair
+ *                                                     [2, batch, d_main + d_draft] that
+ *                                                     sv_linear takes with act_pair)
  *   x[b] = 0                                          (fp32 [batch, d_draft]: the drafter's
  *                                                     residual stream, which the down
  *                                                     projection then adds into)
  * rmsnorm has unit gain.  An out-of-range row or token sets SV_DEV_BAD_TOKEN and
- * gives that part zeros. */
+ * gives that part zeros; another cat_dtype is SV_ERR_ARG. */
 int sv_draft_input(int32_t batch, int32_t d_main, int32_t d_draft, float eps, const void* hidden,
                    int32_t rows_h, const int32_t* hidden_row, int32_t row_stride, const void* emb,
                    int32_t vocab, const int32_t* tokens, int32_t tok_stride, float emb_scale, void* cat,
-                   float* x, int32_t* dev_status, void* stream);
+                   sv_dtype cat_dtype, float* x, int32_t* dev_status, void* stream);
 
 /* Residual add and RMSNorm in one launch (a pre-norm block's "x = x + f(...);
  * y = rmsnorm(x)"): x (fp32 [rows, dim], updated in place) += the sum of the
@@ -466,7 +469,9 @@ typedef struct {
                             2^-16 |v|), multiplied as hi W^T + lo W^T (two MFMAs, fp32
                             accumulation); SV_EPI_STORE writes y in fp32; SV_EPI_GEGLU writes
                             gelu_tanh(g) * u, from the fp32 g and u (no bf16 rounding), as a
-                            bf16 pair [2, R, N/2]; ADD_F32 and SPLIT_F32 are unchanged */
+                            bf16 pair [2, R, N/2]; ADD_F32 and SPLIT_F32 are unchanged.
+                            2: as 1, but SV_EPI_STORE writes y in bf16 (the fp32 result
+                            rounded once, to nearest even).  Other values: SV_ERR_ARG */
 } sv_linear_desc;
 
 /* S of SV_EPI_SPLIT_F32 for this shape on the current device (1 <= S <= the

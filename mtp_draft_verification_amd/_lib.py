@@ -119,7 +119,7 @@ def load():
     L.sv_add_rmsnorm.restype = ctypes.c_int
     L.sv_add_rmsnorm.argtypes = [i32, i32, f32, P, P, i32, P, P, ctypes.c_int, P]
     L.sv_draft_input.restype = ctypes.c_int
-    L.sv_draft_input.argtypes = [i32, i32, i32, f32, P, i32, P, i32, P, i32, P, i32, f32, P, P, P, P]
+    L.sv_draft_input.argtypes = [i32, i32, i32, f32, P, i32, P, i32, P, i32, P, i32, f32, P, i32, P, P, P]
     L.sv_linear_splits.restype = i32
     L.sv_linear_splits.argtypes = [ctypes.POINTER(LinearDesc)]
     L.sv_linear_workspace.restype = sz
@@ -272,11 +272,11 @@ def sv_add_rmsnorm(rows: int, dim: int, eps: float, x, parts, splits: int, gain,
 
 
 def sv_draft_input(batch: int, d_main: int, d_draft: int, eps: float, hidden, rows_h: int, hidden_row,
-                   row_stride: int, emb, vocab: int, tokens, tok_stride: int, emb_scale: float, cat, x,
-                   dev_status=None, stream=None) -> None:
+                   row_stride: int, emb, vocab: int, tokens, tok_stride: int, emb_scale: float, cat,
+                   cat_dtype: int, x, dev_status=None, stream=None) -> None:
     rc = load().sv_draft_input(batch, d_main, d_draft, float(eps), _ptr(hidden), rows_h, _ptr(hidden_row),
                                row_stride, _ptr(emb), vocab, _ptr(tokens), tok_stride, float(emb_scale),
-                               _ptr(cat), _ptr(x), _ptr(dev_status), _stream(stream))
+                               _ptr(cat), cat_dtype, _ptr(x), _ptr(dev_status), _stream(stream))
     _check("sv_draft_input", rc)
 
 

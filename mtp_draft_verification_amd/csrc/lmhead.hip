@@ -1319,7 +1319,7 @@ static int validate_linear(const sv_linear_desc* d) {
       d->epilogue != SV_EPI_SPLIT_F32)
     return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_SPLIT_F32 && d->dtype != SV_BF16) return SV_ERR_ARG;
-  if (d->act_pair != 0 && d->act_pair != 1) return SV_ERR_ARG;
+  if (d->act_pair < 0 || d->act_pair > 2) return SV_ERR_ARG;
   if (d->act_pair && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->out_features % 64) return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_GEGLU && (d->dtype != SV_BF16 || d->out_features % 128)) return SV_ERR_ARG;
@@ -1623,13 +1623,16 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   p.cnt = (int32_t*)workspace;
   p.part = (float*)((char*)workspace + pl.cnt_bytes);
   if (d->act_pair) {
-    // pair activations: x read as its hi and lo bf16 planes; STORE writes fp32, GEGLU a pair
+    // pair activations: x read as its hi and lo bf16 planes; STORE writes fp32 (act_pair
+    // 1) or bf16 (act_pair 2), GEGLU a pair
     auto go = [&](auto tiles) {
       constexpr int T = decltype(tiles)::value;
       switch (d->epilogue) {
         case SV_EPI_GEGLU: return T == 1 ? (int)SV_ERR_UNSUPPORTED : dispatch_ring<T, GM_GEGLU, 1>(p, d->rows, pl.grid, s);
         case SV_EPI_SPLIT_F32: return dispatch_ring<T, GM_SPLIT, 1>(p, d->rows, pl.grid, s);
-        case SV_EPI_STORE: return dispatch_ring<T, GM_STORE_F32, 1>(p, d->rows, pl.grid, s);
+        case SV_EPI_STORE:
+          return d->act_pair == 2 ? dispatch_ring<T, GM_STORE_BF16, 1>(p, d->rows, pl.grid, s)
+                                  : dispatch_ring<T, GM_STORE_F32, 1>(p, d->rows, pl.grid, s);
         default: return dispatch_ring<T, GM_ADD_F32, 1>(p, d->rows, pl.grid, s);
       }
     };

@@ -204,8 +204,8 @@ __device__ __forceinline__ float block_sum_256(float v, float* s_red) {
 __global__ __launch_bounds__(256) void draft_input_kernel(int d_main, int d_draft, float eps, const uint16_t* hidden,
                                                           int rows_h, const int32_t* hidden_row, int row_stride,
                                                           const uint16_t* emb, int vocab, const int32_t* tokens,
-                                                          int tok_stride, float emb_scale, uint16_t* cat, float* x,
-                                                          int32_t* dev_status) {
+                                                          int tok_stride, float emb_scale, uint16_t* cat, int pair,
+                                                          float* x, int32_t* dev_status) {
   __shared__ float s_red[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int dc = d_main + d_draft;
@@ -227,10 +227,16 @@ __global__ __launch_bounds__(256) void draft_input_kernel(int d_main, int d_draf
     ss = fmaf(v, v, ss);
   }
   const float einv = tok_ok ? 1.f / sqrtf(block_sum_256(ss, s_red) / (float)d_draft + eps) : 0.f;
+  // bf16, or the pair: plane 0 bf16(v), plane 1 bf16(v - plane 0), planes gridDim.x * dc apart
   uint16_t* crow = cat + (int64_t)b * dc;
-  for (int i = tid; i < d_main; i += 256) crow[i] = (uint16_t)f32_to_bf16_bits(bf16_to_f32(hrow[i]) * hinv);
-  for (int i = tid; i < d_draft; i += 256)
-    crow[d_main + i] = (uint16_t)f32_to_bf16_bits(emb_scale * bf16_to_f32(erow[i]) * einv);
+  const int64_t plane = (int64_t)gridDim.x * dc;
+  auto put = [&](int i, float v) {
+    const uint32_t h = f32_to_bf16_bits(v);
+    crow[i] = (uint16_t)h;
+    if (pair) crow[plane + i] = (uint16_t)f32_to_bf16_bits(v - bf16_to_f32((uint16_t)h));
+  };
+  for (int i = tid; i < d_main; i += 256) put(i, bf16_to_f32(hrow[i]) * hinv);
+  for (int i = tid; i < d_draft; i += 256) put(d_main + i, emb_scale * bf16_to_f32(erow[i]) * einv);
   for (int i = tid; i < d_draft; i += 256) x[(int64_t)b * d_draft + i] = 0.f;
 }
 
@@ -295,14 +301,15 @@ extern "C" int sv_add_rmsnorm(int32_t rows, int32_t dim, float eps, float* x, co
 extern "C" int sv_draft_input(int32_t batch, int32_t d_main, int32_t d_draft, float eps, const void* hidden,
                               int32_t rows_h, const int32_t* hidden_row, int32_t row_stride, const void* emb,
                               int32_t vocab, const int32_t* tokens, int32_t tok_stride, float emb_scale, void* cat,
-                              float* x, int32_t* dev_status, void* stream) {
+                              sv_dtype cat_dtype, float* x, int32_t* dev_status, void* stream) {
   if (batch <= 0 || d_main <= 0 || d_draft <= 0 || rows_h <= 0 || vocab <= 0 || !(eps >= 0.f)) return SV_ERR_ARG;
+  if (cat_dtype != SV_BF16 && cat_dtype != SV_BF16X2) return SV_ERR_ARG;
   if (!hidden || !hidden_row || !emb || !tokens || !cat || !x || row_stride < 0 || tok_stride < 0) return SV_ERR_ARG;
   int rc = check_device();
   if (rc != SV_OK) return rc;
   hipLaunchKernelGGL(draft_input_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, d_main, d_draft, eps,
                      (const uint16_t*)hidden, rows_h, hidden_row, row_stride, (const uint16_t*)emb, vocab, tokens,
-                     tok_stride, emb_scale, (uint16_t*)cat, x, dev_status);
+                     tok_stride, emb_scale, (uint16_t*)cat, cat_dtype == SV_BF16X2 ? 1 : 0, x, dev_status);
   return launch_status();
 }
 

@@ -13,11 +13,18 @@ draft) proposes k tokens one at a time.  Step i, for every sequence b:
         x += o Wo^T                                         sv_linear (K-split partials)
         m = norm(x)                                         sv_add_rmsnorm
         x += (gelu_tanh(m Wg^T) * (m Wu^T)) Wd^T            sv_linear (GeGLU), sv_linear
-    h  = norm(x) W_up^T                                     sv_add_rmsnorm, sv_linear (bf16)
+    h  = norm(x) W_up^T                                     sv_add_rmsnorm, sv_linear (stored bf16)
     d_{b,i+1} = argmax h E^T                                sv_lmhead_select (greedy; the
                                                             token goes to drafts[b][i])
     or, with a clustering of E given (section 4.3, cheap_unembed), the argmax over
     the tokens of the clusters whose centroids score highest   sv_cluster_unembed
+
+As in the target's verify step, the activations between the calls keep fp32
+precision: the residual stream x is fp32, q is a K-split fp32 partial sum, and the
+projections' inputs (cat, the norm outputs, the attention output and the GeGLU
+output) are bf16 pairs (hi = bf16(v), lo = bf16(v - hi), within 2^-16 |v|).  Only
+h, which the unembedding reads and the next step normalises, is stored in bf16, as
+the target's final hidden state is.
 
 The target's caches may be fp8 E4M3 codes with per-channel scales (kv_scales given
 for the layers the drafter reads): the blocks then read them with
@@ -59,10 +66,11 @@ class Drafter:
         self.reads = dcfg.target_layers(target_cfg)
         dev = self.dev
         z = lambda *s, dtype=torch.bfloat16: torch.zeros(*s, dtype=dtype, device=dev)
-        self.cat = z(B, d + dd)
+        # projection inputs as bf16 pairs [2, B, n]
+        self.cat = z(2, B, d + dd)
         self.x = z(B, dd, dtype=torch.float32)
-        self.a = z(B, dd)
-        self.f = z(B, dcfg.d_ff)
+        self.a = z(2, B, dd)
+        self.f = z(2, B, dcfg.d_ff)
         self.h = z(B, d)
         self.rows = torch.arange(B, dtype=torch.int32, device=dev)
         self.wgu_il = [interleave_gate_up(bw["wgu"]) for bw in weights["blocks"]]
@@ -70,8 +78,10 @@ class Drafter:
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.timers = None
 
-        def lin(K, N, epi):
-            return L.LinearDesc(rows=B, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi)
+        def lin(K, N, epi, pair=1):
+            # pair inputs; pair=2: a plain store writes bf16 (h), otherwise fp32
+            return L.LinearDesc(rows=B, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi,
+                                act_pair=pair)
         self._lin = lin
         # K-split partial buffers: residual projections (added by the next norm) and queries
         self.split = {}
@@ -90,8 +100,8 @@ class Drafter:
         self.q_split = q_split
         self.parts = z(max(self.split.values()) * B * dd, dtype=torch.float32)
         self.q_parts = z(max(q_split) * B * nq_max, dtype=torch.float32)
-        self.o = z(B, nq_max)
-        self.lin_ws = torch.zeros(max(256, L.sv_linear_workspace(lin(dd, d, L.SV_EPI_STORE)),
+        self.o = z(2, B, nq_max)
+        self.lin_ws = torch.zeros(max(256, L.sv_linear_workspace(lin(dd, d, L.SV_EPI_STORE, 2)),
                                       L.sv_linear_workspace(lin(dd, 2 * dcfg.d_ff, L.SV_EPI_GEGLU))),
                                   dtype=torch.uint8, device=dev)
         cap = caches[0]["k"].shape[2]
@@ -120,7 +130,7 @@ class Drafter:
         if key not in self._attn:
             ly = self.t.layers[self.reads[j]]
             self._attn[key] = attn_desc(ly, self.B, 1, self.cap, "bf16", append=False, q_pos_offset=i,
-                                        in_splits=self.q_split[j])
+                                        in_splits=self.q_split[j], act_pair=True)
         return self._attn[key]
 
     def _ev(self, name: str, stream):
@@ -140,7 +150,8 @@ class Drafter:
 
     def _norm(self, pending, stream):
         parts, S = pending if pending is not None else (None, 0)
-        L.sv_add_rmsnorm(self.B, self.cfg.d_draft, self.cfg.eps, self.x, parts, S, None, self.a, L.SV_BF16, stream)
+        L.sv_add_rmsnorm(self.B, self.cfg.d_draft, self.cfg.eps, self.x, parts, S, None, self.a, L.SV_BF16X2,
+                         stream)
         return self.a
 
     def _residual(self, inp, w, stream):
@@ -157,7 +168,7 @@ class Drafter:
         B, d, dd = self.B, t.d_model, dc.d_draft
         tok = self._ev("draft_input", stream)
         L.sv_draft_input(B, d, dd, dc.eps, h_src, rows_h, hidden_row, row_stride, self.W["E"], t.vocab, tokens,
-                         tok_stride, math.sqrt(dd), self.cat, self.x, self.dev_status, stream)
+                         tok_stride, math.sqrt(dd), self.cat, L.SV_BF16X2, self.x, self.dev_status, stream)
         pending = self._residual(self.cat, self.W["w_down"], stream)
         self._end(tok)
         for j, (bw, ti) in enumerate(zip(self.W["blocks"], self.reads)):
@@ -168,7 +179,7 @@ class Drafter:
             S = self.q_split[j]
             qp = self.q_parts.view(-1)[:S * B * nq]
             L.sv_linear(self._lin(dd, nq, L.SV_EPI_SPLIT_F32), a, bw["wq"], qp, None, stream)
-            o = self.o.view(-1)[:B * nq].view(B, nq)
+            o = self.o.view(-1)[:2 * B * nq].view(2, B, nq)
             kc = self.caches[ti]
             if ti in self.kv_scales:
                 ks, vs = self.kv_scales[ti]
@@ -186,7 +197,7 @@ class Drafter:
             self._end(tok)
         tok = self._ev("unembed", stream)
         u = self._norm(pending, stream)
-        L.sv_linear(self._lin(dd, d, L.SV_EPI_STORE), u, self.W["w_up"], self.h, self.lin_ws, stream)
+        L.sv_linear(self._lin(dd, d, L.SV_EPI_STORE, 2), u, self.W["w_up"], self.h, self.lin_ws, stream)
         if self.clusters is not None:
             c = self.clusters
             L.sv_cluster_unembed(self.cl_desc, self.h, c["centroids"], c["w_perm"], c["perm"], self.stats, self.kept,

@@ -142,7 +142,10 @@ class OracleDrafter:
 
     The pages' listing leaves norms and RoPE out; here every norm is an RMSNorm of
     unit gain and the queries get the RoPE of the target layer they read.  Values
-    the GPU path stores are rounded to bf16 at the same points as in OracleModel."""
+    the GPU path stores are rounded at the same points as in OracleModel: the
+    activations between the ops (cat, normed inputs, q, attention output, GeGLU
+    output) to fp32, h -- the unembedding's input, like the target's final hidden
+    state -- to bf16."""
 
     def __init__(self, target_cfg, dcfg, target_E: np.ndarray, weights: dict):
         self.t = target_cfg
@@ -154,8 +157,10 @@ class OracleDrafter:
             last[ly.kind] = i
         self.reads = [last[kind] for kind in dcfg.blocks]
 
-    def _r(self, x):
-        return bf16_round(x)
+    @staticmethod
+    def _r(x):
+        """Round an activation to its storage type (fp32)."""
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
 
     def step(self, state: dict, h_prev: np.ndarray, tokens, i: int) -> tuple[np.ndarray, np.ndarray]:
         """h_prev [B, d_model] (values as stored), tokens [B]; the step's query sits at
@@ -180,11 +185,11 @@ class OracleDrafter:
             o = self._r(o.reshape(B, ly.n_heads_q * ly.head_dim))
             x = x + linear(o, blk["wo"])
             m = self._r(rmsnorm(x, eps))
-            g = self._r(linear(m, blk["wgu"][:dc.d_ff]))
-            u = self._r(linear(m, blk["wgu"][dc.d_ff:]))
+            g = linear(m, blk["wgu"][:dc.d_ff])
+            u = linear(m, blk["wgu"][dc.d_ff:])
             f = self._r(geglu(g, u))
             x = x + linear(f, blk["wd"])
-        h = self._r(linear(self._r(rmsnorm(x, eps)), self.W["w_up"]))
+        h = bf16_round(linear(self._r(rmsnorm(x, eps)), self.W["w_up"]))
         return h, lmhead(h, self.E)
 
 

@@ -98,6 +98,12 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.sv_embed(0, 128, 10, L.SV_BF16, fake, fake, 1.0, fake, None, None) == L.SV_ERR_ARG
     assert lib.sv_rmsnorm(4, 128, -1.0, fake, None, fake, L.SV_BF16, None) == L.SV_ERR_ARG
     assert lib.sv_geglu(4, 128, 5, fake, fake, None) == L.SV_ERR_ARG
+    for pair in (-1, 3):
+        ld = L.LinearDesc(rows=20, in_features=3840, out_features=128, dtype=L.SV_BF16, epilogue=0, act_pair=pair)
+        assert lib.sv_linear(ctypes.byref(ld), fake, fake, fake, fake, 1 << 40, None) == L.SV_ERR_ARG
+    for cat_dtype in (L.SV_F32, 7):
+        assert lib.sv_draft_input(4, 3840, 1024, 1e-6, fake, 40, fake, 1, fake, 1000, fake, 1, 32.0, fake,
+                                  cat_dtype, fake, None, None) == L.SV_ERR_ARG
 
 
 def test_cluster_unembed_rejects_bad_arguments():

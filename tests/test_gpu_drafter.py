@@ -5,8 +5,8 @@ or over the kept clusters) against the oracle.
 Each draft step is checked with matched inputs: the oracle takes the GPU's h_prev
 and token of that step, so a near-tie that sends the two sides to different tokens
 does not carry into later steps.  Per step the row statistics must agree within
-2e-2 (as in the stack test) and the drafted token must equal the oracle's argmax
-wherever its top-2 margin exceeds 1e-2."""
+2e-2 absolute (as in the stack test) and the drafted token must equal the oracle's
+argmax wherever its top-2 margin exceeds 1e-2."""
 import numpy as np
 import pytest
 import torch
@@ -64,15 +64,18 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
                          {"E": inputs.bf16_bits(dw["E"]), "w_down": inputs.bf16_bits(dw["w_down"]),
                           "w_up": inputs.bf16_bits(dw["w_up"]),
                           "blocks": [{kk: inputs.bf16_bits(v) for kk, v in bw.items()} for bw in dw["blocks"]]})
-    hc = host_caches(caches) if not fp8 else [
-        {"k": oracle.dequant_cache(c["k"].cpu().numpy(), kv_scales[ti][0].cpu().numpy()[None, :, None, :]),
-         "v": None if c["v"] is None else oracle.dequant_cache(c["v"].cpu().numpy(),
-                                                                kv_scales[ti][1].cpu().numpy()[None, :, None, :])}
-        if ti in kv_scales else host_caches([c])[0] for ti, c in enumerate(caches)]
+    # host copies of the layers the drafter reads (the others are never touched)
+    reads = set(dcfg.target_layers(tcfg))
+    hc = [None if ti not in reads else
+          {"k": oracle.dequant_cache(c["k"].cpu().numpy(), kv_scales[ti][0].cpu().numpy()[None, :, None, :]),
+           "v": None if c["v"] is None else oracle.dequant_cache(c["v"].cpu().numpy(),
+                                                                  kv_scales[ti][1].cpu().numpy()[None, :, None, :])}
+          if fp8 and ti in kv_scales else host_caches([c])[0] for ti, c in enumerate(caches)]
     st = om.new_state(hc, lens)
     h_prev = host(h_verify)[[b * (tcfg.k + 1) + int(hr[b]) for b in range(B)]]
     tok = acc[:, 1].cpu().numpy()
     checked = 0
+    err = 0.0
     for i in range(k):
         if i == 0:
             dr.step(0, k, h_verify, R, acc.data_ptr() + 28, L.ACCEPT_OUT_WORDS, acc.data_ptr() + 4,
@@ -82,7 +85,6 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
         torch.cuda.synchronize()
         hq, z = o.step(st, h_prev, tok, i)
         gs = L.decode_row_stats(dr.stats)
-        zmax = np.abs(z).max()
         cref = oracle.cluster_unembed(hq, *cu_host, top) if cu is not None else None
         for b in range(B):
             if cref is None:
@@ -93,8 +95,9 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
                 if top < sc.size and sc[top - 1] - sc[top] <= ATOL * max(1.0, np.abs(sc).max()):
                     continue                    # the kept set is a near-tie: either side may differ
                 assert sorted(dr.kept[b].tolist()) == sorted(ref["clusters"]), (i, b)
-            assert abs(float(gs[b]["lse"]) - ref["lse"]) < ATOL * max(1.0, zmax), (i, b)
-            assert abs(float(gs[b]["top1"]) - ref["top1"]) < ATOL * max(1.0, zmax), (i, b)
+            err = max(err, abs(float(gs[b]["lse"]) - ref["lse"]), abs(float(gs[b]["top1"]) - ref["top1"]))
+            assert abs(float(gs[b]["lse"]) - ref["lse"]) < ATOL, (i, b)
+            assert abs(float(gs[b]["top1"]) - ref["top1"]) < ATOL, (i, b)
             if ref["top1"] - ref["top2"] > MARGIN:
                 assert int(drafts[b, i].item()) == ref["top1_id"], (i, b)
                 checked += 1
@@ -102,7 +105,9 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
         h_prev = host(dr.h)
         tok = drafts[:, i].cpu().numpy()
     assert int(dr.dev_status.item()) == 0
-    say(f"[drafter] ok: {checked} of {B * k} drafted tokens decided by a clear margin and equal")
+    say(f"[drafter] ok: {checked} of {B * k} drafted tokens decided by a clear margin and equal; "
+        f"worst |d lse|, |d top1| {err:.2e} (bar {ATOL})")
+    return checked
 
 
 def dataclass_replace(cfg, **kw):
@@ -140,3 +145,13 @@ def test_drafter_fp8_caches():
     tcfg = configs.scaled_stack(name="drafter_target4", d_model=256, vocab=4096, d_ff=512, batch=3, k=3,
                                 window=64, local_heads=(4, 2, 128), global_heads=(4, 1, 256))
     drafter_case(tcfg, configs.scaled_drafter(d_draft=128, d_ff=256), [200, 37, 500], 3, 4, fp8=True)
+
+
+@gpu
+def test_drafter_full_size():
+    """The drafter at its benchmark size (d_draft 1024, d_ff 4096, blocks L,L,L,G) over
+    the full-size stack's caches (d=3840, vocab 262,144, committed context 131,072 and
+    a ragged second sequence): two draft steps, both sequences checked."""
+    tcfg = dataclass_replace(configs.STACK, batch=2)
+    checked = drafter_case(tcfg, configs.DRAFTER, [131072, 126975], 2, 5)
+    assert checked >= 1

@@ -204,6 +204,30 @@ def test_pair_activations(R, K, N, epi):
 
 
 @gpu
+@pytest.mark.parametrize("R,K,N", [(8, 1024, 3840), (3, 96, 192), (40, 256 + 32, 640)])
+def test_pair_activations_bf16_store(R, K, N):
+    """act_pair 2: pair x, the fp32 result stored once in bf16 (round to nearest even):
+    the pair bound plus 2^-8 relative for the store."""
+    dev = need_gpu()
+    say(f"[linear pair bf16] R={R} K={K} N={N}")
+    xf = inputs.normal((R, K), 1.0, 18, "xf", dev, "f32")
+    W = inputs.normal((N, K), K ** -0.5, 18, "W", dev)
+    desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=L.SV_EPI_STORE,
+                        act_pair=2)
+    ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
+    y = torch.full((R, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    L.sv_linear(desc, pair_of(xf), W, y, ws)
+    torch.cuda.synchronize()
+    xh = host(xf)
+    ref = oracle.linear(xh, inputs.bf16_bits(W))
+    bound = pair_linear_bound(xh, W, K) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref) + 1e-30
+    got = host(y)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
+
+
+@gpu
 @pytest.mark.parametrize("R,K,N", [(40, 15360, 3840), (7, 96, 192), (33, 8192 + 32, 640)])
 def test_pair_activations_split(R, K, N):
     dev = need_gpu()
