@@ -48,8 +48,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--ctx", type=int, default=131072)
@@ -731,6 +731,12 @@ def bench_configs(args) -> dict:
             L.sv_accept_rs(xadesc, drafts, stats, cands, q_rows, u_acc, u_rs, cl, toks, acc)
         us_one = _timed(one_pass, it)
         us_res = _timed(lambda: L.sv_lmhead_select(rdesc, h, Wt, drafts, u_tok, q_rows, stats, acc, toks, ws), it)
+        # the standard mode's per-step uniforms (u_tok [B, V], u_accept [B, k], u_rs) drawn on
+        # the device, as a decode loop would before each step
+        u_gen = torch.Generator(device=dev)
+        u_gen.manual_seed(1)
+        us_unif = _timed(lambda: (torch.rand((B, V), generator=u_gen, device=dev, out=u_tok),
+                                  torch.rand((B, k), generator=u_gen, device=dev, out=u_acc)), it)
         # how often a rejecting sequence refuses all four candidates (new key per step)
         rej = fb = 0
         for _ in range(32):
@@ -747,9 +753,12 @@ def bench_configs(args) -> dict:
             "candidates_all_refused_fraction": round(fb / max(rej, 1), 4),
             "single_pass_expected_us_per_step": round(us_one + p_step * us_res, 2),
             "two_pass_n_accepted": n_two.tolist(),
+            "uniforms_us_per_step": round(us_unif, 2),
+            "uniforms_bytes_per_step": int(4 * (B * V + B * k)),
             "note": "two-pass always launches the residual pass (graph-friendly); the single-pass step "
                     "launches it only when some rejecting sequence refused all four candidates, with the "
-                    "probability measured over 32 steps"}
+                    "probability measured over 32 steps; uniforms_us_per_step: drawing the step's "
+                    "uniform inputs on the device (torch.rand), not included in the step times"}
         out[lcfg.name] = line
         del h, Wt, q_rows, ws
         torch.cuda.empty_cache()
@@ -757,54 +766,64 @@ def bench_configs(args) -> dict:
 
 
 def cpu_baseline(cfg, W, caches, tokens, lens, dev):
-    """Time the oracle on a bounded sample: one verify step of sequence 0."""
+    """Time the oracle on a bounded sample: the first recorded verify step of
+    sequences 0..2 (three single-sequence steps, one batched oracle call) on all
+    host threads, and the step of sequence 0 on one thread."""
     import numpy as np
 
     import oracle
     from oracle import model as om
     from mtp_draft_verification_amd import inputs
 
-    log("cpu baseline: host copies for sequence 0")
+    nseq = min(3, cfg.batch)
+    log(f"cpu baseline: host copies for sequences 0..{nseq - 1}")
     hw = {"E": inputs.bf16_bits(W["E"]),
           "layers": [{k: inputs.bf16_bits(v) for k, v in lw.items()} for lw in W["layers"]]}
     cap = caches[0]["k"].shape[2]
-    hc = []
-    L0 = int(lens[0])
-    for ly, c in zip(cfg.layers, caches):
-        ent = {}
-        for nm in ("k", "v"):
-            t = c[nm]
-            if t is None:
-                ent[nm] = None
-                continue
-            a = np.zeros((1, t.shape[1], cap, t.shape[3]), dtype=np.float32)
-            lo = max(0, L0 - ly.window - 8) if ly.window else 0
-            a[0, :, lo:L0] = t[0, :, lo:L0].float().cpu().numpy()
-            ent[nm] = a
-        hc.append(ent)
-    cfg1 = dataclasses.replace(cfg, batch=1)
-    model = om.OracleModel(cfg1, hw)
-    state = om.new_state(hc, [L0])
-    tok = tokens[:1].cpu().numpy()
+    Ls = [int(x) for x in lens[:nseq]]
+
+    def host_state(n):
+        hc = []
+        for ly, c in zip(cfg.layers, caches):
+            ent = {}
+            for nm in ("k", "v"):
+                t = c[nm]
+                if t is None:
+                    ent[nm] = None
+                    continue
+                a = np.zeros((n, t.shape[1], cap, t.shape[3]), dtype=np.float32)
+                for b in range(n):
+                    lo = max(0, Ls[b] - ly.window - 8) if ly.window else 0
+                    a[b, :, lo:Ls[b]] = t[b, :, lo:Ls[b]].float().cpu().numpy()
+                ent[nm] = a
+            hc.append(ent)
+        return om.new_state(hc, Ls[:n])
+
+    model = om.OracleModel(dataclasses.replace(cfg, batch=nseq), hw)
+    state = host_state(nseq)
+    tok = tokens[:nseq].cpu().numpy()
     cores = oracle.num_threads()
-    log(f"cpu baseline: oracle step on {cores} threads")
+    log(f"cpu baseline: oracle steps on {cores} threads")
     t0 = time.perf_counter()
     r = model.greedy_step(state, tok)
     dt = time.perf_counter() - t0
-    n = int(r["n"][0]) + 1
-    # the same step on one thread (from the same starting state)
+    n = int(np.sum(r["n"])) + nseq
+    # sequence 0's step on one thread (from the same starting state)
     log("cpu baseline: oracle step on 1 thread")
+    model1 = om.OracleModel(dataclasses.replace(cfg, batch=1), hw)
+    state1 = host_state(1)
     oracle.set_threads(1)
-    state1 = om.new_state(hc, [L0])
     t0 = time.perf_counter()
-    model.greedy_step(state1, tok)
+    r1 = model1.greedy_step(state1, tok[:1])
     dt1 = time.perf_counter() - t0
     oracle.set_threads(cores)
+    n1 = int(r1["n"][0]) + 1
     return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
-                single_thread_value=n / dt1, cpu_model=host_cpu(), host_threads=os.cpu_count(),
-                sample=f"one verify step of sequence 0 ({cfg.k + 1} rows, all 6 layers, LM head, accept) "
-                       f"of the same workload at its first recorded step: {n} tokens committed in {dt:.1f} s "
-                       f"on {cores} threads, {dt1:.1f} s on one")
+                single_thread_value=n1 / dt1, cpu_model=host_cpu(), host_threads=os.cpu_count(),
+                sample=f"the first recorded verify step of sequences 0..{nseq - 1} ({cfg.k + 1} rows each, all 6 "
+                       f"layers, LM head, accept) of the same workload: {n} tokens committed in {dt:.1f} s on "
+                       f"{cores} threads ({dt / nseq:.2f} s per step); sequence 0's step on one thread: "
+                       f"{n1} tokens in {dt1:.1f} s")
 
 
 def pmc_summary(roots):
