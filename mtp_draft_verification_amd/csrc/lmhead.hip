@@ -361,17 +361,26 @@ __device__ __forceinline__ RowState from_part(const SelPart& p) {
 // With XF (pair activations) a chunk of x is staged twice, the hi plane then the lo
 // plane, each laid out like a bf16 chunk: 16 MT rows x 128 B, 16-byte slots
 // swizzled by row.
-template <int MT, int T, int XF = 0>
+// G = 2 wave groups (8 waves, two per SIMD): the waves of slot w in both groups own
+// the same W rows; group g multiplies k-step g of every 64-dim chunk, and at the end of
+// a block group 1 hands its accumulators to group 0 through the stage just consumed.
+// Two waves per SIMD hide each other's MFMA and LDS latencies, which bind the pair
+// projections at 40 rows with one wave per SIMD.
+template <int MT, int T, int XF = 0, int G = 1>
 struct RingCfg {
   static constexpr int NB = 64 * T;            // output features per block
-  static constexpr int WI = 2 * T;             // W DMA instructions per wave per chunk
+  static constexpr int WI = 2 * T;             // W DMA instructions per wave slot per chunk
+  static constexpr int WIW = WI / G;           // ... issued by each wave of the slot
   static constexpr int XI = 2 * MT * (XF ? 2 : 1);  // x DMA instructions per chunk (workgroup)
-  static constexpr int NX = (XI + 3) / 4;      // x DMA instructions per wave
-  static constexpr int NI = WI + NX;           // DMA instructions per wave per chunk
+  static constexpr int NX = (XI + 4 * G - 1) / (4 * G);  // x DMA instructions per wave
+  static constexpr int NI = WIW + NX;          // DMA instructions per wave per chunk
   static constexpr int WSTAGE = NB * 128;
   static constexpr int STAGEB = WSTAGE + XI * 1024;
   static constexpr int NS_FIT = (160 * 1024) / STAGEB;
   static constexpr int NS = NS_FIT < 6 ? NS_FIT : 6;
+  static_assert(G == 1 || G == 2, "one or two wave groups");
+  static_assert(WI % G == 0, "W DMA split over the groups");
+  static_assert(G == 1 || 4 * T * MT * 1024 <= STAGEB, "group hand-over fits a stage");
   static_assert(NS >= 3, "ring needs three stages");
   static_assert((NS - 2) * NI <= 63, "vmcnt range");
   static_assert(4 * MT * 16 * (int)sizeof(SelPart) <= NS * STAGEB, "select merge reuses the ring");
@@ -389,15 +398,17 @@ __device__ __forceinline__ int logical_wg(int b, int P) {
 }
 
 
-template <int MT, int T, int MODE, int XF = 0>
-__global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
-  using C = RingCfg<MT, T, XF>;
+template <int MT, int T, int MODE, int XF = 0, int G = 1>
+__global__ __launch_bounds__(256 * G) void gemm_ring_kernel(GemmParams p) {
+  using C = RingCfg<MT, T, XF, G>;
   constexpr bool SELECT = select_mode(MODE);
+  static_assert(G == 1 || !SELECT, "select epilogues run with one wave group");
   constexpr int NB = C::NB, NS = C::NS, WROWS = 16 * T;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGEB];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA bases live in SGPRs
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA bases live in SGPRs
+  const int wave = wid & 3, grp = wid >> 2;  // W row slot, wave group
   const int lr = lane & 15, lg = lane >> 4;
   const int K = p.K, KCH = p.kch, P = gridDim.x;
   // K-split slices (GM_SPLIT, workgroup me holds slice me % splits): where the slice
@@ -415,13 +426,17 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
   const int dl8 = lane >> 3;
   const int cq[2] = {(lane & 7) ^ gswz(dl8), (lane & 7) ^ gswz(8 + dl8)};  // chunk fetched, by row parity
   const uint32_t adj[2] = {cq[0] >= 4 ? 64u : 0u, cq[1] >= 4 ? 64u : 0u};
-  uint32_t woff[C::WI];
+  // this wave's W DMA instructions: WIW of its slot's WI (group g takes the g-th share)
+  uint32_t woff[C::WIW];
 #pragma unroll
-  for (int i = 0; i < C::WI; ++i) woff[i] = (uint32_t)((i * 8 + dl8) * K * 2 + cq[i & 1] * 16);
+  for (int i = 0; i < C::WIW; ++i) {
+    const int iw = grp * C::WIW + i;
+    woff[i] = (uint32_t)((iw * 8 + dl8) * K * 2 + cq[iw & 1] * 16);
+  }
   uint32_t xoff[C::NX], xlds[C::NX], xadj[C::NX];
 #pragma unroll
   for (int ii = 0; ii < C::NX; ++ii) {
-    const int j = (wave + 4 * ii) < C::XI ? (wave + 4 * ii) : C::XI - 1;
+    const int j = (wid + 4 * G * ii) < C::XI ? (wid + 4 * G * ii) : C::XI - 1;
     // XF: instruction j moves plane j / (2 MT) (0 = hi, 1 = lo) of the rows of 8-row
     // block j % (2 MT)
     const int plane = XF ? j / (2 * MT) : 0;
@@ -461,8 +476,10 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
     const uint8_t* wb = (const uint8_t*)p.w + ((int64_t)(row0 < p.N ? row0 : 0) * K + kc * 64) * 2;
     const uint32_t dst = ring_lds + (uint32_t)(s * C::STAGEB);
 #pragma unroll
-    for (int i = 0; i < C::WI; ++i)
-      dma16<true, true>(wb, woff[i] - (tail ? adj[i & 1] : 0u), dst + (uint32_t)((wave * C::WI + i) * 1024));
+    for (int i = 0; i < C::WIW; ++i) {
+      const int iw = grp * C::WIW + i;
+      dma16<true, true>(wb, woff[i] - (tail ? adj[iw & 1] : 0u), dst + (uint32_t)((wave * C::WI + iw) * 1024));
+    }
     const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * 128;
 #pragma unroll
     for (int ii = 0; ii < C::NX; ++ii) dma16(xb, xoff[ii] - (tail ? xadj[ii] : 0u), dst + xlds[ii]);
@@ -651,7 +668,10 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
     const int nks = (ragged && ckc == KCH - 1) ? 1 : 2;
     const uint8_t* ws = wrd + s * C::STAGEB;
     const uint8_t* xs = xrd + s * C::STAGEB;
-    for (int js = 0; js < nks; ++js) {
+    const int sc = s;  // the stage this iteration reads
+    // k-steps of this chunk for this wave: both (one group), or k-step grp (two)
+    const int js_end = G == 1 ? nks : (grp < nks ? grp + 1 : 0);
+    for (int js = G == 1 ? 0 : grp; js < js_end; ++js) {
       const int so = ((js * 4 + lg) ^ fsw) << 4;
       V16 a[T];
 #pragma unroll
@@ -685,7 +705,30 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(GemmParams p) {
     }
     s = s + 1 == NS ? 0 : s + 1;
     if (ckc == KCH - 1 || it == n_it - 1) {
-      seg_end(cb, seg_kc0 == 0 && ckc == KCH - 1);
+      if constexpr (G == 2) {
+        // group 1 hands its k-step sums to group 0 through stage sc: every wave has
+        // finished reading it, and its next DMA is issued only after the next
+        // iteration's barrier.  Layout: [slot][t][mt][lane] f32x4.
+        lds_barrier();
+        f32x4_t* xch = (f32x4_t*)(ring + sc * C::STAGEB) + (wave * T * MT) * 64 + lane;
+        if (grp == 1) {
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xch[(t * MT + mt) * 64] = acc[t][mt];
+        }
+        lds_barrier();
+        if (grp == 0) {
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const f32x4_t o = xch[(t * MT + mt) * 64];
+              acc[t][mt][0] += o[0]; acc[t][mt][1] += o[1]; acc[t][mt][2] += o[2]; acc[t][mt][3] += o[3];
+            }
+        }
+      }
+      if (grp == 0) seg_end(cb, seg_kc0 == 0 && ckc == KCH - 1);
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -1295,9 +1338,12 @@ static int validate_lmhead(const sv_lmhead_desc* d) {
   return SV_OK;
 }
 
+// Pair-activation projections run two wave groups (8 waves) where the hand-over of
+// the accumulators fits one ring stage; the select epilogues keep one.
 template <int MT, int T, int MODE, int XF>
 static void launch_ring(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_ring_kernel<MT, T, MODE, XF>), dim3(grid), dim3(256), 0, s, p);
+  constexpr int G = (XF && !select_mode(MODE) && 4 * T * MT * 1024 <= RingCfg<MT, T, XF>::STAGEB) ? 2 : 1;
+  hipLaunchKernelGGL((gemm_ring_kernel<MT, T, MODE, XF, G>), dim3(grid), dim3(256 * G), 0, s, p);
 }
 
 template <int T, int MODE, int XF = 0>
