@@ -380,7 +380,10 @@ struct RingCfg {
   static constexpr int NS = NS_FIT < 6 ? NS_FIT : 6;
   static_assert(G == 1 || G == 2, "one or two wave groups");
   static_assert(WI % G == 0, "W DMA split over the groups");
-  static_assert(G == 1 || 4 * T * MT * 1024 <= STAGEB, "group hand-over fits a stage");
+  // tiles per round of the group hand-over: the largest divisor of T whose
+  // [4 slots][TC][MT] accumulators fit one stage
+  static constexpr int TC = (4 * T * MT * 1024 <= STAGEB) ? T : (4 * (T / 2) * MT * 1024 <= STAGEB) ? T / 2 : 1;
+  static_assert(G == 1 || 4 * TC * MT * 1024 <= STAGEB, "group hand-over fits a stage");
   static_assert(NS >= 3, "ring needs three stages");
   static_assert((NS - 2) * NI <= 63, "vmcnt range");
   static_assert(4 * MT * 16 * (int)sizeof(SelPart) <= NS * STAGEB, "select merge reuses the ring");
@@ -402,7 +405,7 @@ template <int MT, int T, int MODE, int XF = 0, int G = 1>
 __global__ __launch_bounds__(256 * G) void gemm_ring_kernel(GemmParams p) {
   using C = RingCfg<MT, T, XF, G>;
   constexpr bool SELECT = select_mode(MODE);
-  static_assert(G == 1 || !SELECT, "select epilogues run with one wave group");
+  static_assert(G == 1 || MODE != GM_SAMPLE_RS, "the candidate draws run with one wave group");
   constexpr int NB = C::NB, NS = C::NS, WROWS = 16 * T;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGEB];
 
@@ -706,26 +709,31 @@ __global__ __launch_bounds__(256 * G) void gemm_ring_kernel(GemmParams p) {
     s = s + 1 == NS ? 0 : s + 1;
     if (ckc == KCH - 1 || it == n_it - 1) {
       if constexpr (G == 2) {
-        // group 1 hands its k-step sums to group 0 through stage sc: every wave has
-        // finished reading it, and its next DMA is issued only after the next
-        // iteration's barrier.  Layout: [slot][t][mt][lane] f32x4.
-        lds_barrier();
-        f32x4_t* xch = (f32x4_t*)(ring + sc * C::STAGEB) + (wave * T * MT) * 64 + lane;
-        if (grp == 1) {
+        // group 1 hands its k-step sums to group 0 through stage sc, TC tiles per
+        // round: every wave has finished reading the stage, and its next DMA is issued
+        // only after the next iteration's barrier.  Layout: [slot][tc][mt][lane] f32x4.
+        constexpr int TC = C::TC;
+        f32x4_t* xch = (f32x4_t*)(ring + sc * C::STAGEB) + (wave * TC * MT) * 64 + lane;
 #pragma unroll
-          for (int t = 0; t < T; ++t)
+        for (int t0 = 0; t0 < T; t0 += TC) {
+          lds_barrier();
+          if (grp == 1) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) xch[(t * MT + mt) * 64] = acc[t][mt];
-        }
-        lds_barrier();
-        if (grp == 0) {
+            for (int t = 0; t < TC; ++t)
 #pragma unroll
-          for (int t = 0; t < T; ++t)
+              for (int mt = 0; mt < MT; ++mt) xch[(t * MT + mt) * 64] = acc[t0 + t][mt];
+          }
+          lds_barrier();
+          if (grp == 0) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const f32x4_t o = xch[(t * MT + mt) * 64];
-              acc[t][mt][0] += o[0]; acc[t][mt][1] += o[1]; acc[t][mt][2] += o[2]; acc[t][mt][3] += o[3];
-            }
+            for (int t = 0; t < TC; ++t)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) {
+                const f32x4_t o = xch[(t * MT + mt) * 64];
+                f32x4_t& a = acc[t0 + t][mt];
+                a[0] += o[0]; a[1] += o[1]; a[2] += o[2]; a[3] += o[3];
+              }
+          }
         }
       }
       if (grp == 0) seg_end(cb, seg_kc0 == 0 && ckc == KCH - 1);
@@ -747,10 +755,10 @@ __global__ __launch_bounds__(256 * G) void gemm_ring_kernel(GemmParams p) {
     for (int mt = 0; mt < MT; ++mt) {
       state_merge_xor(st[mt], 16);
       state_merge_xor(st[mt], 32);
-      if (lg == 0) s_sel[(wave * MT + mt) * 16 + lr] = to_part(st[mt]);
+      if (lg == 0 && grp == 0) s_sel[(wave * MT + mt) * 16 + lr] = to_part(st[mt]);  // group 0 folded
     }
     __syncthreads();
-    if (wave == 0 && lg == 0) {
+    if (wid == 0 && lg == 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + lr;
@@ -1338,11 +1346,12 @@ static int validate_lmhead(const sv_lmhead_desc* d) {
   return SV_OK;
 }
 
-// Pair-activation projections run two wave groups (8 waves) where the hand-over of
-// the accumulators fits one ring stage; the select epilogues keep one.
+// Pair-activation projections and the LM head's greedy / sampling / residual selects
+// run two wave groups (8 waves); the single-pass candidate draws keep one (their
+// per-row state does not fit two waves per SIMD).
 template <int MT, int T, int MODE, int XF>
 static void launch_ring(const GemmParams& p, int grid, hipStream_t s) {
-  constexpr int G = (XF && !select_mode(MODE) && 4 * T * MT * 1024 <= RingCfg<MT, T, XF>::STAGEB) ? 2 : 1;
+  constexpr int G = ((XF && !select_mode(MODE)) || (select_mode(MODE) && MODE != GM_SAMPLE_RS)) ? 2 : 1;
   hipLaunchKernelGGL((gemm_ring_kernel<MT, T, MODE, XF, G>), dim3(grid), dim3(256 * G), 0, s, p);
 }
 
