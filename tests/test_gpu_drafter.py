@@ -20,6 +20,7 @@ from gpu_util import gpu, host, need_gpu, say
 
 ATOL = 2e-2
 MARGIN = 1e-2
+SCORE_GAP = 1e-4  # cluster scores: relative gap below which the kept set may differ
 
 
 def host_caches(caches):
@@ -75,7 +76,9 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
     h_prev = host(h_verify)[[b * (tcfg.k + 1) + int(hr[b]) for b in range(B)]]
     tok = acc[:, 1].cpu().numpy()
     checked = 0
+    compared = 0
     err = 0.0
+    h_err = 0.0
     for i in range(k):
         if i == 0:
             dr.step(0, k, h_verify, R, acc.data_ptr() + 28, L.ACCEPT_OUT_WORDS, acc.data_ptr() + 4,
@@ -85,16 +88,28 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
         torch.cuda.synchronize()
         hq, z = o.step(st, h_prev, tok, i)
         gs = L.decode_row_stats(dr.stats)
-        cref = oracle.cluster_unembed(hq, *cu_host, top) if cu is not None else None
+        cref = None
+        if cu is not None:
+            # the kept clusters are compared on the GPU's own h (matched input: the
+            # scores then differ only by fp32 against fp64 sums); h itself against the
+            # oracle's separately
+            hg = host(dr.h).astype(np.float64)
+            rel_h = float(np.linalg.norm(hg - hq) / np.linalg.norm(hq))
+            h_err = max(h_err, rel_h)
+            assert rel_h <= 5e-3, (i, rel_h)
+            cref = oracle.cluster_unembed(hg, *cu_host, top)
         for b in range(B):
             if cref is None:
                 ref = oracle.row_stats(z[b])
             else:
                 ref = cref[b]
-                sc = np.sort(ref["scores"])[::-1]
-                if top < sc.size and sc[top - 1] - sc[top] <= ATOL * max(1.0, np.abs(sc).max()):
-                    continue                    # the kept set is a near-tie: either side may differ
-                assert sorted(dr.kept[b].tolist()) == sorted(ref["clusters"]), (i, b)
+                if sorted(dr.kept[b].tolist()) != sorted(ref["clusters"]):
+                    # a different kept set is allowed only across a near-tie of cluster
+                    # scores at the boundary (fp32 dot products against fp64)
+                    sc = np.sort(ref["scores"])[::-1]
+                    assert top < sc.size and sc[top - 1] - sc[top] <= SCORE_GAP * max(1.0, np.abs(sc).max()), (i, b)
+                    continue
+            compared += 1
             err = max(err, abs(float(gs[b]["lse"]) - ref["lse"]), abs(float(gs[b]["top1"]) - ref["top1"]))
             assert abs(float(gs[b]["lse"]) - ref["lse"]) < ATOL, (i, b)
             assert abs(float(gs[b]["top1"]) - ref["top1"]) < ATOL, (i, b)
@@ -105,8 +120,10 @@ def drafter_case(tcfg, dcfg, lens, k, seed, n_clusters=0, top=0, fp8=False):
         h_prev = host(dr.h)
         tok = drafts[:, i].cpu().numpy()
     assert int(dr.dev_status.item()) == 0
-    say(f"[drafter] ok: {checked} of {B * k} drafted tokens decided by a clear margin and equal; "
-        f"worst |d lse|, |d top1| {err:.2e} (bar {ATOL})")
+    assert compared >= (B * k + 1) // 2, f"only {compared} of {B * k} rows compared"
+    say(f"[drafter] ok: {compared} of {B * k} rows compared, {checked} drafted tokens decided by a clear "
+        f"margin and equal; worst |d lse|, |d top1| {err:.2e} (bar {ATOL})"
+        + (f"; h rel L2 {h_err:.2e}" if cu is not None else ""))
     return checked
 
 
@@ -154,4 +171,15 @@ def test_drafter_full_size():
     a ragged second sequence): two draft steps, both sequences checked."""
     tcfg = dataclass_replace(configs.STACK, batch=2)
     checked = drafter_case(tcfg, configs.DRAFTER, [131072, 126975], 2, 5)
+    assert checked >= 1
+
+
+@gpu
+def test_drafter_full_size_clustered_and_fp8():
+    """The drafter at benchmark size with the clustered unembedding (2,048 clusters of
+    128 tokens, 32 kept) and, in a second run, reading fp8 E4M3 copies of the layers it
+    attends: two draft steps over the full stack's caches each."""
+    tcfg = dataclass_replace(configs.STACK, batch=2)
+    drafter_case(tcfg, configs.DRAFTER, [131072, 126975], 2, 6, n_clusters=2048, top=32)
+    checked = drafter_case(tcfg, configs.DRAFTER, [131072, 126975], 2, 7, fp8=True)
     assert checked >= 1
