@@ -891,8 +891,8 @@ def main():
         return
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of "
-              f"this build: the verify step shards by sequence with no exchange (see DESIGN.md).",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library implements the "
+              f"one-GPU path; across GPUs the verify step would shard by sequence, with no exchange.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
