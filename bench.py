@@ -826,7 +826,7 @@ def cpu_baseline(cfg, W, caches, tokens, lens, dev):
                        f"{n1} tokens in {dt1:.1f} s")
 
 
-def pmc_summary(roots):
+def pmc_summary(roots, out_path=None):
     """Write profiles/hbm_traffic.json from rocprofv3 --pmc runs (csv output) of
     `bench.py --only <call> --iters 3`, one run per call and counter:
     roots[0]/<call>/ holds the FETCH_SIZE run, roots[1]/<call>/ the WRITE_SIZE run,
@@ -880,9 +880,10 @@ def pmc_summary(roots):
             except (OSError, ValueError, KeyError, IndexError):
                 pass
             out["calls"][call] = ent
-    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+    with open(out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+    return out
 
 
 def main():
