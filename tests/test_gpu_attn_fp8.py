@@ -136,6 +136,19 @@ def test_fp8_many_sequences_work_split():
 
 
 @gpu
+def test_fp8_two_workgroups_per_cu_work_split():
+    """512-dim heads with one row tile (2 q heads per KV head x 5 rows) run two workgroups
+    per compute unit, so the keys are cut into twice as many pieces: fewer segments than
+    pieces (70 x 4) and more (150 x 4, one piece per segment), ragged and empty
+    sequences, with appends."""
+    ly = configs.global_layer(8, 4, 512)
+    for B, seed in ((70, 21), (150, 22)):
+        lens = inputs.randint((B,), 0, 600, seed, "lens", "cpu").tolist()
+        lens[1] = 0
+        run_case(ly, B, 5, lens, 610, seed, std=0.5, tag=f"two-per-cu-B{B}")
+
+
+@gpu
 def test_fp8_read_only_drafter_queries():
     ly = configs.global_layer(16, 4, 512)
     run_case(ly, 3, 1, [50, 0, 777], 800, 5, append=False, qoff=0, tag="read-only-global")
