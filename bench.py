@@ -193,8 +193,10 @@ def time_one(args, only) -> dict:
         desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_pair=1)
         ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
         # rotate over copies of W (1 GiB in all) so that, as inside the step, no call
-        # finds its weights in the last-level cache
-        Ws = [W] + [W.clone() for _ in range(max(0, -(-(1 << 30) // (2 * N * K)) - 1))]
+        # finds its weights in the last-level cache; tiled as the step's weights are
+        Ws = [L.tiled_weight(desc, W)]
+        Ws += [Ws[0].clone() for _ in range(max(0, -(-(1 << 30) // (2 * N * K)) - 1))]
+        desc.w_layout = L.SV_W_TILED
         turn = [0]
 
         def call():

@@ -472,7 +472,20 @@ typedef struct {
                             bf16 pair [2, R, N/2]; ADD_F32 and SPLIT_F32 are unchanged.
                             2: as 1, but SV_EPI_STORE writes y in bf16 (the fp32 result
                             rounded once, to nearest even).  Other values: SV_ERR_ARG */
+  int32_t w_layout;      /* SV_W_ROWMAJOR: w is [N, K] row-major.  SV_W_TILED (bf16 only):
+                            w is the tiled copy sv_linear_tile_weights made for a descriptor
+                            with the same in_features, out_features, dtype and epilogue
+                            (16-byte aligned).  Other values: SV_ERR_ARG */
 } sv_linear_desc;
+
+enum {
+  SV_W_ROWMAJOR = 0,
+  SV_W_TILED = 1         /* the weight stream reads one contiguous KiB per DMA instruction
+                            instead of 128 bytes from each of eight rows (whole DRAM pages;
+                            a DMA probe with the pair-activation chunk staged beside the
+                            weights streamed 12 % more per workgroup this way).  Results are
+                            bit for bit those of the row-major layout. */
+};
 
 /* S of SV_EPI_SPLIT_F32 for this shape on the current device (1 <= S <= the
  * device's compute units / ceil(N / 128)); 0 if the descriptor is invalid, not
@@ -485,7 +498,21 @@ int32_t sv_linear_splits(const sv_linear_desc* desc);
  * every call, one call at a time. */
 size_t sv_linear_workspace(const sv_linear_desc* desc);
 
-/* Skinny projection y = x W^T for the few verify rows: x [R, K], W [N, K].
+/* Bytes of the tiled copy of a weight for this descriptor (bf16; rows is not used):
+ * ceil(N / 64T) * ceil(K / 64) tiles of 64T x 64 weights, T = 1 or 2 as the library picks
+ * for the shape and epilogue; 0 if the descriptor is invalid or not bf16. */
+size_t sv_linear_tiled_bytes(const sv_linear_desc* desc);
+
+/* Write the tiled copy of w (bf16 [N, K] row-major, 16-byte aligned) into w_tiled
+ * (sv_linear_tiled_bytes(desc) bytes, 16-byte aligned, caller-owned): for each block of
+ * 64T output features and each 64-dim chunk of K, the chunk's weights in the order the
+ * projection's DMA places them in LDS, zero past N and K.  Asynchronous on stream; the
+ * desc's w_layout is ignored.  SV_ERR_ARG: bad descriptor, not bf16, null or misaligned
+ * pointers. */
+int sv_linear_tile_weights(const sv_linear_desc* desc, const void* w, void* w_tiled, void* stream);
+
+/* Skinny projection y = x W^T for the few verify rows: x [R, K], W [N, K] (or its tiled
+ * copy, desc->w_layout).
  * bf16: one persistent workgroup per CU over (64T-feature block, 64-dim chunk)
  * units; a block split across workgroups is summed in a fixed order, so results
  * are deterministic for a given device. */

@@ -21,11 +21,13 @@ SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 SV_F32, SV_BF16, SV_BF16X2 = 0, 1, 2
 SV_SELECT_GREEDY, SV_SELECT_SAMPLE, SV_SELECT_RESIDUAL, SV_SELECT_SAMPLE_RS = 0, 1, 2, 3
 SV_EPI_STORE, SV_EPI_ADD_F32, SV_EPI_GEGLU, SV_EPI_SPLIT_F32 = 0, 1, 2, 3
+SV_W_ROWMAJOR, SV_W_TILED = 0, 1
 SV_DEV_CACHE_OVERFLOW, SV_DEV_BAD_TOKEN, SV_DEV_BAD_LENGTH = 1, 2, 4
 
 EXPORTS = ("sv_status_string", "sv_version", "sv_verify_attn_workspace", "sv_verify_attn", "sv_verify_attn_fp8",
            "sv_lmhead_workspace", "sv_lmhead_select", "sv_accept", "sv_embed", "sv_rmsnorm",
            "sv_add_rmsnorm", "sv_draft_input", "sv_linear_splits", "sv_linear_workspace", "sv_linear",
+           "sv_linear_tiled_bytes", "sv_linear_tile_weights",
            "sv_geglu", "sv_cluster_unembed_workspace", "sv_cluster_unembed", "sv_lmhead_select_rs", "sv_accept_rs",
            "sv_verify_attn_noalloc")
 
@@ -61,7 +63,7 @@ class AcceptDesc(ctypes.Structure):
 class LinearDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("in_features", ctypes.c_int32),
                 ("out_features", ctypes.c_int32), ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32),
-                ("act_pair", ctypes.c_int32)]
+                ("act_pair", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 class ClusterDesc(ctypes.Structure):
@@ -126,6 +128,10 @@ def load():
     L.sv_linear_workspace.argtypes = [ctypes.POINTER(LinearDesc)]
     L.sv_linear.restype = ctypes.c_int
     L.sv_linear.argtypes = [ctypes.POINTER(LinearDesc), P, P, P, P, sz, P]
+    L.sv_linear_tiled_bytes.restype = sz
+    L.sv_linear_tiled_bytes.argtypes = [ctypes.POINTER(LinearDesc)]
+    L.sv_linear_tile_weights.restype = ctypes.c_int
+    L.sv_linear_tile_weights.argtypes = [ctypes.POINTER(LinearDesc), P, P, P]
     L.sv_geglu.restype = ctypes.c_int
     L.sv_geglu.argtypes = [i32, i32, ctypes.c_int, P, P, P]
     u32 = ctypes.c_uint32
@@ -293,6 +299,26 @@ def sv_linear(desc: LinearDesc, x, w, y, workspace=None, stream=None) -> None:
     rc = load().sv_linear(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(y), _ptr(workspace), ws_bytes,
                           _stream(stream))
     _check("sv_linear", rc)
+
+
+def sv_linear_tiled_bytes(desc: LinearDesc) -> int:
+    return int(load().sv_linear_tiled_bytes(ctypes.byref(desc)))
+
+
+def sv_linear_tile_weights(desc: LinearDesc, w, w_tiled, stream=None) -> None:
+    rc = load().sv_linear_tile_weights(ctypes.byref(desc), _ptr(w), _ptr(w_tiled), _stream(stream))
+    _check("sv_linear_tile_weights", rc)
+
+
+def tiled_weight(desc: LinearDesc, w, stream=None):
+    """A new device tensor holding the tiled copy of w ([N, K] bf16) for desc."""
+    import torch
+    n = sv_linear_tiled_bytes(desc)
+    if n <= 0:
+        raise SvError("sv_linear_tiled_bytes", SV_ERR_ARG, "no tiled layout for this descriptor")
+    wt = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    sv_linear_tile_weights(desc, w, wt, stream)
+    return wt
 
 
 def sv_geglu(rows: int, d_ff: int, dtype: int, gate_up, out, stream=None) -> None:

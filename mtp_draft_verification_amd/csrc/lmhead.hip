@@ -40,7 +40,9 @@ struct GemmParams {
   const void* x;         // [R, K] rows, bf16 (with the kernel's XF: two bf16 planes [2, R, K],
                          // hi then lo, of pair activations; RESIDUAL: the hidden states,
                          // gathered per slot)
-  const uint16_t* w;     // [N, K]
+  const uint16_t* w;     // [N, K], or (w_tiled) the tiled copy: per (block, chunk) the W part
+                         // of a ring stage exactly as the DMA lays it out in LDS
+  int w_tiled;
   int R, K, N;
   int nblk, kch;         // feature blocks, 64-wide K chunks
   // select
@@ -475,13 +477,24 @@ __global__ __launch_bounds__(256 * G) void gemm_ring_kernel(GemmParams p) {
   // ---- DMA issue of chunk unit (b, kc) into ring stage s ----
   auto issue = [&](int b, int kc, int s) {
     const bool tail = ragged && kc == KCH - 1;
-    const int row0 = b * NB + wave * WROWS;
-    const uint8_t* wb = (const uint8_t*)p.w + ((int64_t)(row0 < p.N ? row0 : 0) * K + kc * 64) * 2;
     const uint32_t dst = ring_lds + (uint32_t)(s * C::STAGEB);
+    if (p.w_tiled) {
+      // one contiguous 1 KiB per instruction: whole DRAM pages instead of 128 bytes from
+      // each of 8 rows (zero padding covers the ragged last chunk and block)
+      const uint8_t* wt = (const uint8_t*)p.w + ((int64_t)b * KCH + kc) * (NB * 128) + wave * C::WI * 1024;
 #pragma unroll
-    for (int i = 0; i < C::WIW; ++i) {
-      const int iw = grp * C::WIW + i;
-      dma16<true, true>(wb, woff[i] - (tail ? adj[iw & 1] : 0u), dst + (uint32_t)((wave * C::WI + iw) * 1024));
+      for (int i = 0; i < C::WIW; ++i) {
+        const int iw = grp * C::WIW + i;
+        dma16<true, true>(wt + iw * 1024, (uint32_t)(lane * 16), dst + (uint32_t)((wave * C::WI + iw) * 1024));
+      }
+    } else {
+      const int row0 = b * NB + wave * WROWS;
+      const uint8_t* wb = (const uint8_t*)p.w + ((int64_t)(row0 < p.N ? row0 : 0) * K + kc * 64) * 2;
+#pragma unroll
+      for (int i = 0; i < C::WIW; ++i) {
+        const int iw = grp * C::WIW + i;
+        dma16<true, true>(wb, woff[i] - (tail ? adj[iw & 1] : 0u), dst + (uint32_t)((wave * C::WI + iw) * 1024));
+      }
     }
     const uint8_t* xb = (const uint8_t*)p.x + (int64_t)kc * 128;
 #pragma unroll
@@ -810,6 +823,30 @@ __global__ __launch_bounds__(256 * G) void gemm_ring_kernel(GemmParams p) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled weight copy for the ring GEMM: 16-byte unit u of tile (block b, chunk kc) is what
+// lane u % 64 of W DMA instruction u / 64 moves into the ring stage, i.e. wave slot
+// ins / (2T), rows slot*16T + (ins % 2T)*8 + lane/8 of the block, the 16-byte column
+// slot (lane % 8) ^ gswz(row % 16) of the chunk; rows past N and columns past K are zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
+                                                           int N, int K, int T, int kch, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int NB = 64 * T, WI = 2 * T, WROWS = 16 * T;
+  const int per_tile = NB * 8;  // 16-byte units per tile
+  const int64_t tile = u / per_tile;
+  const int su = (int)(u - tile * per_tile);
+  const int b = (int)(tile / kch), kc = (int)(tile - (int64_t)b * kch);
+  const int ins = su >> 6, lane = su & 63, dl8 = lane >> 3;
+  const int iw = ins % WI;
+  const int row = b * NB + (ins / WI) * WROWS + iw * 8 + dl8;
+  const int k0 = kc * 64 + (((lane & 7) ^ gswz(((iw & 1) << 3) + dl8)) << 3);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < N && k0 < K) v = *(const uint4*)(w + (int64_t)row * K + k0);  // K % 32 == 0: k0 + 8 <= K
+  *(uint4*)(wt + u * 8) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -1376,6 +1413,8 @@ static int validate_linear(const sv_linear_desc* d) {
   if (d->epilogue == SV_EPI_SPLIT_F32 && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->act_pair < 0 || d->act_pair > 2) return SV_ERR_ARG;
   if (d->act_pair && d->dtype != SV_BF16) return SV_ERR_ARG;
+  if (d->w_layout != SV_W_ROWMAJOR && d->w_layout != SV_W_TILED) return SV_ERR_ARG;
+  if (d->w_layout == SV_W_TILED && d->dtype != SV_BF16) return SV_ERR_ARG;
   if (d->out_features % 64) return SV_ERR_ARG;
   if (d->epilogue == SV_EPI_GEGLU && (d->dtype != SV_BF16 || d->out_features % 128)) return SV_ERR_ARG;
   if (d->dtype == SV_BF16) {
@@ -1643,11 +1682,37 @@ extern "C" size_t sv_linear_workspace(const sv_linear_desc* d) {
   return pl.cnt_bytes + pl.part_bytes;
 }
 
+// The tiled copy holds every (block, chunk) tile of the ring plan whole: nblk * kch tiles
+// of 64T rows x 128 bytes.  T comes from the descriptor (epilogue, K, N), never from the
+// device, so the size is a property of the descriptor alone.
+extern "C" size_t sv_linear_tiled_bytes(const sv_linear_desc* d) {
+  if (validate_linear(d) != SV_OK || d->dtype != SV_BF16) return 0;
+  const int T = lin_tiles(*d);
+  const int64_t nblk = (d->out_features + 64 * T - 1) / (64 * T), kch = (d->in_features + 63) / 64;
+  return (size_t)(nblk * kch * (64 * T) * 128);
+}
+
+extern "C" int sv_linear_tile_weights(const sv_linear_desc* d, const void* w, void* w_tiled, void* stream) {
+  const int rc = validate_linear(d);
+  if (rc != SV_OK) return rc;
+  if (d->dtype != SV_BF16) return SV_ERR_ARG;
+  if (!w || !w_tiled || ((uintptr_t)w & 15) || ((uintptr_t)w_tiled & 15)) return SV_ERR_ARG;
+  const int drc = check_device();
+  if (drc != SV_OK) return drc;
+  const int T = lin_tiles(*d);
+  const int kch = (d->in_features + 63) / 64;
+  const int64_t units = (int64_t)sv_linear_tiled_bytes(d) / 16;
+  hipLaunchKernelGGL(tile_weights_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)w, (uint16_t*)w_tiled, d->out_features, d->in_features, T, kch, units);
+  return launch_status();
+}
+
 extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, void* y,
                          void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_linear(d);
   if (rc != SV_OK) return rc;
   if (!x || !w || !y) return SV_ERR_ARG;
+  if (d->w_layout == SV_W_TILED && ((uintptr_t)w & 15)) return SV_ERR_ARG;
   const size_t need = sv_linear_workspace(d);
   if (need && (!workspace || workspace_bytes < need)) return SV_ERR_WORKSPACE;
   rc = check_device();
@@ -1669,6 +1734,7 @@ extern "C" int sv_linear(const sv_linear_desc* d, const void* x, const void* w, 
   }
   p.x = x;
   p.w = (const uint16_t*)w;
+  p.w_tiled = d->w_layout == SV_W_TILED;
   p.R = d->rows;
   p.K = d->in_features;
   p.N = d->out_features;

@@ -64,7 +64,8 @@ def interleave_gate_up(wgu: torch.Tensor) -> torch.Tensor:
 class VerifyStack:
     """Device-resident state of a stack: weights, caches, committed lengths, buffers."""
 
-    def __init__(self, cfg, weights: dict, caches: list, cache_len: torch.Tensor, device="cuda"):
+    def __init__(self, cfg, weights: dict, caches: list, cache_len: torch.Tensor, device="cuda",
+                 tiled_weights: bool = True):
         self.cfg = cfg
         self.W = weights
         self.caches = caches
@@ -128,6 +129,16 @@ class VerifyStack:
         self.attn_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.lin_ws = torch.zeros(max([self._lin_ws(*s) for s in self._lin_shapes()] + [256]),
                                   dtype=torch.uint8, device=dev)
+        # bf16 projections read tiled copies of their weights (made once here, for the
+        # epilogue each call uses): the weight stream then reads whole DRAM pages
+        self.tiled = {}
+        if self.bf16 and tiled_weights:
+            for i, (ly, lw) in enumerate(zip(cfg.layers, weights["layers"])):
+                self._tile(lw["wqkv"], L.SV_EPI_SPLIT_F32 if self.qkv_split[i] else L.SV_EPI_STORE)
+                self._tile(lw["wo"], self._residual_epi(lw["wo"].shape[1]))
+                if cfg.d_ff:
+                    self._tile(self.wgu_il[i], L.SV_EPI_GEGLU)
+                    self._tile(lw["wd"], self._residual_epi(cfg.d_ff))
         self.lm_desc = L.LMHeadDesc(batch=B, k=k, d_model=d, vocab=cfg.vocab, mode=L.SV_SELECT_GREEDY,
                                     dtype=self.dt)
         self.lm_ws = torch.zeros(max(L.sv_lmhead_workspace(self.lm_desc), 256), dtype=torch.uint8, device=dev)
@@ -174,11 +185,22 @@ class VerifyStack:
         return L.sv_linear_workspace(L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt,
                                                   epilogue=epi, act_pair=self.act))
 
+    def _tile(self, w, epi):
+        N, K = w.shape
+        desc = L.LinearDesc(rows=self.R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi,
+                            act_pair=self.act)
+        self.tiled[(w.data_ptr(), epi)] = L.tiled_weight(desc, w)
+
+    def _residual_epi(self, K: int) -> int:
+        return L.SV_EPI_SPLIT_F32 if self.split.get(K, 0) else L.SV_EPI_ADD_F32
+
     def _linear(self, x, w, y, epi, stream):
         R, K = self.R, w.shape[1]
         N = w.shape[0]
-        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi, act_pair=self.act)
-        L.sv_linear(desc, x, w, y, self.lin_ws, stream)
+        wt = self.tiled.get((w.data_ptr(), epi))
+        desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=self.dt, epilogue=epi, act_pair=self.act,
+                            w_layout=L.SV_W_ROWMAJOR if wt is None else L.SV_W_TILED)
+        L.sv_linear(desc, x, w if wt is None else wt, y, self.lin_ws, stream)
 
     def _residual(self, inp, w, stream):
         """x += inp W^T: K-split partials left for the next norm (returned as

@@ -106,6 +106,33 @@ def test_other_entry_points_reject_bad_arguments():
                                   cat_dtype, fake, None, None) == L.SV_ERR_ARG
 
 
+def test_tiled_weights_sizes_and_validation():
+    lib = L.load()
+    fake = ctypes.c_void_p(4096)
+    base = dict(rows=40, in_features=3840, out_features=30720, dtype=L.SV_BF16, epilogue=L.SV_EPI_GEGLU,
+                act_pair=1)
+    # GeGLU and K-split use two 64-feature tiles per wave (blocks of 128 features)
+    assert L.sv_linear_tiled_bytes(L.LinearDesc(**base)) == 240 * 60 * 128 * 128
+    split = dict(base, in_features=4096 + 32, out_features=704, epilogue=L.SV_EPI_SPLIT_F32)
+    assert L.sv_linear_tiled_bytes(L.LinearDesc(**split)) == 6 * 65 * 128 * 128   # ragged N and K padded
+    small = dict(base, in_features=96, out_features=192, epilogue=L.SV_EPI_STORE)
+    assert L.sv_linear_tiled_bytes(L.LinearDesc(**small)) == 3 * 2 * 64 * 128       # one tile per wave
+    assert L.sv_linear_tiled_bytes(L.LinearDesc(**dict(base, dtype=L.SV_F32, act_pair=0,
+                                                         epilogue=L.SV_EPI_STORE))) == 0
+    for bad in (dict(w_layout=2), dict(w_layout=-1), dict(w_layout=L.SV_W_TILED, dtype=L.SV_F32, act_pair=0,
+                                                        epilogue=L.SV_EPI_STORE)):
+        d = L.LinearDesc(**{**base, **bad})
+        assert lib.sv_linear(ctypes.byref(d), fake, fake, fake, fake, 1 << 40, None) == L.SV_ERR_ARG, bad
+    d = L.LinearDesc(**base)
+    assert lib.sv_linear_tile_weights(ctypes.byref(d), None, fake, None) == L.SV_ERR_ARG
+    assert lib.sv_linear_tile_weights(ctypes.byref(d), fake, None, None) == L.SV_ERR_ARG
+    assert lib.sv_linear_tile_weights(ctypes.byref(d), ctypes.c_void_p(4104), fake, None) == L.SV_ERR_ARG
+    d32 = L.LinearDesc(**dict(base, dtype=L.SV_F32, act_pair=0, epilogue=L.SV_EPI_STORE))
+    assert lib.sv_linear_tile_weights(ctypes.byref(d32), fake, fake, None) == L.SV_ERR_ARG
+    dt = L.LinearDesc(**dict(base, w_layout=L.SV_W_TILED))
+    assert lib.sv_linear(ctypes.byref(dt), fake, ctypes.c_void_p(4104), fake, fake, 1 << 40, None) == L.SV_ERR_ARG
+
+
 def test_cluster_unembed_rejects_bad_arguments():
     lib = L.load()
     fake = ctypes.c_void_p(4096)

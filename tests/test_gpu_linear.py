@@ -284,3 +284,90 @@ def test_pair_activations_geglu(R, K, dff):
     err = np.abs(got - ref)
     assert np.all(err <= bound), f"worst excess {(err - bound).max():.3e}"
     say(f"[linear pair geglu] ok, max err/bound {float((err / bound).max()):.3f}")
+
+
+def tile_layout(W, T):
+    """The tiled copy written out from its definition (host, uint16 bits): for block b of 64T
+    rows and chunk kc of 64 columns, DMA instruction (slot, iw) = (s, i) of the chunk holds,
+    in lane l, the 8 weights of row b*64T + s*16T + i*8 + l//8 starting at column
+    kc*64 + 8*((l % 8) ^ g(r)), r = (i % 2)*8 + l//8, g(r) = ((r >> 1) & 7) ^ ((r & 1) << 2);
+    zeros past the matrix."""
+    N, K = W.shape
+    NB, WI = 64 * T, 2 * T
+    nblk, kch = -(-N // NB), -(-K // 64)
+    out = np.zeros((nblk, kch, 4, WI, 64, 8), dtype=np.uint16)
+    lane = np.arange(64)
+    for i in range(WI):
+        r = (i % 2) * 8 + lane // 8
+        col = ((lane % 8) ^ (((r >> 1) & 7) ^ ((r & 1) << 2))) * 8
+        for s in range(4):
+            for b in range(nblk):
+                rows = b * NB + s * 16 * T + i * 8 + lane // 8
+                for kc in range(kch):
+                    k0 = kc * 64 + col
+                    ok = (rows < N) & (k0 < K)
+                    for l in np.nonzero(ok)[0]:
+                        out[b, kc, s, i, l] = W[rows[l], k0[l]:k0[l] + 8]
+    return out.reshape(-1)
+
+
+@gpu
+@pytest.mark.parametrize("N,K,epi", [(192, 96, L.SV_EPI_STORE), (704, 4096 + 32, L.SV_EPI_SPLIT_F32)])
+def test_tiled_weights_layout(N, K, epi):
+    """sv_linear_tile_weights against the layout built on the host (one tile width each)."""
+    dev = need_gpu()
+    say(f"[linear tiled layout] N={N} K={K} epi={epi}")
+    W = inputs.normal((N, K), K ** -0.5, 21, "W", dev)
+    desc = L.LinearDesc(rows=8, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_pair=1)
+    wt = L.tiled_weight(desc, W)
+    torch.cuda.synchronize()
+    nbytes = L.sv_linear_tiled_bytes(desc)
+    T = 2 if nbytes == -(-N // 128) * -(-K // 64) * 128 * 128 else 1
+    assert nbytes == -(-N // (64 * T)) * -(-K // 64) * 64 * T * 128
+    ref = tile_layout(W.view(torch.int16).cpu().numpy().view(np.uint16), T)
+    got = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert got.shape == ref.shape and np.array_equal(got, ref)
+
+
+# (rows, K, N, epilogue, act_pair): the stack's gate/up, down and q/k/v; ragged K (a
+# 32-dim last chunk) and ragged N (a half block) with K-split; one tile per wave; the
+# fused residual add; bf16 store; a plain bf16 (not pair) projection
+TILED_CASES = [(40, 3840, 30720, L.SV_EPI_GEGLU, 1), (40, 15360, 3840, L.SV_EPI_SPLIT_F32, 1),
+               (40, 3840, 8192, L.SV_EPI_SPLIT_F32, 1), (13, 4096 + 32, 704, L.SV_EPI_SPLIT_F32, 1),
+               (7, 96, 192, L.SV_EPI_STORE, 1), (64, 4096 + 32, 320, L.SV_EPI_ADD_F32, 1),
+               (5, 256, 1088, L.SV_EPI_STORE, 2), (33, 2048, 7168, L.SV_EPI_ADD_F32, 1),
+               (24, 1024, 3840, L.SV_EPI_STORE, 0)]
+
+
+@gpu
+@pytest.mark.parametrize("R,K,N,epi,pair", TILED_CASES)
+def test_tiled_weights_bit_exact(R, K, N, epi, pair):
+    """The tiled weight layout gives the row-major layout's results bit for bit (the same
+    values reach the same LDS slots; only the DMA's global addresses differ)."""
+    dev = need_gpu()
+    say(f"[linear tiled] R={R} K={K} N={N} epi={epi} pair={pair}")
+    W = inputs.normal((N, K), K ** -0.5, 22, "W", dev)
+    xf = inputs.normal((R, K), 1.0, 22, "xf", dev, "f32")
+    x = pair_of(xf) if pair else xf.to(torch.bfloat16)
+    desc = L.LinearDesc(rows=R, in_features=K, out_features=N, dtype=L.SV_BF16, epilogue=epi, act_pair=pair)
+    S = L.sv_linear_splits(desc) if epi == L.SV_EPI_SPLIT_F32 else 0
+    ws = torch.zeros(max(L.sv_linear_workspace(desc), 256), dtype=torch.uint8, device=dev)
+    if epi == L.SV_EPI_GEGLU:
+        shape, dt = (2, R, N // 2), torch.bfloat16
+    elif epi == L.SV_EPI_SPLIT_F32:
+        shape, dt = (S, R, N), torch.float32
+    elif epi == L.SV_EPI_ADD_F32 or pair == 1:
+        shape, dt = (R, N), torch.float32
+    else:
+        shape, dt = (R, N), torch.bfloat16
+    y0 = inputs.normal(shape, 1.0, 23, "y0", dev, "f32").to(dt) if epi == L.SV_EPI_ADD_F32 else \
+        torch.full(shape, float("nan"), dtype=dt, device=dev)
+    y_rm, y_t = y0.clone(), y0.clone()
+    L.sv_linear(desc, x, W, y_rm, ws)
+    wt = L.tiled_weight(desc, W)
+    desc.w_layout = L.SV_W_TILED
+    L.sv_linear(desc, x, wt, y_t, ws)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert not torch.isnan(y_t.float()).any(), "an output was left unwritten"
+    assert torch.equal(y_t.view(bits), y_rm.view(bits)), "tiled and row-major results differ"
