@@ -835,7 +835,8 @@ def pmc_summary(roots, out_path=None):
     and <root>/<call>.json that run's own output line (for the algorithmic bytes).
     A call's bytes: its library kernels' counter values summed over the run and
     divided by the number of calls made (the dispatch count of its most frequent
-    kernel), each counter scaled by what it reads for the plain 1 GiB copy."""
+    kernel), each counter scaled by what it reads for the plain 1 GiB copy.  The
+    weight tiling that sets up a projection call runs once and is left out."""
     import csv
     from collections import Counter
 
@@ -848,7 +849,9 @@ def pmc_summary(roots, out_path=None):
         return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
 
     def ours(name):
-        return name.startswith(("sv::", "void sv::"))
+        # the library's kernels of the call itself: the one-time weight tiling that sets
+        # up a projection call is not part of it
+        return name.startswith(("sv::", "void sv::")) and "tile_weights_kernel" not in name
 
     out = {"source_digest": source_digest(), "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch)",
            "method": "one rocprofv3 --pmc run per call and counter of bench.py --only <call> --iters 3; "

@@ -42,6 +42,9 @@ def test_pmc_summary_per_call_bytes_and_copy_scaling(tmp_path):
         rows_f += [(10 * c, att, "FETCH_SIZE", 1000.0), (10 * c + 1, mrg, "FETCH_SIZE", 10.0),
                    (10 * c + 2, "void at::native::fill", "FETCH_SIZE", 5000.0)]
         rows_w += [(10 * c, att, "WRITE_SIZE", 20.0), (10 * c + 1, mrg, "WRITE_SIZE", 4.0)]
+    # a one-time setup kernel of the library (weight tiling) is not part of the call
+    rows_f.append((99, "sv::tile_weights_kernel(unsigned short const*, unsigned short*, int, int, int, int, long)",
+                   "FETCH_SIZE", 9000.0))
     _write_counters(fetch / "attn_global", rows_f)
     _write_counters(write / "attn_global", rows_w)
     with open(fetch / "attn_global.json", "w") as f:
